@@ -1,0 +1,164 @@
+/*
+ * moe_ffn.h — C ABI of the MI355X (gfx950) MoE expert-FFN layer.
+ *
+ * The operation (HyperMegaMoE issue page, section 2.1 "forward fusion" and the
+ * parameter table of section 3.1 "Python API"): for T tokens x [T, H], each
+ * routed to K experts topk_ids [T, K] with gates topk_weights [T, K],
+ *
+ *     h_s   = x_t · up_proj_weight[e_s]            up_proj_weight   [E, H, 2I]
+ *     act_s = silu(h_s[:, 0:I]) ⊙ h_s[:, I:2I]     (SwiGLU; gate half first)
+ *     o_s   = act_s · down_proj_weight[e_s]        down_proj_weight [E, I, H]
+ *     y_t   = Σ_k topk_weights[t, k] · o_{t·K+k}   y [T, H]
+ *
+ * where slot s = t·K + k.  The routing (per-expert counts, prefix-sum offsets,
+ * the stable permutation of slots into expert-contiguous order and its
+ * inverse), the unpermute and the gate-weighted combine all happen inside the
+ * call (section 3.1: the call keeps the full MoE semantics).  The backward
+ * (section 2.2 "backward fusion") returns dx, d_up_proj_weight,
+ * d_down_proj_weight and d_topk_weights; topk_ids has no gradient.
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers to dense row-major arrays owned by
+ *    the caller.  The library keeps no pointer after a call returns and holds
+ *    no per-call state; two calls with distinct buffers are independent.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *    asynchronous on that stream unless stated otherwise; outputs are valid
+ *    once the stream has reached the call.
+ *  - Every function returns a moe_ffn_status.  Host-detectable errors (NULL
+ *    pointers, sizes, dtypes, alignment, workspace size) are returned before
+ *    anything is launched; nothing is written then.
+ *  - Device pointers must be 16-byte aligned; H and I must be multiples of 8.
+ *  - Workspace `ws` is caller-allocated scratch of at least the size the
+ *    matching *_workspace_size query returns; its contents need no
+ *    initialisation and are meaningless after the call.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. x, both weights, y, dy, dx and the weight gradients share
+ * one floating-point dtype; topk_weights and d_topk_weights are fp32. */
+typedef enum {
+    MOE_FFN_F32 = 0,
+    MOE_FFN_BF16 = 1,
+    MOE_FFN_I32 = 2, /* topk_ids */
+    MOE_FFN_I64 = 3  /* topk_ids */
+} moe_ffn_dtype;
+
+typedef enum {
+    MOE_FFN_OK = 0,
+    MOE_FFN_ERR_NULL = 1,      /* a required pointer is NULL */
+    MOE_FFN_ERR_SHAPE = 2,     /* a size is out of the supported range */
+    MOE_FFN_ERR_DTYPE = 3,     /* unsupported dtype combination */
+    MOE_FFN_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+    MOE_FFN_ERR_WORKSPACE = 5, /* ws_bytes (or saved) smaller than required */
+    MOE_FFN_ERR_EXPERT_ID = 6, /* a topk_ids value outside [0, E) (found on the device) */
+    MOE_FFN_ERR_SAVED = 7,     /* the saved context does not belong to this problem */
+    MOE_FFN_ERR_HIP = 8,       /* a HIP runtime call failed; see moe_ffn_last_error() */
+    MOE_FFN_ERR_DEVICE = 9     /* the current device is not a gfx950 GPU */
+} moe_ffn_status;
+
+/* Problem description.  Limits: 0 <= T, 1 <= K <= 32, 1 <= E <= 1024,
+ * T·K < 2^31, 8 <= H, 8 <= I, H % 8 == 0, I % 8 == 0, H·2I < 2^31. */
+typedef struct {
+    int64_t T, H, I, E, K;
+    int32_t dtype;     /* MOE_FFN_F32 or MOE_FFN_BF16 */
+    int32_t ids_dtype; /* MOE_FFN_I32 or MOE_FFN_I64 */
+} moe_ffn_problem;
+
+/* Flags. */
+#define MOE_FFN_CHECK_IDS 0x1u /* fwd: after routing, synchronise the stream and return
+                                  MOE_FFN_ERR_EXPERT_ID before any GEMM runs if an id was
+                                  out of range (the call is then synchronous). */
+
+/* Stages of the forward, for the timing hook below. */
+enum {
+    MOE_FFN_STAGE_ROUTE = 0,   /* counts, offsets, permutation, inverse index */
+    MOE_FFN_STAGE_GEMM1 = 1,   /* gathered up_proj GEMM with the SwiGLU epilogue */
+    MOE_FFN_STAGE_GEMM2 = 2,   /* down_proj GEMM */
+    MOE_FFN_STAGE_COMBINE = 3, /* unpermute + gate-weighted sum */
+    MOE_FFN_NUM_FWD_STAGES = 4
+};
+
+/* Optional per-stage timing: hipEvent_t handles created by the caller (see
+ * moe_ffn_event_create).  When an entry is non-NULL the library records it on
+ * `stream` right before (begin) / after (end) that stage's launches. */
+typedef struct {
+    void *begin[8];
+    void *end[8];
+} moe_ffn_stage_events;
+
+/* ---- forward ------------------------------------------------------------ */
+
+/* Sizes of the forward workspace and of the saved context that the backward
+ * needs (route arrays and the pre-activation h = x·up_proj_weight in the
+ * problem dtype).  Pure host function; no device is touched. */
+int moe_ffn_fwd_workspace_size(const moe_ffn_problem *p, uint32_t flags, size_t *ws_bytes,
+                               size_t *saved_bytes);
+
+/* y [T, H] = layer(x [T, H], topk_ids [T, K], topk_weights [T, K] fp32,
+ *                  up_proj_weight [E, H, 2I], down_proj_weight [E, I, H]).
+ * `saved` may be NULL (inference).  When non-NULL it must hold saved_bytes
+ * and receives what moe_ffn_bwd needs; it stays owned by the caller.
+ * An expert id outside [0, E) never causes an out-of-bounds access: the slot
+ * is dropped, a status word in `ws` records it (moe_ffn_read_status) and,
+ * with MOE_FFN_CHECK_IDS, the call fails with MOE_FFN_ERR_EXPERT_ID. */
+int moe_ffn_fwd(const moe_ffn_problem *p, const void *x, const void *topk_ids,
+                const float *topk_weights, const void *up_proj_weight,
+                const void *down_proj_weight, void *y, void *saved, void *ws, size_t ws_bytes,
+                uint32_t flags, void *stream);
+
+/* moe_ffn_fwd with the per-stage timing hook (ev may be NULL). */
+int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids,
+                   const float *topk_weights, const void *up_proj_weight,
+                   const void *down_proj_weight, void *y, void *saved, void *ws, size_t ws_bytes,
+                   uint32_t flags, void *stream, const moe_ffn_stage_events *ev);
+
+/* ---- routing alone -------------------------------------------------------- */
+
+/* Workspace for moe_ffn_route. */
+int moe_ffn_route_workspace_size(const moe_ffn_problem *p, size_t *ws_bytes);
+
+/* The routing step alone (section 4.1 "routing and expert parallelism"):
+ * counts [E], offsets [E+1] (offsets[E] = number of valid slots), the stable
+ * permutation sorted_slot [T·K] (position p -> slot s, ordered by expert then
+ * by s) and its inverse slot_pos [T·K] (slot s -> position p, -1 for a slot
+ * whose id is out of range).  All int32 device arrays owned by the caller. */
+int moe_ffn_route(const moe_ffn_problem *p, const void *topk_ids, int32_t *counts,
+                  int32_t *offsets, int32_t *sorted_slot, int32_t *slot_pos, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/* ---- status and measurement helpers ---------------------------------------- */
+
+/* Synchronises `stream`, then reads the device status word that the last
+ * forward or route call on this workspace left: 0, or 1 when an expert id was
+ * out of range. */
+int moe_ffn_read_status(const void *ws, void *stream, int32_t *device_status);
+
+/* Static text for a status code. */
+const char *moe_ffn_status_string(int status);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char *moe_ffn_last_error(void);
+
+/* hipEvent helpers for the timing hook, so a caller needs no other HIP
+ * binding: create / destroy an event and read the elapsed milliseconds
+ * between two recorded events (synchronises on `end`). */
+int moe_ffn_event_create(void **event);
+int moe_ffn_event_destroy(void *event);
+int moe_ffn_event_elapsed_ms(void *begin, void *end, float *ms);
+
+/* Library version, "major.minor.patch". */
+const char *moe_ffn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

@@ -1,0 +1,285 @@
+"""MI355X (gfx950) MoE expert-FFN layer: Python binding of ``libmoe_ffn.so``.
+
+The binding only marshals arguments: every step of the layer (routing,
+gathered up_proj GEMM with SwiGLU, down_proj GEMM, combine, and the backward)
+runs in the HIP kernels of the library.  PyTorch provides device memory and
+the current stream.  There is no CPU or eager fallback: if the library is not
+built, or the tensors are not on a GPU, the calls raise.
+
+Public API (names follow the C ABI of ``include/moe_ffn.h``):
+
+* ``moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
+  save_for_backward=False, check_ids=False)`` -> ``y`` (and the saved context)
+* ``moe_ffn_route(topk_ids, E)`` -> counts, offsets, sorted_slot, slot_pos
+* ``moe_ffn(...)`` autograd-aware layer (forward + backward through the library)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+__all__ = [
+    "MoEFFNError",
+    "load_library",
+    "library_path",
+    "exported_symbols",
+    "Problem",
+    "StageEvents",
+    "fwd_workspace_size",
+    "route_workspace_size",
+    "moe_ffn_fwd",
+    "moe_ffn_route",
+    "read_status",
+    "STAGES",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmoe_ffn.so")
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "moe_ffn.h")
+_lock = threading.Lock()
+_lib = None
+
+F32, BF16, I32, I64 = 0, 1, 2, 3
+CHECK_IDS = 0x1
+STAGES = ("route", "gemm1", "gemm2", "combine")
+
+ERR_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN",
+             5: "ERR_WORKSPACE", 6: "ERR_EXPERT_ID", 7: "ERR_SAVED", 8: "ERR_HIP",
+             9: "ERR_DEVICE"}
+
+
+class MoEFFNError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{ERR_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
+                ("E", ctypes.c_int64), ("K", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("ids_dtype", ctypes.c_int32)]
+
+
+class StageEvents(ctypes.Structure):
+    _fields_ = [("begin", ctypes.c_void_p * 8), ("end", ctypes.c_void_p * 8)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libmoe_ffn.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is not built; run `python -m mixture_experts_ffn_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, sz, i32, u32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32
+        pp = ctypes.POINTER(Problem)
+        psz = ctypes.POINTER(ctypes.c_size_t)
+        sigs = {
+            "moe_ffn_fwd_workspace_size": [pp, u32, psz, psz],
+            "moe_ffn_fwd": [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
+            "moe_ffn_fwd_ex": [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp,
+                               ctypes.POINTER(StageEvents)],
+            "moe_ffn_route_workspace_size": [pp, psz],
+            "moe_ffn_route": [pp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "moe_ffn_read_status": [vp, vp, ctypes.POINTER(ctypes.c_int32)],
+            "moe_ffn_event_create": [ctypes.POINTER(ctypes.c_void_p)],
+            "moe_ffn_event_destroy": [vp],
+            "moe_ffn_event_elapsed_ms": [vp, vp, ctypes.POINTER(ctypes.c_float)],
+        }
+        for name, args in sigs.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = i32
+        for name in ("moe_ffn_status_string",):
+            getattr(lib, name).argtypes = [i32]
+            getattr(lib, name).restype = ctypes.c_char_p
+        lib.moe_ffn_last_error.argtypes = []
+        lib.moe_ffn_last_error.restype = ctypes.c_char_p
+        lib.moe_ffn_version.argtypes = []
+        lib.moe_ffn_version.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def exported_symbols() -> list[str]:
+    """Function names declared in include/moe_ffn.h."""
+    text = open(_HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_ffn_\w+)\s*\(", text)))
+
+
+def _check(rc: int):
+    if rc != 0:
+        lib = load_library()
+        detail = lib.moe_ffn_last_error().decode() or lib.moe_ffn_status_string(rc).decode()
+        raise MoEFFNError(rc, detail)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise MoEFFNError(3, f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ids_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.int32:
+        return I32
+    if t.dtype == torch.int64:
+        return I64
+    raise MoEFFNError(3, f"topk_ids must be int32 or int64, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise MoEFFNError(1, "all tensors must be on the GPU (no CPU fallback exists)")
+        if t is not None and not t.is_contiguous():
+            raise MoEFFNError(4, "all tensors must be contiguous")
+
+
+def make_problem(x, topk_ids, up_proj_weight, down_proj_weight) -> Problem:
+    if x.dim() != 2 or topk_ids.dim() != 2 or up_proj_weight.dim() != 3 or down_proj_weight.dim() != 3:
+        raise MoEFFNError(2, "expected x [T,H], topk_ids [T,K], up [E,H,2I], down [E,I,H]")
+    T, H = x.shape
+    E, H2, I2 = up_proj_weight.shape
+    E2, I, H3 = down_proj_weight.shape
+    if topk_ids.shape[0] != T or H2 != H or H3 != H or E2 != E or I2 != 2 * I:
+        raise MoEFFNError(2, f"inconsistent shapes x{tuple(x.shape)} ids{tuple(topk_ids.shape)} "
+                             f"up{tuple(up_proj_weight.shape)} down{tuple(down_proj_weight.shape)}")
+    if up_proj_weight.dtype != x.dtype or down_proj_weight.dtype != x.dtype:
+        raise MoEFFNError(3, "x, up_proj_weight and down_proj_weight must share one dtype")
+    return Problem(T, H, I, E, topk_ids.shape[1], _dtype_code(x), _ids_code(topk_ids))
+
+
+def fwd_workspace_size(problem: Problem, flags: int = 0):
+    ws, saved = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load_library().moe_ffn_fwd_workspace_size(ctypes.byref(problem), flags,
+                                                     ctypes.byref(ws), ctypes.byref(saved)))
+    return ws.value, saved.value
+
+
+def route_workspace_size(problem: Problem) -> int:
+    ws = ctypes.c_size_t()
+    _check(load_library().moe_ffn_route_workspace_size(ctypes.byref(problem), ctypes.byref(ws)))
+    return ws.value
+
+
+def moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *,
+                save_for_backward: bool = False, check_ids: bool = False, ws=None,
+                stage_events: StageEvents | None = None, return_ws: bool = False):
+    """y [T, H] of the MoE expert-FFN layer (see include/moe_ffn.h).
+
+    With ``save_for_backward`` also returns the saved context (a uint8 device
+    tensor) that the backward consumes.  ``ws`` may pass a preallocated
+    workspace (uint8 tensor of at least ``fwd_workspace_size`` bytes).
+    """
+    lib = load_library()
+    _require_gpu(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
+    if topk_weights.dtype != torch.float32 or topk_weights.shape != topk_ids.shape:
+        raise MoEFFNError(3, "topk_weights must be float32 with the shape of topk_ids")
+    prob = make_problem(x, topk_ids, up_proj_weight, down_proj_weight)
+    ws_bytes, saved_bytes = fwd_workspace_size(prob)
+    dev = x.device
+    y = torch.empty_like(x)
+    if ws is None:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    elif ws.numel() < ws_bytes:
+        raise MoEFFNError(5, f"workspace has {ws.numel()} bytes, {ws_bytes} needed")
+    saved = torch.empty(saved_bytes, dtype=torch.uint8, device=dev) if save_for_backward else None
+    flags = CHECK_IDS if check_ids else 0
+    ev = ctypes.byref(stage_events) if stage_events is not None else None
+    with torch.cuda.device(dev):
+        rc = lib.moe_ffn_fwd_ex(ctypes.byref(prob), _ptr(x), _ptr(topk_ids), _ptr(topk_weights),
+                                _ptr(up_proj_weight), _ptr(down_proj_weight), _ptr(y),
+                                _ptr(saved), _ptr(ws), ws.numel(), flags, _stream(dev), ev)
+    _check(rc)
+    out = (y,)
+    if save_for_backward:
+        out += (saved,)
+    if return_ws:
+        out += (ws,)
+    return out[0] if len(out) == 1 else out
+
+
+def moe_ffn_route(topk_ids: torch.Tensor, E: int, H: int = 8, I: int = 8):
+    """Routing alone: (counts [E], offsets [E+1], sorted_slot [TK], slot_pos [TK], ws)."""
+    lib = load_library()
+    _require_gpu(topk_ids)
+    T, K = topk_ids.shape
+    prob = Problem(T, H, I, E, K, BF16, _ids_code(topk_ids))
+    ws_bytes = route_workspace_size(prob)
+    dev = topk_ids.device
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_slot = torch.empty(max(T * K, 1), dtype=torch.int32, device=dev)
+    slot_pos = torch.empty(max(T * K, 1), dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib.moe_ffn_route(ctypes.byref(prob), _ptr(topk_ids), _ptr(counts), _ptr(offsets),
+                               _ptr(sorted_slot), _ptr(slot_pos), _ptr(ws), ws_bytes,
+                               _stream(dev))
+    _check(rc)
+    return counts, offsets, sorted_slot[:T * K], slot_pos[:T * K], ws
+
+
+def read_status(ws: torch.Tensor) -> int:
+    """Device status word of the last forward/route on `ws` (1 = an id was out of range)."""
+    lib = load_library()
+    st = ctypes.c_int32()
+    with torch.cuda.device(ws.device):
+        _check(lib.moe_ffn_read_status(_ptr(ws), _stream(ws.device), ctypes.byref(st)))
+    return st.value
+
+
+class EventPool:
+    """hipEvents (through the library's helpers) for the per-stage timing hook."""
+
+    def __init__(self, n_sets: int, n_stages: int = 4):
+        self.lib = load_library()
+        self.sets = []
+        for _ in range(n_sets):
+            ev = StageEvents()
+            for s in range(n_stages):
+                for arr in (ev.begin, ev.end):
+                    h = ctypes.c_void_p()
+                    _check(self.lib.moe_ffn_event_create(ctypes.byref(h)))
+                    arr[s] = h
+            self.sets.append(ev)
+        self.n_stages = n_stages
+
+    def elapsed_ms(self, i: int, stage: int) -> float:
+        ms = ctypes.c_float()
+        ev = self.sets[i]
+        _check(self.lib.moe_ffn_event_elapsed_ms(ev.begin[stage], ev.end[stage], ctypes.byref(ms)))
+        return ms.value
+
+    def close(self):
+        for ev in self.sets:
+            for s in range(self.n_stages):
+                for arr in (ev.begin, ev.end):
+                    if arr[s]:
+                        self.lib.moe_ffn_event_destroy(arr[s])
+                        arr[s] = None
+        self.sets = []

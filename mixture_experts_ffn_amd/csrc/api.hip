@@ -1,0 +1,460 @@
+// api.hip — the C ABI of moe_ffn.h: validation, workspace layout, launches.
+//
+// Host side of the operator.  The two-phase shape of the interface (query the
+// workspace size, then execute) follows the HyperMegaMoE issue page, section
+// 2.3 (workspace query + execute entry points for forward and backward);
+// checking shapes, dtypes, layout and buffer sizes at the host boundary
+// before any kernel runs follows section 4.2, and the host-computed workspace
+// size follows section 5.3.  The library keeps no per-call state: every
+// buffer belongs to the caller (the issue page of the FSDP + EP composition
+// shows why per-call context must not live in the operator).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "kernels.h"
+#include "moe_ffn.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_fail(hipError_t err, const char *what)
+{
+    return fail(MOE_FFN_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+#define HIP_TRY(expr, what)                                                                        \
+    do {                                                                                           \
+        hipError_t e_ = (expr);                                                                    \
+        if (e_ != hipSuccess)                                                                      \
+            return hip_fail(e_, what);                                                             \
+    } while (0)
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_size(int dtype) { return dtype == MOE_FFN_BF16 ? 2 : 4; }
+
+int validate_problem(const moe_ffn_problem *p)
+{
+    if (!p)
+        return fail(MOE_FFN_ERR_NULL, "problem is NULL");
+    if (p->dtype != MOE_FFN_F32 && p->dtype != MOE_FFN_BF16)
+        return fail(MOE_FFN_ERR_DTYPE, "dtype must be F32 or BF16 (got %d)", p->dtype);
+    if (p->ids_dtype != MOE_FFN_I32 && p->ids_dtype != MOE_FFN_I64)
+        return fail(MOE_FFN_ERR_DTYPE, "ids_dtype must be I32 or I64 (got %d)", p->ids_dtype);
+    if (p->T < 0)
+        return fail(MOE_FFN_ERR_SHAPE, "T must be >= 0 (got %lld)", (long long)p->T);
+    if (p->K < 1 || p->K > 32)
+        return fail(MOE_FFN_ERR_SHAPE, "K must be in [1, 32] (got %lld)", (long long)p->K);
+    if (p->E < 1 || p->E > 1024)
+        return fail(MOE_FFN_ERR_SHAPE, "E must be in [1, 1024] (got %lld)", (long long)p->E);
+    if (p->H < 8 || p->H % 8)
+        return fail(MOE_FFN_ERR_SHAPE, "H must be a positive multiple of 8 (got %lld)",
+                    (long long)p->H);
+    if (p->I < 8 || p->I % 8)
+        return fail(MOE_FFN_ERR_SHAPE, "I must be a positive multiple of 8 (got %lld)",
+                    (long long)p->I);
+    if (p->T * p->K >= (int64_t(1) << 31))
+        return fail(MOE_FFN_ERR_SHAPE, "T*K must be < 2^31");
+    if (p->H * 2 * p->I >= (int64_t(1) << 31))
+        return fail(MOE_FFN_ERR_SHAPE, "H*2I must be < 2^31");
+    return MOE_FFN_OK;
+}
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int check_ptr(const void *ptr, const char *name, size_t align = 16)
+{
+    if (!ptr)
+        return fail(MOE_FFN_ERR_NULL, "%s is NULL", name);
+    if (reinterpret_cast<uintptr_t>(ptr) % align)
+        return fail(MOE_FFN_ERR_ALIGN, "%s is not %zu-byte aligned", name, align);
+    return MOE_FFN_OK;
+}
+
+// The current device must be a gfx950 GPU.  Cached per device ordinal.
+int check_device()
+{
+    static std::mutex mu;
+    static signed char known[64] = {0}; // 0 unknown, 1 ok, -1 not gfx950
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return hip_fail(err, "hipGetDevice");
+    if (dev < 0 || dev >= 64)
+        return fail(MOE_FFN_ERR_DEVICE, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (known[dev] == 0) {
+        hipDeviceProp_t prop;
+        err = hipGetDeviceProperties(&prop, dev);
+        if (err != hipSuccess)
+            return hip_fail(err, "hipGetDeviceProperties");
+        known[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    if (known[dev] < 0)
+        return fail(MOE_FFN_ERR_DEVICE, "device %d is not gfx950", dev);
+    return MOE_FFN_OK;
+}
+
+moe::FwdTiles pick_tiles(const moe_ffn_problem &p)
+{
+    moe::FwdTiles t;
+    if (p.dtype == MOE_FFN_F32) {
+        t.BM = 64;
+    } else {
+        const double avg_rows = (double)(p.T * p.K) / (double)p.E;
+        t.BM = avg_rows <= 64.0 ? 64 : 128;
+    }
+    return t;
+}
+
+// Region offsets inside the forward workspace (and the saved context).
+struct FwdLayout {
+    moe::FwdTiles tiles;
+    moe::RoutePlan rp;
+    int64_t max_mtiles;
+    // ws
+    size_t status, hist, bad, counts, offsets, mtile_off, mtile_expert, sorted_slot, slot_pos;
+    size_t act, o, ws_total;
+    // saved
+    size_t s_counts, s_offsets, s_sorted, s_slotpos, s_h, saved_total;
+};
+
+FwdLayout fwd_layout(const moe_ffn_problem &p)
+{
+    FwdLayout L;
+    const int64_t TK = p.T * p.K;
+    const int E = (int)p.E;
+    const size_t es = elem_size(p.dtype);
+    L.tiles = pick_tiles(p);
+    L.rp = moe::make_route_plan(TK, E);
+    L.max_mtiles = moe::max_mtiles_bound(TK, E, L.tiles.BM);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + (bytes ? bytes : 1));
+        return at;
+    };
+    L.status = take(sizeof(int32_t));
+    L.hist = take(sizeof(int32_t) * (size_t)E * (size_t)L.rp.NB);
+    L.bad = take(sizeof(int32_t) * (size_t)L.rp.NB);
+    L.counts = take(sizeof(int32_t) * (size_t)E);
+    L.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
+    L.mtile_off = take(sizeof(int32_t) * (size_t)(E + 1));
+    L.mtile_expert = take(sizeof(int32_t) * (size_t)L.max_mtiles);
+    L.sorted_slot = take(sizeof(int32_t) * (size_t)TK);
+    L.slot_pos = take(sizeof(int32_t) * (size_t)TK);
+    L.act = take(es * (size_t)TK * (size_t)p.I);
+    L.o = take(es * (size_t)TK * (size_t)p.H);
+    L.ws_total = off;
+    off = 0;
+    L.s_counts = take(sizeof(int32_t) * (size_t)E);
+    L.s_offsets = take(sizeof(int32_t) * (size_t)(E + 1));
+    L.s_sorted = take(sizeof(int32_t) * (size_t)TK);
+    L.s_slotpos = take(sizeof(int32_t) * (size_t)TK);
+    L.s_h = take(es * (size_t)TK * (size_t)(2 * p.I));
+    L.saved_total = off;
+    return L;
+}
+
+// Workspace of the routing step alone.
+struct RouteLayout {
+    moe::RoutePlan rp;
+    int BM;
+    size_t status, hist, bad, mtile_off, mtile_expert, total;
+};
+
+RouteLayout route_layout(const moe_ffn_problem &p)
+{
+    RouteLayout R;
+    const int64_t TK = p.T * p.K;
+    const int E = (int)p.E;
+    R.rp = moe::make_route_plan(TK, E);
+    R.BM = pick_tiles(p).BM;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + (bytes ? bytes : 1));
+        return at;
+    };
+    R.status = take(sizeof(int32_t));
+    R.hist = take(sizeof(int32_t) * (size_t)E * (size_t)R.rp.NB);
+    R.bad = take(sizeof(int32_t) * (size_t)R.rp.NB);
+    R.mtile_off = take(sizeof(int32_t) * (size_t)(E + 1));
+    R.mtile_expert = take(sizeof(int32_t) * (size_t)moe::max_mtiles_bound(TK, E, R.BM));
+    R.total = off;
+    return R;
+}
+
+template <typename P> P *at(void *base, size_t off)
+{
+    return reinterpret_cast<P *>(static_cast<char *>(base) + off);
+}
+
+void record(const moe_ffn_stage_events *ev, int stage, bool begin, hipStream_t s)
+{
+    if (!ev)
+        return;
+    void *e = begin ? ev->begin[stage] : ev->end[stage];
+    if (e)
+        (void)hipEventRecord(static_cast<hipEvent_t>(e), s);
+}
+
+} // namespace
+
+extern "C" {
+
+int moe_ffn_fwd_workspace_size(const moe_ffn_problem *p, uint32_t flags, size_t *ws_bytes,
+                               size_t *saved_bytes)
+{
+    (void)flags;
+    g_err[0] = 0;
+    int rc = validate_problem(p);
+    if (rc)
+        return rc;
+    if (!ws_bytes)
+        return fail(MOE_FFN_ERR_NULL, "ws_bytes is NULL");
+    const FwdLayout L = fwd_layout(*p);
+    *ws_bytes = L.ws_total;
+    if (saved_bytes)
+        *saved_bytes = L.saved_total;
+    return MOE_FFN_OK;
+}
+
+int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids,
+                   const float *topk_weights, const void *up_proj_weight,
+                   const void *down_proj_weight, void *y, void *saved, void *ws, size_t ws_bytes,
+                   uint32_t flags, void *stream, const moe_ffn_stage_events *ev)
+{
+    g_err[0] = 0;
+    int rc = validate_problem(p);
+    if (rc)
+        return rc;
+    const FwdLayout L = fwd_layout(*p);
+    if (p->T == 0)
+        return MOE_FFN_OK;
+    const size_t id_align = p->ids_dtype == MOE_FFN_I64 ? 8 : 4;
+    if ((rc = check_ptr(x, "x")) || (rc = check_ptr(topk_ids, "topk_ids", id_align)) ||
+        (rc = check_ptr(topk_weights, "topk_weights", 4)) ||
+        (rc = check_ptr(up_proj_weight, "up_proj_weight")) ||
+        (rc = check_ptr(down_proj_weight, "down_proj_weight")) || (rc = check_ptr(y, "y")) ||
+        (rc = check_ptr(ws, "ws")))
+        return rc;
+    if (saved && !aligned16(saved))
+        return fail(MOE_FFN_ERR_ALIGN, "saved is not 16-byte aligned");
+    if (ws_bytes < L.ws_total)
+        return fail(MOE_FFN_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, L.ws_total);
+    if ((rc = check_device()))
+        return rc;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t TK = p->T * p->K;
+    const int E = (int)p->E;
+    moe::RouteBufs rb;
+    rb.hist = at<int32_t>(ws, L.hist);
+    rb.bad = at<int32_t>(ws, L.bad);
+    rb.mtile_off = at<int32_t>(ws, L.mtile_off);
+    rb.mtile_expert = at<int32_t>(ws, L.mtile_expert);
+    rb.status = at<int32_t>(ws, L.status);
+    if (saved) {
+        rb.counts = at<int32_t>(saved, L.s_counts);
+        rb.offsets = at<int32_t>(saved, L.s_offsets);
+        rb.sorted_slot = at<int32_t>(saved, L.s_sorted);
+        rb.slot_pos = at<int32_t>(saved, L.s_slotpos);
+    } else {
+        rb.counts = at<int32_t>(ws, L.counts);
+        rb.offsets = at<int32_t>(ws, L.offsets);
+        rb.sorted_slot = at<int32_t>(ws, L.sorted_slot);
+        rb.slot_pos = at<int32_t>(ws, L.slot_pos);
+    }
+
+    record(ev, MOE_FFN_STAGE_ROUTE, true, s);
+    HIP_TRY(moe::launch_route(topk_ids, p->ids_dtype == MOE_FFN_I64, TK, E, L.tiles.BM, L.rp, rb,
+                              s),
+            "route launch");
+    record(ev, MOE_FFN_STAGE_ROUTE, false, s);
+
+    if (flags & MOE_FFN_CHECK_IDS) {
+        int32_t st = 0;
+        HIP_TRY(hipMemcpyAsync(&st, rb.status, sizeof st, hipMemcpyDeviceToHost, s),
+                "status copy");
+        HIP_TRY(hipStreamSynchronize(s), "stream sync");
+        if (st)
+            return fail(MOE_FFN_ERR_EXPERT_ID, "topk_ids holds a value outside [0, %d)", E);
+    }
+
+    moe::GroupedGemmArgs g1{};
+    g1.A = x;
+    g1.B = up_proj_weight;
+    g1.C = at<void>(ws, L.act);
+    g1.Hsave = saved ? at<void>(saved, L.s_h) : nullptr;
+    g1.sorted_slot = rb.sorted_slot;
+    g1.offsets = rb.offsets;
+    g1.mtile_off = rb.mtile_off;
+    g1.mtile_expert = rb.mtile_expert;
+    g1.Kdim = (int)p->H;
+    g1.Nout = (int)p->I;
+    g1.ldb = (int)(2 * p->I);
+    g1.topk = (int)p->K;
+    g1.E = E;
+    g1.max_mtiles = (int)L.max_mtiles;
+    record(ev, MOE_FFN_STAGE_GEMM1, true, s);
+    HIP_TRY(moe::launch_gemm1_swiglu(p->dtype, L.tiles, g1, s), "gemm1 launch");
+    record(ev, MOE_FFN_STAGE_GEMM1, false, s);
+
+    moe::GroupedGemmArgs g2 = g1;
+    g2.A = at<void>(ws, L.act);
+    g2.B = down_proj_weight;
+    g2.C = at<void>(ws, L.o);
+    g2.Hsave = nullptr;
+    g2.sorted_slot = nullptr;
+    g2.Kdim = (int)p->I;
+    g2.Nout = (int)p->H;
+    g2.ldb = (int)p->H;
+    record(ev, MOE_FFN_STAGE_GEMM2, true, s);
+    HIP_TRY(moe::launch_gemm2(p->dtype, L.tiles, g2, s), "gemm2 launch");
+    record(ev, MOE_FFN_STAGE_GEMM2, false, s);
+
+    record(ev, MOE_FFN_STAGE_COMBINE, true, s);
+    HIP_TRY(moe::launch_combine(p->dtype, at<void>(ws, L.o), rb.slot_pos, topk_weights, y, p->T,
+                                (int)p->H, (int)p->K, s),
+            "combine launch");
+    record(ev, MOE_FFN_STAGE_COMBINE, false, s);
+    return MOE_FFN_OK;
+}
+
+int moe_ffn_fwd(const moe_ffn_problem *p, const void *x, const void *topk_ids,
+                const float *topk_weights, const void *up_proj_weight,
+                const void *down_proj_weight, void *y, void *saved, void *ws, size_t ws_bytes,
+                uint32_t flags, void *stream)
+{
+    return moe_ffn_fwd_ex(p, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, y,
+                          saved, ws, ws_bytes, flags, stream, nullptr);
+}
+
+int moe_ffn_route_workspace_size(const moe_ffn_problem *p, size_t *ws_bytes)
+{
+    g_err[0] = 0;
+    int rc = validate_problem(p);
+    if (rc)
+        return rc;
+    if (!ws_bytes)
+        return fail(MOE_FFN_ERR_NULL, "ws_bytes is NULL");
+    *ws_bytes = route_layout(*p).total;
+    return MOE_FFN_OK;
+}
+
+int moe_ffn_route(const moe_ffn_problem *p, const void *topk_ids, int32_t *counts,
+                  int32_t *offsets, int32_t *sorted_slot, int32_t *slot_pos, void *ws,
+                  size_t ws_bytes, void *stream)
+{
+    g_err[0] = 0;
+    int rc = validate_problem(p);
+    if (rc)
+        return rc;
+    const RouteLayout R = route_layout(*p);
+    const size_t need = R.total;
+    const int64_t TK = p->T * p->K;
+    const size_t id_align = p->ids_dtype == MOE_FFN_I64 ? 8 : 4;
+    if ((rc = check_ptr(counts, "counts", 4)) || (rc = check_ptr(offsets, "offsets", 4)) ||
+        (rc = check_ptr(ws, "ws")))
+        return rc;
+    if (TK > 0 && ((rc = check_ptr(topk_ids, "topk_ids", id_align)) ||
+                   (rc = check_ptr(sorted_slot, "sorted_slot", 4)) ||
+                   (rc = check_ptr(slot_pos, "slot_pos", 4))))
+        return rc;
+    if (ws_bytes < need)
+        return fail(MOE_FFN_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, need);
+    if ((rc = check_device()))
+        return rc;
+    moe::RouteBufs rb;
+    rb.status = at<int32_t>(ws, R.status);
+    rb.hist = at<int32_t>(ws, R.hist);
+    rb.bad = at<int32_t>(ws, R.bad);
+    rb.mtile_off = at<int32_t>(ws, R.mtile_off);
+    rb.mtile_expert = at<int32_t>(ws, R.mtile_expert);
+    rb.counts = counts;
+    rb.offsets = offsets;
+    rb.sorted_slot = sorted_slot;
+    rb.slot_pos = slot_pos;
+    HIP_TRY(moe::launch_route(topk_ids, p->ids_dtype == MOE_FFN_I64, TK, (int)p->E, R.BM, R.rp,
+                              rb, static_cast<hipStream_t>(stream)),
+            "route launch");
+    return MOE_FFN_OK;
+}
+
+int moe_ffn_read_status(const void *ws, void *stream, int32_t *device_status)
+{
+    g_err[0] = 0;
+    if (!ws || !device_status)
+        return fail(MOE_FFN_ERR_NULL, "ws or device_status is NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    HIP_TRY(hipStreamSynchronize(s), "stream sync");
+    HIP_TRY(hipMemcpy(device_status, ws, sizeof(int32_t), hipMemcpyDeviceToHost), "status copy");
+    return MOE_FFN_OK;
+}
+
+const char *moe_ffn_status_string(int status)
+{
+    switch (status) {
+    case MOE_FFN_OK: return "ok";
+    case MOE_FFN_ERR_NULL: return "a required pointer is NULL";
+    case MOE_FFN_ERR_SHAPE: return "a size is out of the supported range";
+    case MOE_FFN_ERR_DTYPE: return "unsupported dtype";
+    case MOE_FFN_ERR_ALIGN: return "a pointer is not suitably aligned";
+    case MOE_FFN_ERR_WORKSPACE: return "workspace or saved buffer too small";
+    case MOE_FFN_ERR_EXPERT_ID: return "an expert id is outside [0, E)";
+    case MOE_FFN_ERR_SAVED: return "saved context does not match the problem";
+    case MOE_FFN_ERR_HIP: return "HIP runtime error";
+    case MOE_FFN_ERR_DEVICE: return "current device is not gfx950";
+    default: return "unknown status";
+    }
+}
+
+const char *moe_ffn_last_error(void) { return g_err; }
+
+int moe_ffn_event_create(void **event)
+{
+    if (!event)
+        return fail(MOE_FFN_ERR_NULL, "event is NULL");
+    hipEvent_t e;
+    HIP_TRY(hipEventCreate(&e), "hipEventCreate");
+    *event = e;
+    return MOE_FFN_OK;
+}
+
+int moe_ffn_event_destroy(void *event)
+{
+    if (event)
+        HIP_TRY(hipEventDestroy(static_cast<hipEvent_t>(event)), "hipEventDestroy");
+    return MOE_FFN_OK;
+}
+
+int moe_ffn_event_elapsed_ms(void *begin, void *end, float *ms)
+{
+    if (!begin || !end || !ms)
+        return fail(MOE_FFN_ERR_NULL, "event or ms is NULL");
+    HIP_TRY(hipEventSynchronize(static_cast<hipEvent_t>(end)), "hipEventSynchronize");
+    HIP_TRY(hipEventElapsedTime(ms, static_cast<hipEvent_t>(begin), static_cast<hipEvent_t>(end)),
+            "hipEventElapsedTime");
+    return MOE_FFN_OK;
+}
+
+const char *moe_ffn_version(void) { return "0.1.0"; }
+
+} // extern "C"

@@ -1,0 +1,73 @@
+// kernels.h — host-side launchers of the gfx950 kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- routing -----------------------------------------------------------------
+struct RoutePlan {
+    int RC;    // slots per chunk (one wave per chunk)
+    int NB;    // number of chunks
+    int nbits; // bits needed for an expert id
+};
+
+struct RouteBufs {
+    int32_t *hist;        // [E * NB]
+    int32_t *bad;         // [NB]
+    int32_t *counts;      // [E]
+    int32_t *offsets;     // [E + 1]
+    int32_t *mtile_off;   // [E + 1]
+    int32_t *mtile_expert; // [max_mtiles]: expert owning each M-tile
+    int32_t *status;      // [1]
+    int32_t *sorted_slot; // [TK]
+    int32_t *slot_pos;    // [TK]
+};
+
+RoutePlan make_route_plan(int64_t TK, int E);
+hipError_t launch_route(const void *ids, bool ids64, int64_t TK, int E, int BM,
+                        const RoutePlan &rp, const RouteBufs &rb, hipStream_t stream);
+
+// upper bound of sum_e ceil(counts[e] / BM) over any routing of TK slots
+inline int64_t max_mtiles_bound(int64_t TK, int E, int BM)
+{
+    const int64_t ne = TK < E ? TK : E;
+    return (TK + BM - 1) / BM + ne;
+}
+
+// ---- grouped GEMMs ---------------------------------------------------------------
+// One launch covers every expert: M-tiles of BM rows walk each expert's
+// segment [offsets[e], offsets[e+1]) of the permuted rows.
+struct GroupedGemmArgs {
+    const void *A;               // GEMM1: x [T, Kdim] (rows gathered); GEMM2: act [TK, Kdim]
+    const void *B;               // weights [E, Kdim, ldb], N-contiguous
+    void *C;                     // GEMM1: act [TK, Nout]; GEMM2: o [TK, Nout]
+    void *Hsave;                 // GEMM1 only, optional: pre-activation h [TK, 2*Nout]
+    const int32_t *sorted_slot;  // GEMM1: permuted row p -> slot s (token s / topk)
+    const int32_t *offsets;      // [E + 1]
+    const int32_t *mtile_off;    // [E + 1]
+    const int32_t *mtile_expert; // [max_mtiles]
+    int Kdim;                    // contraction length
+    int Nout;                    // output columns
+    int ldb;                     // row stride of B (2I for GEMM1, H for GEMM2)
+    int topk;                    // K
+    int E;
+    int max_mtiles;              // upper bound of sum_e ceil(counts[e] / BM)
+};
+
+// plan-level tile choice for the forward
+struct FwdTiles {
+    int BM; // 64 or 128
+};
+
+hipError_t launch_gemm1_swiglu(int dtype, const FwdTiles &t, const GroupedGemmArgs &a,
+                               hipStream_t stream);
+hipError_t launch_gemm2(int dtype, const FwdTiles &t, const GroupedGemmArgs &a,
+                        hipStream_t stream);
+
+// ---- combine ---------------------------------------------------------------------
+hipError_t launch_combine(int dtype, const void *o, const int32_t *slot_pos, const float *gates,
+                          void *y, int64_t T, int H, int K, hipStream_t stream);
+
+} // namespace moe
