@@ -1,0 +1,179 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert-FFN layer on one MI355X.
+
+One step = one full forward of the layer (route -> gathered up_proj GEMM with
+SwiGLU -> down_proj GEMM -> combine) on a seeded synthetic batch that is
+already resident in HBM.  Prints ONE JSON line.
+
+Default workload: prefill, bf16 with fp32 accumulation, T=4096 tokens,
+H=2048, I=1408, E=64 experts, K=6, uniform routing.  Other workloads:
+--workload {tiny_f32,prefill_bf16,skewed_bf16,decode_bf16,fwdbwd_bf16}.
+
+Besides tokens/s the line carries
+* "roofline": the dominant kernel (the up_proj GEMM with SwiGLU epilogue,
+  or for the HBM-bound decode shape the same kernel against HBM bandwidth),
+  its algorithmic work per launch divided by its average launch time, where
+  the launch times come from HIP events that the library records around that
+  kernel on the call's stream during the timed steps;
+* "cpu_baseline": the CPU oracle on the host's cores over a bounded sample of
+  the same workload (its first tokens), unless --no-cpu-baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE-FFN layer tokens/s + % peak MFMA (prefill) / % peak HBM BW (decode)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not supported "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_ffn_amd as m
+    from synth import make_inputs, workload
+
+    m.load_library()
+    w = workload(args.workload)
+    inp = make_inputs(w, with_dy=False)
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    d = {k: to_dev(v) for k, v in inp.items()}
+    prob = m.make_problem(d["x"], d["topk_ids"], d["up_proj"], d["down_proj"])
+    ws_bytes, _ = m.fwd_workspace_size(prob)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        return m.moe_ffn_fwd(d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
+                             d["down_proj"], ws=ws, stage_events=ev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    pool = m.EventPool(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        y = step(pool.sets[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {name: float(np.mean([pool.elapsed_ms(i, s) for i in range(args.steps)]))
+                for s, name in enumerate(m.STAGES)}
+    pool.close()
+
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = w.T * args.steps / elapsed
+    counts = np.bincount(inp["topk_ids"].ravel(), minlength=w.E)
+    live = counts > 0
+    es = 2 if w.dtype == "bf16" else 4
+    # algorithmic work of the up_proj kernel per launch
+    g1_flops = 4.0 * w.T * w.K * w.H * w.I
+    g1_bytes = (live.sum() * w.H * 2 * w.I * es + w.T * w.H * es + w.T * w.K * w.I * es)
+    g1_s = stage_ms["gemm1"] * 1e-3
+    layer_flops = w.fwd_flops()
+    layer_bytes = live.sum() * 3 * w.H * w.I * es + 2 * w.T * w.H * es + w.T * w.K * 8
+    if w.name.startswith("decode"):
+        roof = {"bound": "hbm", "achieved": g1_bytes / g1_s / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+        roof = {"bound": "mfma", "achieved": g1_flops / g1_s / 1e12, "peak": peak,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "grouped_gemm_kernel (up_proj + SwiGLU)"
+    roof["avg_launch_ms"] = stage_ms["gemm1"]
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded numpy PCG64; random-init weights)",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "K": w.K,
+                   "routing": w.routing, "accumulate": "f32"},
+        "layer": {"tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
+                  "frac_mfma": layer_flops / (ms_per_step * 1e-3) / 1e12 /
+                  (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS),
+                  "hbm_gbs_alg": layer_bytes / (ms_per_step * 1e-3) / 1e9,
+                  "stage_ms": stage_ms},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, y, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, inp, y_gpu, target_s):
+    """The CPU oracle on the first n tokens of the same batch (n sized for ~target_s)."""
+    import oracle
+
+    def run(n):
+        t0 = time.perf_counter()
+        yo = oracle.forward(inp["x"][:n], inp["topk_ids"][:n], inp["topk_weights"][:n],
+                            inp["up_proj"], inp["down_proj"])
+        return yo, time.perf_counter() - t0
+
+    n = min(w.T, 8)
+    _, dt = run(n)
+    while dt < 0.5 and n < w.T:
+        n = min(w.T, n * 4)
+        _, dt = run(n)
+    n = int(min(w.T, max(1, n * target_s / max(dt, 1e-6))))
+    yo, dt = run(n)
+    got = y_gpu[:n].float().cpu().numpy().astype(np.float64)
+    err = float(np.abs(got - yo).max() / max(np.abs(yo).max(), 1e-300))
+    return {"value": n / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens of the same batch (all {w.E} experts' weights), "
+                      f"{dt:.1f} s, fp64 accumulation",
+            "max_rel_err_gpu_vs_oracle_on_sample": err}
+
+
+if __name__ == "__main__":
+    main()

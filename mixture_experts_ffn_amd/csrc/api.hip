@@ -314,7 +314,10 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
     g1.E = E;
     g1.max_mtiles = (int)L.max_mtiles;
     record(ev, MOE_FFN_STAGE_GEMM1, true, s);
-    HIP_TRY(moe::launch_gemm1_swiglu(p->dtype, L.tiles, g1, s), "gemm1 launch");
+    const bool fast = moe::fast_gemm_supported(p->dtype, p->H, p->I);
+    HIP_TRY(fast ? moe::launch_fast_gemm1(L.tiles, g1, s)
+                 : moe::launch_gemm1_swiglu(p->dtype, L.tiles, g1, s),
+            "gemm1 launch");
     record(ev, MOE_FFN_STAGE_GEMM1, false, s);
 
     moe::GroupedGemmArgs g2 = g1;
@@ -327,7 +330,9 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
     g2.Nout = (int)p->H;
     g2.ldb = (int)p->H;
     record(ev, MOE_FFN_STAGE_GEMM2, true, s);
-    HIP_TRY(moe::launch_gemm2(p->dtype, L.tiles, g2, s), "gemm2 launch");
+    HIP_TRY(fast ? moe::launch_fast_gemm2(L.tiles, g2, s)
+                 : moe::launch_gemm2(p->dtype, L.tiles, g2, s),
+            "gemm2 launch");
     record(ev, MOE_FFN_STAGE_GEMM2, false, s);
 
     record(ev, MOE_FFN_STAGE_COMBINE, true, s);

@@ -48,8 +48,13 @@ template <typename T> __device__ inline T from_f32(float v);
 template <> __device__ inline float from_f32<float>(float v) { return v; }
 template <> __device__ inline bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
 
-// silu(a) = a * sigmoid(a)
-__device__ inline float silu_f(float a) { return a / (1.0f + __expf(-a)); }
+// silu(a) = a * sigmoid(a) = a / (1 + e^-a), with the hardware exp and
+// reciprocal (about 1 ulp each).  Saturates correctly: a -> -inf gives -0
+// (e^-a = inf, 1/inf = 0), a -> +inf gives a.
+__device__ inline float silu_f(float a)
+{
+    return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
 
 // 16-byte vector of T
 template <typename T> struct Vec16 {

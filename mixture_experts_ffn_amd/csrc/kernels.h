@@ -66,6 +66,11 @@ hipError_t launch_gemm1_swiglu(int dtype, const FwdTiles &t, const GroupedGemmAr
 hipError_t launch_gemm2(int dtype, const FwdTiles &t, const GroupedGemmArgs &a,
                         hipStream_t stream);
 
+// bf16 fast path (gemm_mfma.hip): H % 256 == 0, I % 128 == 0
+bool fast_gemm_supported(int dtype, int64_t H, int64_t I);
+hipError_t launch_fast_gemm1(const FwdTiles &t, const GroupedGemmArgs &a, hipStream_t stream);
+hipError_t launch_fast_gemm2(const FwdTiles &t, const GroupedGemmArgs &a, hipStream_t stream);
+
 // ---- combine ---------------------------------------------------------------------
 hipError_t launch_combine(int dtype, const void *o, const int32_t *slot_pos, const float *gates,
                           void *y, int64_t T, int H, int K, hipStream_t stream);
