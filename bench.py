@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run one elementwise copy of this many MiB (for scaling HBM "
+                         "byte counters against a kernel of known traffic)")
     return ap.parse_args()
 
 
@@ -117,8 +120,10 @@ def main():
         roof = {"bound": "mfma", "achieved": g1_flops / g1_s / 1e12, "peak": peak,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = "grouped_gemm_kernel (up_proj + SwiGLU)"
+    roof["traffic"] = measured_traffic(w.name)
+    roof["kernel"] = ("moe::fast::moe_gemm_bf16<BM,true,true,...> (gathered up_proj GEMM + SwiGLU)"
+                      if w.dtype == "bf16" and w.H % 256 == 0 and w.I % 128 == 0 else
+                      "moe::grouped_gemm_kernel<...,SWIGLU=true,...> (gathered up_proj GEMM + SwiGLU)")
     roof["avg_launch_ms"] = stage_ms["gemm1"]
 
     out = {
@@ -145,9 +150,36 @@ def main():
         "cpu_baseline": None,
     }
 
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        torch.add(src, 0.0, out=dst)  # reads n*4 bytes, writes n*4 bytes
+        torch.cuda.synchronize()
+        out["copy_calibration"] = {"bytes_read": n * 4, "bytes_written": n * 4}
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, y, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch of the up_proj kernel from the committed PMC summary
+    (profiles/traffic_gemm1.txt), or None when the kernel source has changed since the
+    counters were taken or no summary exists for this workload."""
+    import hashlib
+
+    src = os.path.join(ROOT, "mixture_experts_ffn_amd", "csrc", "gemm_mfma.hip")
+    table = os.path.join(ROOT, "profiles", "traffic_gemm1.txt")
+    if not (os.path.exists(src) and os.path.exists(table)):
+        return None
+    sha = hashlib.sha1(open(src, "rb").read()).hexdigest()[:12]
+    for line in open(table):
+        parts = line.split()
+        if len(parts) == 4 and parts[0] == workload_name and parts[1] == f"gemm_mfma.hip:{sha}":
+            vals = dict(p.split("=") for p in parts[2:])
+            return float(vals["fetch_bytes"]) + float(vals["write_bytes"])
+    return None
 
 
 def cpu_baseline(w, inp, y_gpu, target_s):

@@ -87,8 +87,11 @@ int check_ptr(const void *ptr, const char *name, size_t align = 16)
     return MOE_FFN_OK;
 }
 
-// The current device must be a gfx950 GPU.  Cached per device ordinal.
-int check_device()
+// The current device must be a gfx950 GPU.  Cached per device ordinal, with
+// its compute-unit count (the persistent kernels launch one workgroup per CU).
+int g_num_cus[64] = {0};
+
+int check_device(int *num_cus = nullptr)
 {
     static std::mutex mu;
     static signed char known[64] = {0}; // 0 unknown, 1 ok, -1 not gfx950
@@ -105,15 +108,19 @@ int check_device()
         if (err != hipSuccess)
             return hip_fail(err, "hipGetDeviceProperties");
         known[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        g_num_cus[dev] = prop.multiProcessorCount;
     }
     if (known[dev] < 0)
         return fail(MOE_FFN_ERR_DEVICE, "device %d is not gfx950", dev);
+    if (num_cus)
+        *num_cus = g_num_cus[dev];
     return MOE_FFN_OK;
 }
 
 moe::FwdTiles pick_tiles(const moe_ffn_problem &p)
 {
     moe::FwdTiles t;
+    t.num_cus = 0;
     if (p.dtype == MOE_FFN_F32) {
         t.BM = 64;
     } else {
@@ -259,7 +266,8 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
         return fail(MOE_FFN_ERR_ALIGN, "saved is not 16-byte aligned");
     if (ws_bytes < L.ws_total)
         return fail(MOE_FFN_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, L.ws_total);
-    if ((rc = check_device()))
+    int num_cus = 0;
+    if ((rc = check_device(&num_cus)))
         return rc;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -315,7 +323,9 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
     g1.max_mtiles = (int)L.max_mtiles;
     record(ev, MOE_FFN_STAGE_GEMM1, true, s);
     const bool fast = moe::fast_gemm_supported(p->dtype, p->H, p->I);
-    HIP_TRY(fast ? moe::launch_fast_gemm1(L.tiles, g1, s)
+    moe::FwdTiles tiles = L.tiles;
+    tiles.num_cus = num_cus;
+    HIP_TRY(fast ? moe::launch_fast_gemm1(tiles, g1, s)
                  : moe::launch_gemm1_swiglu(p->dtype, L.tiles, g1, s),
             "gemm1 launch");
     record(ev, MOE_FFN_STAGE_GEMM1, false, s);
@@ -330,7 +340,7 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
     g2.Nout = (int)p->H;
     g2.ldb = (int)p->H;
     record(ev, MOE_FFN_STAGE_GEMM2, true, s);
-    HIP_TRY(fast ? moe::launch_fast_gemm2(L.tiles, g2, s)
+    HIP_TRY(fast ? moe::launch_fast_gemm2(tiles, g2, s)
                  : moe::launch_gemm2(p->dtype, L.tiles, g2, s),
             "gemm2 launch");
     record(ev, MOE_FFN_STAGE_GEMM2, false, s);

@@ -36,13 +36,16 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int BK = 64;
 constexpr int NSTAGE = 3;
+constexpr int kFastWaves = 8; // two waves per SIMD: one's MFMAs cover the other's LDS waits
+constexpr int kWavesM128 = 1; // waves along M for 128-row tiles (each wave owns all rows)
 
-template <int BM_, bool SWIGLU> struct Cfg {
+template <int BM_, bool SWIGLU, int NW_, int WM_> struct Cfg {
     static constexpr int BM = BM_;
+    static constexpr int NW = NW_; // waves per workgroup (4 or 8)
     static constexpr int NPANEL = SWIGLU ? 2 : 1;
     static constexpr int PW = SWIGLU ? 128 : 256; // weight columns per panel
-    static constexpr int WAVES_M = BM == 128 ? 2 : 1;
-    static constexpr int WAVES_N = 4 / WAVES_M;
+    static constexpr int WAVES_M = WM_;           // waves along M
+    static constexpr int WAVES_N = NW / WAVES_M;
     static constexpr int WTM = BM / WAVES_M;        // rows per wave
     static constexpr int WTN = PW / WAVES_N;        // columns per wave per panel
     static constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -50,10 +53,11 @@ template <int BM_, bool SWIGLU> struct Cfg {
     static constexpr int B_BYTES = BK * NPANEL * PW * 2; // 32 KB
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
-    static constexpr int A_LOADS = A_BYTES / 1024 / 4; // per wave per stage
-    static constexpr int B_LOADS = B_BYTES / 1024 / 4;
-    static constexpr int ROWS_PER_BCHUNK = 1024 / (PW * 2);
-    static_assert(A_LOADS >= 1 && B_LOADS == 8, "stage split");
+    static constexpr int A_LOADS = A_BYTES / 1024 / NW; // per wave per stage
+    static constexpr int B_LOADS = B_BYTES / 1024 / NW;
+    static_assert(A_LOADS >= 1 && B_LOADS * NW * 1024 == B_BYTES, "stage split");
+    static_assert(A_LOADS * NW * 1024 == A_BYTES, "stage split");
+    static_assert(FM >= 1 && FN >= 1, "wave tile");
 };
 
 __device__ __forceinline__ int bswz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
@@ -92,23 +96,21 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <int BM, bool SWIGLU, bool GATHER>
-__global__ __launch_bounds__(256, 1) void moe_gemm_bf16(GroupedGemmArgs args)
-{
-    using C = Cfg<BM, SWIGLU>;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * C::STAGE_BYTES];
+struct TileInfo {
+    int e, row0, rows, n0;
+};
 
-    // ---- tile decode (same order as the generic kernels)
-    const int out_tile = SWIGLU ? C::PW : C::NPANEL * C::PW; // output columns per tile
-    const int ntn = args.Nout / out_tile;
-    const int g8 = gridDim.x >> 3;
-    const int L = (blockIdx.x & 7) * g8 + (blockIdx.x >> 3);
-    const int total_mt = args.mtile_off[args.E];
-    if (L >= total_mt * ntn)
-        return;
-    const int e = args.mtile_expert[L / ntn];
-    const int mt0 = args.mtile_off[e];
-    const int mt_e = args.mtile_off[e + 1] - mt0;
+// Logical tile L -> (expert, first permuted row, real rows, first output
+// column).  Order: expert-major; inside an expert, groups of up to 8 M-tiles
+// with N-tiles outer and M-tiles inner, so consecutive tiles share a weight
+// panel.  All operands are wave-uniform (scalar loads).
+__device__ __forceinline__ TileInfo decode_tile(const GroupedGemmArgs &args, int L, int ntn,
+                                                int BM, int out_tile)
+{
+    TileInfo t;
+    t.e = args.mtile_expert[L / ntn];
+    const int mt0 = args.mtile_off[t.e];
+    const int mt_e = args.mtile_off[t.e + 1] - mt0;
     const int local = L - mt0 * ntn;
     constexpr int GM = 8;
     const int grp = local / (GM * ntn);
@@ -117,75 +119,107 @@ __global__ __launch_bounds__(256, 1) void moe_gemm_bf16(GroupedGemmArgs args)
     const int rr = local - grp * GM * ntn;
     const int n_t = rr / gm;
     const int m_t = first_m + rr % gm;
-    const int row0 = args.offsets[e] + m_t * BM;
-    const int rows = min(BM, args.offsets[e + 1] - row0);
-    const int n0 = n_t * out_tile;
-    const int Kdim = args.Kdim, Nout = args.Nout, ldb = args.ldb;
+    t.row0 = args.offsets[t.e] + m_t * BM;
+    t.rows = min(BM, args.offsets[t.e + 1] - t.row0);
+    t.n0 = n_t * out_tile;
+    return t;
+}
 
+// Persistent grouped GEMM: gridDim.x workgroups (a multiple of 8, one per CU)
+// walk the logical tiles.  The hardware hands workgroups to the 8 XCDs round
+// robin, so workgroup b sits on XCD b % 8; each XCD owns one contiguous eighth
+// of the tile order and its workgroups take consecutive tiles of it, so the
+// tiles in flight on one XCD share weight panels and token rows in its L2.
+// The K loop runs continuously across a workgroup's tiles: the copies of the
+// next tile's first two K steps are in flight while the current tile's last
+// steps and its epilogue run.
+template <int BM, bool SWIGLU, bool GATHER, int NW, int WM>
+__global__ __launch_bounds__(64 * NW, 1) void moe_gemm_bf16(GroupedGemmArgs args)
+{
+    using C = Cfg<BM, SWIGLU, NW, WM>;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * C::STAGE_BYTES];
+
+    const int out_tile = SWIGLU ? C::PW : C::NPANEL * C::PW; // output columns per tile
+    const int ntn = args.Nout / out_tile;
+    const int total = args.mtile_off[args.E] * ntn;
+    const int per_xcd_wg = gridDim.x >> 3;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int range = (total + 7) >> 3;
+    const int hi = min((xcd + 1) * range, total);
+    int L = xcd * range + slot;
+    if (L >= hi)
+        return;
+
+    const int Kdim = args.Kdim, Nout = args.Nout, ldb = args.ldb;
+    const int nk = Kdim / BK;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-
     const bf16 *__restrict__ A = static_cast<const bf16 *>(args.A);
-    const bf16 *__restrict__ W = static_cast<const bf16 *>(args.B) + (int64_t)e * Kdim * ldb;
 
-    // ---- per-lane copy sources
-    // A: chunk c covers rows 8c .. 8c+7; this lane fills 16-byte unit `lane`
-    const bf16 *a_src[C::A_LOADS];
+    // per-lane copy sources of one tile
+    struct Src {
+        const bf16 *a[C::A_LOADS];
+        const bf16 *b[C::B_LOADS];
+    };
+    auto make_src = [&](const TileInfo &t, Src &sr) {
 #pragma unroll
-    for (int i = 0; i < C::A_LOADS; ++i) {
-        const int c = wave * C::A_LOADS + i;
-        const int r = c * 8 + (lane >> 3);
-        const int piece = (lane & 7) ^ ((r >> 1) & 7);
-        const int rc = r < rows ? r : 0; // tail rows copy row 0; never stored
-        int64_t grow;
-        if (GATHER)
-            grow = args.sorted_slot[row0 + rc] / args.topk;
-        else
-            grow = row0 + rc;
-        a_src[i] = A + grow * Kdim + piece * 8;
-    }
-    // B: chunk c covers 1024 bytes = 4 (SwiGLU panels) or 2 k-rows of one panel
-    const bf16 *b_src[C::B_LOADS];
+        for (int i = 0; i < C::A_LOADS; ++i) {
+            // chunk c covers rows 8c .. 8c+7; this lane fills 16-byte unit `lane`
+            const int c = wave * C::A_LOADS + i;
+            const int r = c * 8 + (lane >> 3);
+            const int piece = (lane & 7) ^ ((r >> 1) & 7);
+            int64_t grow;
+            if constexpr (GATHER) {
+                // the 8 row indices of the chunk are wave-uniform: scalar loads
+                int idx[8];
 #pragma unroll
-    for (int i = 0; i < C::B_LOADS; ++i) {
-        const int c = wave * C::B_LOADS + i;
-        int panel, kr, pp;
-        if (SWIGLU) {
-            panel = c >> 4;
-            kr = (c & 15) * 4 + (lane >> 4);
-            pp = lane & 15;
-        } else {
-            panel = 0;
-            kr = c * 2 + (lane >> 5);
-            pp = lane & 31;
+                for (int j = 0; j < 8; ++j) {
+                    const int rj = c * 8 + j < t.rows ? c * 8 + j : 0; // tail rows copy row 0
+                    idx[j] = args.sorted_slot[t.row0 + rj];
+                }
+                int v = idx[0];
+#pragma unroll
+                for (int j = 1; j < 8; ++j)
+                    v = (lane >> 3) == j ? idx[j] : v;
+                grow = v / args.topk;
+            } else {
+                grow = t.row0 + (r < t.rows ? r : 0);
+            }
+            sr.a[i] = A + grow * Kdim + piece * 8;
         }
-        const int u = (pp >> 1) ^ bswz(kr);
-        const int col = n0 + panel * Nout + (2 * u + (pp & 1)) * 8;
-        b_src[i] = W + (int64_t)kr * ldb + col;
-    }
-
-    auto issue = [&](int kb, unsigned char *sbase) {
+        const bf16 *W = static_cast<const bf16 *>(args.B) + (int64_t)t.e * Kdim * ldb;
+#pragma unroll
+        for (int i = 0; i < C::B_LOADS; ++i) {
+            // chunk c covers 1024 bytes = 4 (SwiGLU panels) or 2 k-rows of one panel
+            const int c = wave * C::B_LOADS + i;
+            int panel, kr, pp;
+            if constexpr (SWIGLU) {
+                panel = c >> 4;
+                kr = (c & 15) * 4 + (lane >> 4);
+                pp = lane & 15;
+            } else {
+                panel = 0;
+                kr = c * 2 + (lane >> 5);
+                pp = lane & 31;
+            }
+            const int u = (pp >> 1) ^ bswz(kr);
+            const int col = t.n0 + panel * Nout + (2 * u + (pp & 1)) * 8;
+            sr.b[i] = W + (int64_t)kr * ldb + col;
+        }
+    };
+    auto issue = [&](const Src &sr, int kb, unsigned char *sbase) {
         const int k0 = kb * BK;
 #pragma unroll
         for (int i = 0; i < C::A_LOADS; ++i)
-            g2l16(a_src[i] + k0, (lds_void *)(sbase + (wave * C::A_LOADS + i) * 1024));
+            g2l16(sr.a[i] + k0, (lds_void *)(sbase + (wave * C::A_LOADS + i) * 1024));
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i)
-            g2l16(b_src[i] + (int64_t)k0 * ldb,
+            g2l16(sr.b[i] + (int64_t)k0 * ldb,
                   (lds_void *)(sbase + C::A_BYTES + (wave * C::B_LOADS + i) * 1024));
     };
 
     f32x4 acc[C::NPANEL][C::FM][C::FN];
-#pragma unroll
-    for (int p = 0; p < C::NPANEL; ++p)
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn)
-                acc[p][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // fragment addressing
     const int fr = lane & 15;                      // A: row within a 16-row block
     const int fk = lane >> 4;                      // A: piece in a 32-k step; B: 8-k group
     const int tq = lane & 3, tr = (lane >> 2) & 3; // B transposing read: column part / row
@@ -227,79 +261,111 @@ __global__ __launch_bounds__(256, 1) void moe_gemm_bf16(GroupedGemmArgs args)
         }
     };
 
-    const int nk = Kdim / BK;
-    constexpr int NL = C::A_LOADS + C::B_LOADS;
-    issue(0, smem);
-    if (nk > 1)
-        issue(1, smem + C::STAGE_BYTES);
-    int s_cur = 0; // stage of step kb (kb % 3)
-    for (int kb = 0; kb < nk; ++kb) {
-        // wait for this wave's copies of step kb, publish the stage, then
-        // start the copies of step kb + 2 into the stage step kb - 1 used
-        if (kb + 1 < nk)
-            wait_vm<NL>();
-        else
-            wait_vm<0>();
-        lds_barrier();
-        const int s_next = s_cur == 0 ? 2 : s_cur - 1; // (kb + 2) % 3
-        if (kb + 2 < nk)
-            issue(kb + 2, smem + s_next * C::STAGE_BYTES);
-        compute(smem + s_cur * C::STAGE_BYTES);
-        s_cur = s_cur == 2 ? 0 : s_cur + 1;
-    }
-
-    // ---- epilogue: lane owns row (lane & 15) and columns 4*(lane >> 4) + [0, 4)
-    bf16 *__restrict__ Cout = static_cast<bf16 *>(args.C);
-    bf16 *__restrict__ Hs = static_cast<bf16 *>(args.Hsave);
+    // epilogue: lane owns row (lane & 15) and columns 4*(lane >> 4) + [0, 4)
+    auto epilogue = [&](const TileInfo &t) {
+        bf16 *__restrict__ Cout = static_cast<bf16 *>(args.C);
+        bf16 *__restrict__ Hs = static_cast<bf16 *>(args.Hsave);
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm) {
-        const int r = wm * C::WTM + fm * 16 + (lane & 15);
-        if (r >= rows)
-            continue;
-        const int64_t p = row0 + r;
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int r = wm * C::WTM + fm * 16 + (lane & 15);
+            if (r >= t.rows)
+                continue;
+            const int64_t p = t.row0 + r;
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) {
-            const int c = n0 + wn * C::WTN + fn * 16 + 4 * (lane >> 4);
-            if constexpr (SWIGLU) {
-                u32x2 outv, gv, uv;
-                bf16 *o = reinterpret_cast<bf16 *>(&outv);
-                bf16 *go = reinterpret_cast<bf16 *>(&gv);
-                bf16 *uo = reinterpret_cast<bf16 *>(&uv);
+            for (int fn = 0; fn < C::FN; ++fn) {
+                const int c = t.n0 + wn * C::WTN + fn * 16 + 4 * (lane >> 4);
+                if constexpr (SWIGLU) {
+                    u32x2 outv, gv, uv;
+                    bf16 *o = reinterpret_cast<bf16 *>(&outv);
+                    bf16 *go = reinterpret_cast<bf16 *>(&gv);
+                    bf16 *uo = reinterpret_cast<bf16 *>(&uv);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float g = acc[0][fm][fn][i], u = acc[1][fm][fn][i];
-                    o[i] = static_cast<bf16>(silu_f(g) * u);
-                    go[i] = static_cast<bf16>(g);
-                    uo[i] = static_cast<bf16>(u);
+                    for (int i = 0; i < 4; ++i) {
+                        const float g = acc[0][fm][fn][i], u = acc[1][fm][fn][i];
+                        o[i] = static_cast<bf16>(silu_f(g) * u);
+                        go[i] = static_cast<bf16>(g);
+                        uo[i] = static_cast<bf16>(u);
+                    }
+                    *reinterpret_cast<u32x2 *>(Cout + p * Nout + c) = outv;
+                    if (Hs) {
+                        *reinterpret_cast<u32x2 *>(Hs + p * 2 * Nout + c) = gv;
+                        *reinterpret_cast<u32x2 *>(Hs + p * 2 * Nout + Nout + c) = uv;
+                    }
+                } else {
+                    u32x2 outv;
+                    bf16 *o = reinterpret_cast<bf16 *>(&outv);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        o[i] = static_cast<bf16>(acc[0][fm][fn][i]);
+                    *reinterpret_cast<u32x2 *>(Cout + p * Nout + c) = outv;
                 }
-                *reinterpret_cast<u32x2 *>(Cout + p * Nout + c) = outv;
-                if (Hs) {
-                    *reinterpret_cast<u32x2 *>(Hs + p * 2 * Nout + c) = gv;
-                    *reinterpret_cast<u32x2 *>(Hs + p * 2 * Nout + Nout + c) = uv;
-                }
-            } else {
-                u32x2 outv;
-                bf16 *o = reinterpret_cast<bf16 *>(&outv);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    o[i] = static_cast<bf16>(acc[0][fm][fn][i]);
-                *reinterpret_cast<u32x2 *>(Cout + p * Nout + c) = outv;
             }
+        }
+    };
+
+    constexpr int NL = C::A_LOADS + C::B_LOADS;
+    TileInfo cur = decode_tile(args, L, ntn, BM, out_tile);
+    Src scur, snext;
+    make_src(cur, scur);
+    int Lnext = L + per_xcd_wg;
+    bool has_next = Lnext < hi;
+    TileInfo nxt = cur;
+    if (has_next) {
+        nxt = decode_tile(args, Lnext, ntn, BM, out_tile);
+        make_src(nxt, snext);
+    }
+    // prologue: the first two K steps (nk >= 2 on this path)
+    issue(scur, 0, smem);
+    issue(scur, 1, smem + C::STAGE_BYTES);
+    int s_cur = 0; // stage of the current step (global step index % 3)
+    while (true) {
+#pragma unroll
+        for (int p = 0; p < C::NPANEL; ++p)
+#pragma unroll
+            for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < C::FN; ++fn)
+                    acc[p][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < nk; ++kb) {
+            // wait for this wave's copies of the current step (the next step's
+            // may stay in flight), publish the stage, then start the copies of
+            // the step after next into the stage the previous step used
+            if (kb + 1 < nk || has_next)
+                wait_vm<NL>();
+            else
+                wait_vm<0>();
+            lds_barrier();
+            const int s_next = s_cur == 0 ? 2 : s_cur - 1; // (step + 2) % 3
+            if (kb + 2 < nk)
+                issue(scur, kb + 2, smem + s_next * C::STAGE_BYTES);
+            else if (has_next)
+                issue(snext, kb + 2 - nk, smem + s_next * C::STAGE_BYTES);
+            compute(smem + s_cur * C::STAGE_BYTES);
+            s_cur = s_cur == 2 ? 0 : s_cur + 1;
+        }
+        epilogue(cur);
+        if (!has_next)
+            break;
+        cur = nxt;
+        scur = snext;
+        Lnext += per_xcd_wg;
+        has_next = Lnext < hi;
+        if (has_next) {
+            nxt = decode_tile(args, Lnext, ntn, BM, out_tile);
+            make_src(nxt, snext);
         }
     }
 }
 
-template <int BM, bool SWIGLU, bool GATHER>
-static hipError_t launch(const GroupedGemmArgs &a, hipStream_t stream)
+template <int BM, bool SWIGLU, bool GATHER, int NW = kFastWaves,
+          int WM = (BM == 128 ? kWavesM128 : 1)>
+static hipError_t launch(const GroupedGemmArgs &a, int num_cus, hipStream_t stream)
 {
-    using C = Cfg<BM, SWIGLU>;
-    auto kern = moe_gemm_bf16<BM, SWIGLU, GATHER>;
-    const int out_tile = SWIGLU ? C::PW : C::NPANEL * C::PW;
-    const int64_t tiles = (int64_t)a.max_mtiles * (a.Nout / out_tile);
-    if (tiles <= 0)
+    auto kern = moe_gemm_bf16<BM, SWIGLU, GATHER, NW, WM>;
+    if (a.max_mtiles <= 0)
         return hipSuccess;
-    const int64_t grid = (tiles + 7) / 8 * 8;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    const int grid = (num_cus + 7) / 8 * 8; // one workgroup per CU, whole XCDs
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NW), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -314,15 +380,15 @@ bool fast_gemm_supported(int dtype, int64_t H, int64_t I)
 hipError_t launch_fast_gemm1(const FwdTiles &t, const GroupedGemmArgs &a, hipStream_t stream)
 {
     if (t.BM == 64)
-        return fast::launch<64, true, true>(a, stream);
-    return fast::launch<128, true, true>(a, stream);
+        return fast::launch<64, true, true>(a, t.num_cus, stream);
+    return fast::launch<128, true, true>(a, t.num_cus, stream);
 }
 
 hipError_t launch_fast_gemm2(const FwdTiles &t, const GroupedGemmArgs &a, hipStream_t stream)
 {
     if (t.BM == 64)
-        return fast::launch<64, false, false>(a, stream);
-    return fast::launch<128, false, false>(a, stream);
+        return fast::launch<64, false, false>(a, t.num_cus, stream);
+    return fast::launch<128, false, false>(a, t.num_cus, stream);
 }
 
 } // namespace moe

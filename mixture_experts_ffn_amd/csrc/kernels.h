@@ -58,7 +58,8 @@ struct GroupedGemmArgs {
 
 // plan-level tile choice for the forward
 struct FwdTiles {
-    int BM; // 64 or 128
+    int BM;       // 64 or 128
+    int num_cus;  // compute units of the device (persistent grids)
 };
 
 hipError_t launch_gemm1_swiglu(int dtype, const FwdTiles &t, const GroupedGemmArgs &a,
