@@ -86,6 +86,16 @@ enum {
     MOE_FFN_NUM_FWD_STAGES = 4
 };
 
+/* Stages of the backward, for the timing hook below. */
+enum {
+    MOE_FFN_STAGE_BWD_ACT_GRAD = 0,   /* dY gather, dY·W2^T with the SwiGLU backward epilogue */
+    MOE_FFN_STAGE_BWD_INPUT_GRAD = 1, /* dh·W1^T per permuted row */
+    MOE_FFN_STAGE_BWD_COMBINE = 2,    /* dx k-ordered sum and d_topk_weights */
+    MOE_FFN_STAGE_BWD_W2_GRAD = 3,    /* d_down_proj_weight */
+    MOE_FFN_STAGE_BWD_W1_GRAD = 4,    /* d_up_proj_weight */
+    MOE_FFN_NUM_BWD_STAGES = 5
+};
+
 /* Optional per-stage timing: hipEvent_t handles created by the caller (see
  * moe_ffn_event_create).  When an entry is non-NULL the library records it on
  * `stream` right before (begin) / after (end) that stage's launches. */
@@ -133,6 +143,32 @@ int moe_ffn_route_workspace_size(const moe_ffn_problem *p, size_t *ws_bytes);
 int moe_ffn_route(const moe_ffn_problem *p, const void *topk_ids, int32_t *counts,
                   int32_t *offsets, int32_t *sorted_slot, int32_t *slot_pos, void *ws,
                   size_t ws_bytes, void *stream);
+
+/* ---- backward ------------------------------------------------------------- */
+
+/* Size of the backward workspace. Pure host function.  The backward supports
+ * bf16 problems (MOE_FFN_ERR_DTYPE for fp32). */
+int moe_ffn_bwd_workspace_size(const moe_ffn_problem *p, uint32_t flags, size_t *ws_bytes);
+
+/* Gradients of y with respect to the inputs, given dy [T, H] and the `saved`
+ * context written by moe_ffn_fwd for the same problem and inputs (section 2.2):
+ * dx [T, H], d_up_proj_weight [E, H, 2I], d_down_proj_weight [E, I, H] in the
+ * problem dtype and d_topk_weights [T, K] fp32.  Outputs are overwritten, not
+ * accumulated; an expert that received no slot gets exact zero gradients. */
+int moe_ffn_bwd(const moe_ffn_problem *p, const void *dy, const void *x, const void *topk_ids,
+                const float *topk_weights, const void *up_proj_weight,
+                const void *down_proj_weight, const void *saved, void *dx,
+                void *d_up_proj_weight, void *d_down_proj_weight, float *d_topk_weights,
+                void *ws, size_t ws_bytes, uint32_t flags, void *stream);
+
+/* moe_ffn_bwd with the per-stage timing hook (ev may be NULL; stages
+ * MOE_FFN_STAGE_BWD_*). */
+int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, const void *topk_ids,
+                   const float *topk_weights, const void *up_proj_weight,
+                   const void *down_proj_weight, const void *saved, void *dx,
+                   void *d_up_proj_weight, void *d_down_proj_weight, float *d_topk_weights,
+                   void *ws, size_t ws_bytes, uint32_t flags, void *stream,
+                   const moe_ffn_stage_events *ev);
 
 /* ---- status and measurement helpers ---------------------------------------- */
 

@@ -36,6 +36,11 @@ __all__ = [
     "moe_ffn_route",
     "read_status",
     "STAGES",
+    "BWD_STAGES",
+    "bwd_workspace_size",
+    "moe_ffn_bwd",
+    "moe_ffn",
+    "MoEFFNFunction",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -47,6 +52,7 @@ _lib = None
 F32, BF16, I32, I64 = 0, 1, 2, 3
 CHECK_IDS = 0x1
 STAGES = ("route", "gemm1", "gemm2", "combine")
+BWD_STAGES = ("act_grad", "input_grad", "dx_combine", "w2_grad", "w1_grad")
 
 ERR_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN",
              5: "ERR_WORKSPACE", 6: "ERR_EXPERT_ID", 7: "ERR_SAVED", 8: "ERR_HIP",
@@ -92,6 +98,10 @@ def load_library():
             "moe_ffn_fwd_ex": [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp,
                                ctypes.POINTER(StageEvents)],
             "moe_ffn_route_workspace_size": [pp, psz],
+            "moe_ffn_bwd_workspace_size": [pp, u32, psz],
+            "moe_ffn_bwd": [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
+            "moe_ffn_bwd_ex": [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp,
+                               ctypes.POINTER(StageEvents)],
             "moe_ffn_route": [pp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_ffn_read_status": [vp, vp, ctypes.POINTER(ctypes.c_int32)],
             "moe_ffn_event_create": [ctypes.POINTER(ctypes.c_void_p)],
@@ -221,6 +231,68 @@ def moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *,
     if return_ws:
         out += (ws,)
     return out[0] if len(out) == 1 else out
+
+
+def bwd_workspace_size(problem: Problem, flags: int = 0) -> int:
+    ws = ctypes.c_size_t()
+    _check(load_library().moe_ffn_bwd_workspace_size(ctypes.byref(problem), flags,
+                                                     ctypes.byref(ws)))
+    return ws.value
+
+
+def moe_ffn_bwd(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved, *,
+                ws=None, stage_events: StageEvents | None = None):
+    """Gradients (dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights) of the layer.
+
+    `saved` is the context returned by ``moe_ffn_fwd(..., save_for_backward=True)`` for the
+    same inputs.  Outputs are freshly allocated and overwritten (never accumulated).
+    """
+    lib = load_library()
+    _require_gpu(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved)
+    prob = make_problem(x, topk_ids, up_proj_weight, down_proj_weight)
+    if dy.shape != x.shape or dy.dtype != x.dtype:
+        raise MoEFFNError(2, "dy must have the shape and dtype of x")
+    ws_bytes = bwd_workspace_size(prob)
+    dev = x.device
+    dx = torch.empty_like(x)
+    d_up = torch.empty_like(up_proj_weight)
+    d_down = torch.empty_like(down_proj_weight)
+    d_topk = torch.empty(topk_ids.shape, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ev = ctypes.byref(stage_events) if stage_events is not None else None
+    with torch.cuda.device(dev):
+        rc = lib.moe_ffn_bwd_ex(ctypes.byref(prob), _ptr(dy), _ptr(x), _ptr(topk_ids),
+                                _ptr(topk_weights), _ptr(up_proj_weight), _ptr(down_proj_weight),
+                                _ptr(saved), _ptr(dx), _ptr(d_up), _ptr(d_down), _ptr(d_topk),
+                                _ptr(ws), ws.numel(), 0, _stream(dev), ev)
+    _check(rc)
+    return dx, d_up, d_down, d_topk
+
+
+class MoEFFNFunction(torch.autograd.Function):
+    """Autograd wrapper: forward saves the library's context (route arrays and the
+    pre-activation), backward returns one gradient per input (None for topk_ids)."""
+
+    @staticmethod
+    def forward(ctx, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight):
+        y, saved = moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
+                               save_for_backward=True)
+        ctx.save_for_backward(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
+                              saved)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, topk_ids, topk_weights, up, down, saved = ctx.saved_tensors
+        dx, d_up, d_down, d_topk = moe_ffn_bwd(dy.contiguous(), x, topk_ids, topk_weights, up,
+                                               down, saved)
+        return dx, None, d_topk, d_up, d_down
+
+
+def moe_ffn(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight):
+    """y = MoE expert-FFN layer; differentiable in x, topk_weights and both weights."""
+    return MoEFFNFunction.apply(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
 
 
 def moe_ffn_route(topk_ids: torch.Tensor, E: int, H: int = 8, I: int = 8):

@@ -208,6 +208,38 @@ RouteLayout route_layout(const moe_ffn_problem &p)
     return R;
 }
 
+// Region offsets inside the backward workspace.
+struct BwdLayout {
+    int BM;
+    int64_t max_mtiles;
+    int dgp_width;
+    size_t mtile_off, mtile_expert, dh, act_g, dgp, dxp, total;
+};
+
+BwdLayout bwd_layout(const moe_ffn_problem &p)
+{
+    BwdLayout B;
+    const int64_t TK = p.T * p.K;
+    const int E = (int)p.E;
+    B.BM = 128;
+    B.max_mtiles = moe::max_mtiles_bound(TK, E, B.BM);
+    B.dgp_width = moe::engine_dgp_width((int)p.I);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + (bytes ? bytes : 1));
+        return at;
+    };
+    B.mtile_off = take(sizeof(int32_t) * (size_t)(E + 1));
+    B.mtile_expert = take(sizeof(int32_t) * (size_t)B.max_mtiles);
+    B.dh = take(2 * (size_t)TK * (size_t)(2 * p.I));
+    B.act_g = take(2 * (size_t)TK * (size_t)p.I);
+    B.dgp = take(sizeof(float) * (size_t)TK * (size_t)B.dgp_width);
+    B.dxp = take(2 * (size_t)TK * (size_t)p.H);
+    B.total = off;
+    return B;
+}
+
 template <typename P> P *at(void *base, size_t off)
 {
     return reinterpret_cast<P *>(static_cast<char *>(base) + off);
@@ -306,44 +338,77 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
             return fail(MOE_FFN_ERR_EXPERT_ID, "topk_ids holds a value outside [0, %d)", E);
     }
 
-    moe::GroupedGemmArgs g1{};
-    g1.A = x;
-    g1.B = up_proj_weight;
-    g1.C = at<void>(ws, L.act);
-    g1.Hsave = saved ? at<void>(saved, L.s_h) : nullptr;
-    g1.sorted_slot = rb.sorted_slot;
-    g1.offsets = rb.offsets;
-    g1.mtile_off = rb.mtile_off;
-    g1.mtile_expert = rb.mtile_expert;
-    g1.Kdim = (int)p->H;
-    g1.Nout = (int)p->I;
-    g1.ldb = (int)(2 * p->I);
-    g1.topk = (int)p->K;
-    g1.E = E;
-    g1.max_mtiles = (int)L.max_mtiles;
-    record(ev, MOE_FFN_STAGE_GEMM1, true, s);
-    const bool fast = moe::fast_gemm_supported(p->dtype, p->H, p->I);
-    moe::FwdTiles tiles = L.tiles;
-    tiles.num_cus = num_cus;
-    HIP_TRY(fast ? moe::launch_fast_gemm1(tiles, g1, s)
-                 : moe::launch_gemm1_swiglu(p->dtype, L.tiles, g1, s),
-            "gemm1 launch");
-    record(ev, MOE_FFN_STAGE_GEMM1, false, s);
+    if (p->dtype == MOE_FFN_BF16) {
+        // bf16: the persistent engine (gemm_engine.hip), any H, I multiple of 8
+        moe::EngineArgs g1{};
+        g1.A = static_cast<const moe::bf16_t *>(x);
+        g1.B = static_cast<const moe::bf16_t *>(up_proj_weight);
+        g1.C = at<moe::bf16_t>(ws, L.act);
+        g1.C2 = saved ? at<moe::bf16_t>(saved, L.s_h) : nullptr;
+        g1.sorted_slot = rb.sorted_slot;
+        g1.offsets = rb.offsets;
+        g1.mtile_off = rb.mtile_off;
+        g1.mtile_expert = rb.mtile_expert;
+        g1.topk = (int)p->K;
+        g1.E = E;
+        g1.N = (int)p->I;
+        g1.Kd = (int)p->H;
+        g1.lda = (int)p->H;
+        g1.ldb = (int)(2 * p->I);
+        g1.ldc = (int)p->I;
+        g1.b_estride = p->H * 2 * p->I;
+        record(ev, MOE_FFN_STAGE_GEMM1, true, s);
+        HIP_TRY(moe::launch_engine(moe::ENG_F1, L.tiles.BM, g1, num_cus, s), "gemm1 launch");
+        record(ev, MOE_FFN_STAGE_GEMM1, false, s);
 
-    moe::GroupedGemmArgs g2 = g1;
-    g2.A = at<void>(ws, L.act);
-    g2.B = down_proj_weight;
-    g2.C = at<void>(ws, L.o);
-    g2.Hsave = nullptr;
-    g2.sorted_slot = nullptr;
-    g2.Kdim = (int)p->I;
-    g2.Nout = (int)p->H;
-    g2.ldb = (int)p->H;
-    record(ev, MOE_FFN_STAGE_GEMM2, true, s);
-    HIP_TRY(fast ? moe::launch_fast_gemm2(tiles, g2, s)
-                 : moe::launch_gemm2(p->dtype, L.tiles, g2, s),
-            "gemm2 launch");
-    record(ev, MOE_FFN_STAGE_GEMM2, false, s);
+        moe::EngineArgs g2 = g1;
+        g2.A = at<moe::bf16_t>(ws, L.act);
+        g2.B = static_cast<const moe::bf16_t *>(down_proj_weight);
+        g2.C = at<moe::bf16_t>(ws, L.o);
+        g2.C2 = nullptr;
+        g2.N = (int)p->H;
+        g2.Kd = (int)p->I;
+        g2.lda = (int)p->I;
+        g2.ldb = (int)p->H;
+        g2.ldc = (int)p->H;
+        g2.b_estride = p->I * p->H;
+        record(ev, MOE_FFN_STAGE_GEMM2, true, s);
+        HIP_TRY(moe::launch_engine(moe::ENG_F2, L.tiles.BM, g2, num_cus, s), "gemm2 launch");
+        record(ev, MOE_FFN_STAGE_GEMM2, false, s);
+    } else {
+        // fp32: the generic kernels (gemm.hip)
+        moe::GroupedGemmArgs g1{};
+        g1.A = x;
+        g1.B = up_proj_weight;
+        g1.C = at<void>(ws, L.act);
+        g1.Hsave = saved ? at<void>(saved, L.s_h) : nullptr;
+        g1.sorted_slot = rb.sorted_slot;
+        g1.offsets = rb.offsets;
+        g1.mtile_off = rb.mtile_off;
+        g1.mtile_expert = rb.mtile_expert;
+        g1.Kdim = (int)p->H;
+        g1.Nout = (int)p->I;
+        g1.ldb = (int)(2 * p->I);
+        g1.topk = (int)p->K;
+        g1.E = E;
+        g1.max_mtiles = (int)L.max_mtiles;
+        record(ev, MOE_FFN_STAGE_GEMM1, true, s);
+        HIP_TRY(moe::launch_gemm1_swiglu(p->dtype, L.tiles, g1, s), "gemm1 launch");
+        record(ev, MOE_FFN_STAGE_GEMM1, false, s);
+
+        moe::GroupedGemmArgs g2 = g1;
+        g2.A = at<void>(ws, L.act);
+        g2.B = down_proj_weight;
+        g2.C = at<void>(ws, L.o);
+        g2.Hsave = nullptr;
+        g2.sorted_slot = nullptr;
+        g2.Kdim = (int)p->I;
+        g2.Nout = (int)p->H;
+        g2.ldb = (int)p->H;
+        record(ev, MOE_FFN_STAGE_GEMM2, true, s);
+        HIP_TRY(moe::launch_gemm2(p->dtype, L.tiles, g2, s), "gemm2 launch");
+        record(ev, MOE_FFN_STAGE_GEMM2, false, s);
+    }
 
     record(ev, MOE_FFN_STAGE_COMBINE, true, s);
     HIP_TRY(moe::launch_combine(p->dtype, at<void>(ws, L.o), rb.slot_pos, topk_weights, y, p->T,
@@ -411,6 +476,167 @@ int moe_ffn_route(const moe_ffn_problem *p, const void *topk_ids, int32_t *count
                               rb, static_cast<hipStream_t>(stream)),
             "route launch");
     return MOE_FFN_OK;
+}
+
+int moe_ffn_bwd_workspace_size(const moe_ffn_problem *p, uint32_t flags, size_t *ws_bytes)
+{
+    (void)flags;
+    g_err[0] = 0;
+    int rc = validate_problem(p);
+    if (rc)
+        return rc;
+    if (!ws_bytes)
+        return fail(MOE_FFN_ERR_NULL, "ws_bytes is NULL");
+    if (p->dtype != MOE_FFN_BF16)
+        return fail(MOE_FFN_ERR_DTYPE, "the backward supports bf16 problems only");
+    *ws_bytes = bwd_layout(*p).total;
+    return MOE_FFN_OK;
+}
+
+int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, const void *topk_ids,
+                   const float *topk_weights, const void *up_proj_weight,
+                   const void *down_proj_weight, const void *saved, void *dx,
+                   void *d_up_proj_weight, void *d_down_proj_weight, float *d_topk_weights,
+                   void *ws, size_t ws_bytes, uint32_t flags, void *stream,
+                   const moe_ffn_stage_events *ev)
+{
+    (void)flags;
+    g_err[0] = 0;
+    int rc = validate_problem(p);
+    if (rc)
+        return rc;
+    if (p->dtype != MOE_FFN_BF16)
+        return fail(MOE_FFN_ERR_DTYPE, "the backward supports bf16 problems only");
+    const BwdLayout B = bwd_layout(*p);
+    const FwdLayout L = fwd_layout(*p);
+    if ((rc = check_ptr(d_up_proj_weight, "d_up_proj_weight")) ||
+        (rc = check_ptr(d_down_proj_weight, "d_down_proj_weight")))
+        return rc;
+    const size_t id_align = p->ids_dtype == MOE_FFN_I64 ? 8 : 4;
+    if (p->T > 0 &&
+        ((rc = check_ptr(dy, "dy")) || (rc = check_ptr(x, "x")) ||
+         (rc = check_ptr(topk_ids, "topk_ids", id_align)) ||
+         (rc = check_ptr(topk_weights, "topk_weights", 4)) ||
+         (rc = check_ptr(up_proj_weight, "up_proj_weight")) ||
+         (rc = check_ptr(down_proj_weight, "down_proj_weight")) ||
+         (rc = check_ptr(saved, "saved")) || (rc = check_ptr(dx, "dx")) ||
+         (rc = check_ptr(d_topk_weights, "d_topk_weights", 4)) || (rc = check_ptr(ws, "ws"))))
+        return rc;
+    if (p->T > 0 && ws_bytes < B.total)
+        return fail(MOE_FFN_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, B.total);
+    int num_cus = 0;
+    if ((rc = check_device(&num_cus)))
+        return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t dw_bytes = 2 * (size_t)p->E * (size_t)p->H * (size_t)p->I;
+    if (p->T == 0) {
+        // no slot reached any expert: the weight gradients are exactly zero
+        HIP_TRY(moe::launch_zero_fill(d_up_proj_weight, 2 * dw_bytes, s), "zero fill");
+        HIP_TRY(moe::launch_zero_fill(d_down_proj_weight, dw_bytes, s), "zero fill");
+        return MOE_FFN_OK;
+    }
+    const int E = (int)p->E, I = (int)p->I, H = (int)p->H;
+    void *sv = const_cast<void *>(saved);
+    const int32_t *counts = at<int32_t>(sv, L.s_counts);
+    const int32_t *offsets = at<int32_t>(sv, L.s_offsets);
+    const int32_t *sorted_slot = at<int32_t>(sv, L.s_sorted);
+    const int32_t *slot_pos = at<int32_t>(sv, L.s_slotpos);
+    const moe::bf16_t *h = at<moe::bf16_t>(sv, L.s_h);
+    int32_t *mtile_off = at<int32_t>(ws, B.mtile_off);
+    int32_t *mtile_expert = at<int32_t>(ws, B.mtile_expert);
+    moe::bf16_t *dh = at<moe::bf16_t>(ws, B.dh);
+    moe::bf16_t *act_g = at<moe::bf16_t>(ws, B.act_g);
+    float *dgp = at<float>(ws, B.dgp);
+    moe::bf16_t *dxp = at<moe::bf16_t>(ws, B.dxp);
+
+    HIP_TRY(moe::launch_build_mtiles(counts, E, B.BM, mtile_off, mtile_expert, s), "mtiles");
+
+    moe::EngineArgs base{};
+    base.sorted_slot = sorted_slot;
+    base.offsets = offsets;
+    base.mtile_off = mtile_off;
+    base.mtile_expert = mtile_expert;
+    base.topk = (int)p->K;
+    base.E = E;
+
+    // act_grad with the SwiGLU backward in its epilogue: dh, act_g, d_g partials
+    moe::EngineArgs a2 = base;
+    a2.A = static_cast<const moe::bf16_t *>(dy);
+    a2.B = static_cast<const moe::bf16_t *>(down_proj_weight);
+    a2.C = dh;
+    a2.C2 = act_g;
+    a2.Hs = h;
+    a2.gates = topk_weights;
+    a2.dgp = dgp;
+    a2.dgp_stride = B.dgp_width;
+    a2.N = I;
+    a2.Kd = H;
+    a2.lda = H;
+    a2.ldb = H;
+    a2.b_estride = (int64_t)I * H;
+    record(ev, MOE_FFN_STAGE_BWD_ACT_GRAD, true, s);
+    HIP_TRY(moe::launch_engine(moe::ENG_B2, B.BM, a2, num_cus, s), "act_grad launch");
+    record(ev, MOE_FFN_STAGE_BWD_ACT_GRAD, false, s);
+
+    // input_grad: dx_perm = dh W1[e]^T
+    moe::EngineArgs a4 = base;
+    a4.A = dh;
+    a4.B = static_cast<const moe::bf16_t *>(up_proj_weight);
+    a4.C = dxp;
+    a4.N = H;
+    a4.Kd = 2 * I;
+    a4.lda = 2 * I;
+    a4.ldb = 2 * I;
+    a4.ldc = H;
+    a4.b_estride = (int64_t)H * 2 * I;
+    record(ev, MOE_FFN_STAGE_BWD_INPUT_GRAD, true, s);
+    HIP_TRY(moe::launch_engine(moe::ENG_B4, B.BM, a4, num_cus, s), "input_grad launch");
+    record(ev, MOE_FFN_STAGE_BWD_INPUT_GRAD, false, s);
+
+    record(ev, MOE_FFN_STAGE_BWD_COMBINE, true, s);
+    HIP_TRY(moe::launch_combine_bwd(dxp, dgp, B.dgp_width, slot_pos, dx, d_topk_weights, p->T, H,
+                                    (int)p->K, s),
+            "dx combine launch");
+    record(ev, MOE_FFN_STAGE_BWD_COMBINE, false, s);
+
+    // W2Grad: dW2[e] = act_g^T dY_perm
+    moe::EngineArgs a5 = base;
+    a5.A = act_g;
+    a5.B = static_cast<const moe::bf16_t *>(dy);
+    a5.C = static_cast<moe::bf16_t *>(d_down_proj_weight);
+    a5.M = I;
+    a5.N = H;
+    a5.lda = I;
+    a5.ldb = H;
+    record(ev, MOE_FFN_STAGE_BWD_W2_GRAD, true, s);
+    HIP_TRY(moe::launch_engine(moe::ENG_B5, B.BM, a5, num_cus, s), "W2Grad launch");
+    record(ev, MOE_FFN_STAGE_BWD_W2_GRAD, false, s);
+
+    // W1Grad: dW1[e] = x_perm^T dh
+    moe::EngineArgs a7 = base;
+    a7.A = static_cast<const moe::bf16_t *>(x);
+    a7.B = dh;
+    a7.C = static_cast<moe::bf16_t *>(d_up_proj_weight);
+    a7.M = H;
+    a7.N = 2 * I;
+    a7.lda = H;
+    a7.ldb = 2 * I;
+    record(ev, MOE_FFN_STAGE_BWD_W1_GRAD, true, s);
+    HIP_TRY(moe::launch_engine(moe::ENG_B7, B.BM, a7, num_cus, s), "W1Grad launch");
+    record(ev, MOE_FFN_STAGE_BWD_W1_GRAD, false, s);
+    (void)topk_ids;
+    return MOE_FFN_OK;
+}
+
+int moe_ffn_bwd(const moe_ffn_problem *p, const void *dy, const void *x, const void *topk_ids,
+                const float *topk_weights, const void *up_proj_weight,
+                const void *down_proj_weight, const void *saved, void *dx,
+                void *d_up_proj_weight, void *d_down_proj_weight, float *d_topk_weights,
+                void *ws, size_t ws_bytes, uint32_t flags, void *stream)
+{
+    return moe_ffn_bwd_ex(p, dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
+                          saved, dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights, ws,
+                          ws_bytes, flags, stream, nullptr);
 }
 
 int moe_ffn_read_status(const void *ws, void *stream, int32_t *device_status)

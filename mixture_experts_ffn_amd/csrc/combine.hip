@@ -50,6 +50,83 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ o,
     }
 }
 
+// Backward combine (issue page, section 2.2 "Combine(dX)"): one workgroup per
+// token sums its K rows of dx_perm in k order (no gate: it is already inside
+// dh) and finishes d_topk_weights[t, k] by summing that row's partial dots in a
+// fixed order.  Deterministic; a dropped slot (slot_pos = -1) gives 0.
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16 *__restrict__ dxp,
+                                                          const float *__restrict__ dgp,
+                                                          int dgp_stride,
+                                                          const int32_t *__restrict__ slot_pos,
+                                                          bf16 *__restrict__ dx,
+                                                          float *__restrict__ d_topk, int H, int K)
+{
+    const int64_t t = blockIdx.x;
+    const int nch = H / 8;
+    for (int c = threadIdx.x; c < nch; c += 256) {
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc[j] = 0.f;
+        for (int k = 0; k < K; ++k) {
+            const int32_t p = slot_pos[t * K + k];
+            if (p < 0)
+                continue;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(dxp + (int64_t)p * H + (int64_t)c * 8);
+            const bf16 *vv = reinterpret_cast<const bf16 *>(&v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[j] += static_cast<float>(vv[j]);
+        }
+        u32x4 out;
+        bf16 *oo = reinterpret_cast<bf16 *>(&out);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            oo[j] = static_cast<bf16>(acc[j]);
+        *reinterpret_cast<u32x4 *>(dx + t * H + (int64_t)c * 8) = out;
+    }
+    // d_topk: wave 0, one lane per k
+    if (threadIdx.x < K) {
+        const int k = threadIdx.x;
+        const int32_t p = slot_pos[t * K + k];
+        float d = 0.f;
+        if (p >= 0)
+            for (int j = 0; j < dgp_stride; ++j)
+                d += dgp[(int64_t)p * dgp_stride + j];
+        d_topk[t * K + k] = d;
+    }
+}
+
+hipError_t launch_combine_bwd(const void *dxp, const float *dgp, int dgp_stride,
+                              const int32_t *slot_pos, void *dx, float *d_topk, int64_t T, int H,
+                              int K, hipStream_t stream)
+{
+    if (T <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)T), dim3(256), 0, stream,
+                       static_cast<const bf16 *>(dxp), dgp, dgp_stride, slot_pos,
+                       static_cast<bf16 *>(dx), d_topk, H, K);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(u32x4 *__restrict__ p, int64_t n)
+{
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = z;
+}
+
+hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t stream)
+{
+    const int64_t n = (int64_t)(bytes / 16);
+    if (n <= 0)
+        return hipSuccess;
+    const int64_t blocks = n / 256 + 1 < 4096 ? n / 256 + 1 : 4096;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<u32x4 *>(p), n);
+    return hipGetLastError();
+}
+
 hipError_t launch_combine(int dtype, const void *o, const int32_t *slot_pos, const float *gates,
                           void *y, int64_t T, int H, int K, hipStream_t stream)
 {

@@ -1,0 +1,677 @@
+// gemm_engine.hip — the bf16 grouped-GEMM engine of the MoE expert FFN on
+// gfx950 matrix cores: all six contractions of the layer, forward and
+// backward, as instances of one persistent, LDS-pipelined kernel.
+//
+// The contractions (HyperMegaMoE issue page, section 2.1 "forward fusion" and
+// section 2.2 "backward fusion"); p is a permuted (expert-contiguous) row,
+// t_p its token, g_p its gate, e its expert:
+//
+//   F1  act = SwiGLU(x[t_p] · W1[e])        M = rows of e, N = I, K = H
+//   F2  o   = act[p] · W2[e]                M = rows of e, N = H, K = I
+//   B2  u   = dY[t_p] · W2[e]^T, epilogue:  M = rows of e, N = I, K = H
+//       dact = g_p u, dh = [dact ⊙ b ⊙ σ(a)(1 + a(1-σ(a))), dact ⊙ silu(a)],
+//       act_g = g_p silu(a) ⊙ b and per-row partials of Σ_i u·act (= d_g)
+//   B4  dx_p = dh[p] · W1[e]^T              M = rows of e, N = H, K = 2I
+//   B5  dW2[e] = Σ_p act_g[p]^T dY[t_p]     M = I, N = H, K = rows of e
+//   B7  dW1[e] = Σ_p x[t_p]^T dh[p]         M = H, N = 2I, K = rows of e
+//
+// Operand layouts in memory decide the LDS layout and the fragment read:
+//  * KROW: the operand's M (or N) rows are contiguous along K (x, act, dY,
+//    dh rows; W2 rows for B2; W1 rows for B4).  LDS tile [R][64] with the
+//    16-byte piece index XOR-ed by (row / 2) % 8; fragments are one 128-bit
+//    LDS read.
+//  * KCOL: memory rows are K indices, contiguous along M (or N) (W1/W2 in
+//    the forward; act_g, dY, x, dh rows in the weight gradients).  LDS tile
+//    [64][R] untransposed with the 32-byte unit index XOR-ed by a 3-bit hash
+//    of k; fragments are two transposing 64-bit LDS reads.
+//  Both swizzles were measured conflict-free.  Copies go global -> LDS
+//  directly (16 bytes per lane); pieces outside the problem (K or N edges,
+//  rows past an expert's count in the weight gradients) copy from a zero
+//  page, so no tile needs a special path.
+//
+// Pipeline: one 512-thread workgroup per CU, 3-stage LDS ring, copies two K
+// steps ahead.  A producer cursor walks the workgroup's tile sequence two
+// steps ahead of the consumer, across tile boundaries and over tiles without
+// K steps (empty experts), so the next tile's first copies overlap the
+// current tile's tail and epilogue.  Each wave waits only for its own copies
+// of the stage it consumes (vmcnt), then one barrier publishes the stage.
+//
+// Matrix-core step: v_mfma_f32_16x16x32_bf16 with the B fragment as the first
+// operand, so the accumulator block is C^T and each lane holds row
+// (lane % 16) and columns 4 (lane / 16) + [0, 4) of a 16x16 block.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace eng {
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+constexpr int BK = 64;
+constexpr int NSTAGE = 3;
+constexpr int NW = 8; // waves per workgroup: two per SIMD
+
+// A page of zeros that out-of-problem pieces copy from.
+__device__ __attribute__((aligned(256))) const uint32_t kZeroPage[64] = {0};
+
+enum Kind { F1 = 0, F2 = 1, B2 = 2, B4 = 3, B5 = 4, B7 = 5 };
+enum Lay { KROW = 0, KCOL = 1 };
+
+template <int KIND> struct KindTraits;
+// token-tiled kinds: M = permuted rows of one expert
+template <> struct KindTraits<F1> {
+    static constexpr bool TOKEN_M = true, A_GATHER = true, B_GATHER = false, PAIRED = true;
+    static constexpr int ALAY = KROW, BLAY = KCOL;
+};
+template <> struct KindTraits<F2> {
+    static constexpr bool TOKEN_M = true, A_GATHER = false, B_GATHER = false, PAIRED = false;
+    static constexpr int ALAY = KROW, BLAY = KCOL;
+};
+template <> struct KindTraits<B2> {
+    static constexpr bool TOKEN_M = true, A_GATHER = true, B_GATHER = false, PAIRED = false;
+    static constexpr int ALAY = KROW, BLAY = KROW;
+};
+template <> struct KindTraits<B4> {
+    static constexpr bool TOKEN_M = true, A_GATHER = false, B_GATHER = false, PAIRED = false;
+    static constexpr int ALAY = KROW, BLAY = KROW;
+};
+// feature-tiled kinds: K = permuted rows of one expert
+template <> struct KindTraits<B5> {
+    static constexpr bool TOKEN_M = false, A_GATHER = false, B_GATHER = true, PAIRED = false;
+    static constexpr int ALAY = KCOL, BLAY = KCOL;
+};
+template <> struct KindTraits<B7> {
+    static constexpr bool TOKEN_M = false, A_GATHER = true, B_GATHER = false, PAIRED = false;
+    static constexpr int ALAY = KCOL, BLAY = KCOL;
+};
+
+template <int KIND, int BM_, int WM_> struct Cfg {
+    using KT = KindTraits<KIND>;
+    static constexpr int BM = BM_;
+    static constexpr int BNT = 256;                      // B columns staged per tile
+    static constexpr int PW = KT::PAIRED ? 128 : 256;    // columns per panel
+    static constexpr int NPANEL = KT::PAIRED ? 2 : 1;
+    static constexpr int OUT_N = KT::PAIRED ? 128 : 256; // output columns per tile
+    static constexpr int WAVES_M = WM_;
+    static constexpr int WAVES_N = NW / WAVES_M;
+    static constexpr int WTM = BM / WAVES_M;
+    static constexpr int WTN = PW / WAVES_N; // per panel
+    static constexpr int FM = WTM / 16, FN = WTN / 16;
+    static constexpr int A_BYTES = BM * BK * 2;
+    static constexpr int B_BYTES = BK * BNT * 2;
+    static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+    static constexpr int A_LOADS = A_BYTES / 1024 / NW;
+    static constexpr int B_LOADS = B_BYTES / 1024 / NW;
+    static constexpr int NL = A_LOADS + B_LOADS;
+    static_assert(A_LOADS * NW * 1024 == A_BYTES && B_LOADS * NW * 1024 == B_BYTES, "split");
+    static_assert(FM >= 1 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
+    static_assert(NSTAGE * STAGE_BYTES <= 160 * 1024, "LDS");
+};
+
+__device__ __forceinline__ int bswz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+
+// 16-byte global -> LDS copy per lane into [l, l + 1024) (lane i at l + 16 i),
+// issued as inline assembly so that the compiler does not track these LDS
+// writes: completion is established per stage with wait_vm, instead of the
+// compiler waiting for every copy in flight before each LDS read.  `l` must
+// be wave-uniform.  M0 is not used by any compiler-generated code here.
+__device__ __forceinline__ void g2l16(const void *g, lds_void *l)
+{
+    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_addr), "v"(g)
+                 : "memory", "m0");
+}
+
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N> __device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Barrier of the K loop.  Inside the loop LDS is written only by the
+// global->LDS copies, whose completion each wave establishes itself before
+// arriving, and read only into registers that the matrix cores consume
+// before the wave can arrive again; so no memory fence is needed, only a
+// compiler-level ordering of LDS accesses around the barrier.  (A fence would
+// also wait for the copies of later stages still in flight.)
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+struct TileInfo {
+    int e;     // expert
+    int m0;    // token-tiled: first permuted row; feature-tiled: first feature row
+    int rows;  // valid M rows of the tile
+    int n0;    // first output column
+    int seg0;  // feature-tiled: first permuted row of the expert (K origin)
+    int klen;  // contraction length of the tile (Kd, or the expert's row count)
+    int nk;    // K steps
+};
+
+template <int KIND, int BM, int WM>
+__device__ __forceinline__ TileInfo decode_tile(const EngineArgs &a, int L)
+{
+    using C = Cfg<KIND, BM, WM>;
+    TileInfo t;
+    if constexpr (C::KT::TOKEN_M) {
+        const int ntn = (a.N + C::OUT_N - 1) / C::OUT_N;
+        t.e = a.mtile_expert[L / ntn];
+        const int mt0 = a.mtile_off[t.e];
+        const int mt_e = a.mtile_off[t.e + 1] - mt0;
+        const int local = L - mt0 * ntn;
+        constexpr int GM = 8;
+        const int grp = local / (GM * ntn);
+        const int first_m = grp * GM;
+        const int gm = min(mt_e - first_m, GM);
+        const int rr = local - grp * GM * ntn;
+        const int n_t = rr / gm;
+        const int m_t = first_m + rr % gm;
+        t.m0 = a.offsets[t.e] + m_t * BM;
+        t.rows = min(BM, a.offsets[t.e + 1] - t.m0);
+        t.n0 = n_t * C::OUT_N;
+        t.seg0 = 0;
+        t.klen = a.Kd;
+    } else {
+        const int mtm = (a.M + BM - 1) / BM, ntn = (a.N + C::OUT_N - 1) / C::OUT_N;
+        t.e = L / (mtm * ntn);
+        const int local = L - t.e * mtm * ntn;
+        const int n_t = local / mtm, m_t = local % mtm;
+        t.m0 = m_t * BM;
+        t.rows = min(BM, a.M - t.m0);
+        t.n0 = n_t * C::OUT_N;
+        t.seg0 = a.offsets[t.e];
+        t.klen = a.offsets[t.e + 1] - t.seg0;
+    }
+    t.nk = (t.klen + BK - 1) / BK;
+    return t;
+}
+
+template <int KIND, int BM, int WM>
+__device__ __forceinline__ int total_tiles(const EngineArgs &a)
+{
+    using C = Cfg<KIND, BM, WM>;
+    const int ntn = (a.N + C::OUT_N - 1) / C::OUT_N;
+    if constexpr (C::KT::TOKEN_M)
+        return a.mtile_off[a.E] * ntn;
+    else
+        return a.E * ((a.M + BM - 1) / BM) * ntn;
+}
+
+// Per-lane copy state of one tile.  KROW operands and weight operands are
+// affine in k, so one pointer per chunk suffices; token-row KCOL operands
+// (the weight gradients) look their rows up per K step.
+template <int KIND, int BM, int WM> struct Src {
+    using C = Cfg<KIND, BM, WM>;
+    const bf16 *a[C::A_LOADS];
+    const bf16 *b[C::B_LOADS];
+    int a_k[C::A_LOADS];       // KROW: k offset of the lane's piece
+    int b_k[C::B_LOADS];
+    bool a_col_ok[C::A_LOADS]; // KCOL: column inside the problem
+    bool b_col_ok[C::B_LOADS];
+};
+
+// Memory row of the lane's k-row for a token-row KCOL operand (weight
+// gradients): k-rows kbase .. kbase + KPC - 1 of the chunk are permuted rows
+// seg0 + k; gathered operands read the chunk's KPC row indices with scalar
+// loads (wave-uniform addresses), so the vector-memory counter holds only the
+// copies.  Rows past the expert's count return 0 (their pieces copy zeros).
+template <int RB>
+__device__ __forceinline__ int64_t kcol_token_row(const EngineArgs &a, const TileInfo &t,
+                                                  int kbase, int lane, bool gather)
+{
+    constexpr int KPC = 1024 / RB;
+    const int j = lane / (RB / 16);
+    if (!gather)
+        return (int64_t)t.seg0 + kbase + j;
+    int idx[KPC];
+#pragma unroll
+    for (int q = 0; q < KPC; ++q)
+        idx[q] = kbase + q < t.klen ? a.sorted_slot[t.seg0 + kbase + q] : 0;
+    int v = idx[0];
+#pragma unroll
+    for (int q = 1; q < KPC; ++q)
+        v = j == q ? idx[q] : v;
+    return (int64_t)(v / a.topk);
+}
+
+template <int KIND, int BM, int WM>
+__device__ __forceinline__ void make_src(const EngineArgs &a, const TileInfo &t, int wave, int lane,
+                                         Src<KIND, BM, WM> &s)
+{
+    using C = Cfg<KIND, BM, WM>;
+    using KT = typename C::KT;
+    // ---- A
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i) {
+        const int c = wave * C::A_LOADS + i;
+        if constexpr (KT::ALAY == KROW) {
+            // chunk c: rows 8c .. 8c+7 of the tile, 16-byte unit `lane`
+            const int r = c * 8 + (lane >> 3);
+            const int piece = (lane & 7) ^ ((r >> 1) & 7);
+            int64_t mrow;
+            if constexpr (KT::A_GATHER) {
+                // the chunk's 8 row indices are wave-uniform: scalar loads
+                int idx[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int rj = c * 8 + j < t.rows ? c * 8 + j : 0; // tail rows repeat row 0
+                    idx[j] = a.sorted_slot[t.m0 + rj];
+                }
+                int v = idx[0];
+#pragma unroll
+                for (int j = 1; j < 8; ++j)
+                    v = (lane >> 3) == j ? idx[j] : v;
+                mrow = v / a.topk;
+            } else {
+                mrow = t.m0 + (r < t.rows ? r : 0);
+            }
+            s.a[i] = a.A + mrow * a.lda + piece * 8;
+            s.a_k[i] = piece * 8;
+            s.a_col_ok[i] = true;
+        } else {
+            // KCOL A (feature tiles): chunk c covers 1024 / (2 BM) k-rows of BM columns
+            constexpr int RB = BM * 2;       // bytes per k-row
+            constexpr int KPC = 1024 / RB;   // k-rows per chunk
+            const int pp = lane % (RB / 16); // 16-byte piece within the k-row
+            const int u = (pp >> 1) ^ bswz(c * KPC + lane / (RB / 16));
+            const int col = t.m0 + (2 * u + (pp & 1)) * 8;
+            s.a_col_ok[i] = col < a.M;
+            s.a[i] = a.A + (s.a_col_ok[i] ? col : 0); // row part added per step
+            s.a_k[i] = 0;
+        }
+    }
+    // ---- B
+#pragma unroll
+    for (int i = 0; i < C::B_LOADS; ++i) {
+        const int c = wave * C::B_LOADS + i;
+        if constexpr (KT::BLAY == KROW) {
+            // weight rows n of expert e (B2: W2[e][n][:], B4: W1[e][n][:])
+            const int r = c * 8 + (lane >> 3);
+            const int piece = (lane & 7) ^ ((r >> 1) & 7);
+            const int n = t.n0 + r;
+            const int nc = n < a.N ? n : 0; // tail columns repeat column 0; never stored
+            s.b[i] = a.B + (int64_t)t.e * a.b_estride + (int64_t)nc * a.ldb + piece * 8;
+            s.b_k[i] = piece * 8;
+            s.b_col_ok[i] = true;
+        } else {
+            int panel, kr, pp;
+            if constexpr (KT::PAIRED) { // two 128-column panels: 256-byte k-rows
+                panel = c >> 4;
+                kr = (c & 15) * 4 + (lane >> 4);
+                pp = lane & 15;
+            } else { // one 256-column panel: 512-byte k-rows
+                panel = 0;
+                kr = c * 2 + (lane >> 5);
+                pp = lane & 31;
+            }
+            const int u = (pp >> 1) ^ bswz(kr);
+            const int colp = t.n0 + (2 * u + (pp & 1)) * 8; // column within the panel
+            s.b_col_ok[i] = colp < a.N;
+            s.b_k[i] = 0;
+            const int col = (s.b_col_ok[i] ? colp : 0) + panel * a.N;
+            if constexpr (KT::TOKEN_M) // weight operand: memory rows are k
+                s.b[i] = a.B + (int64_t)t.e * a.b_estride + (int64_t)kr * a.ldb + col;
+            else // token operand: memory row looked up per step
+                s.b[i] = a.B + col;
+        }
+    }
+}
+
+// k-row of lane within chunk c for a KCOL operand with `RB`-byte k-rows
+template <int RB> __device__ __forceinline__ int kcol_krow(int c, int lane)
+{
+    return c * (1024 / RB) + lane / (RB / 16);
+}
+
+template <int KIND, int BM, int WM>
+__device__ __forceinline__ void issue(const EngineArgs &a, const TileInfo &t,
+                                      const Src<KIND, BM, WM> &s, int kb, unsigned char *sbase,
+                                      int wave, int lane)
+{
+    using C = Cfg<KIND, BM, WM>;
+    using KT = typename C::KT;
+    const int k0 = kb * BK;
+    // ---- A
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i) {
+        lds_void *dst = (lds_void *)(sbase + (wave * C::A_LOADS + i) * 1024);
+        const void *src;
+        if constexpr (KT::ALAY == KROW) {
+            src = (k0 + s.a_k[i] < t.klen) ? (const void *)(s.a[i] + k0) : (const void *)kZeroPage;
+        } else {
+            constexpr int RB = BM * 2;
+            const int kr = kcol_krow<RB>(wave * C::A_LOADS + i, lane);
+            const int kk = k0 + kr;
+            const int64_t mrow =
+                kcol_token_row<RB>(a, t, k0 + (wave * C::A_LOADS + i) * (1024 / RB), lane,
+                                   KT::A_GATHER);
+            src = (s.a_col_ok[i] && kk < t.klen) ? (const void *)(s.a[i] + mrow * a.lda)
+                                                  : (const void *)kZeroPage;
+        }
+        g2l16(src, dst);
+    }
+    // ---- B
+#pragma unroll
+    for (int i = 0; i < C::B_LOADS; ++i) {
+        lds_void *dst = (lds_void *)(sbase + C::A_BYTES + (wave * C::B_LOADS + i) * 1024);
+        const void *src;
+        if constexpr (KT::BLAY == KROW) {
+            src = (k0 + s.b_k[i] < t.klen) ? (const void *)(s.b[i] + k0) : (const void *)kZeroPage;
+        } else if constexpr (KT::TOKEN_M) {
+            constexpr int RB = C::PW * 2;
+            const int c = wave * C::B_LOADS + i;
+            const int kr = KT::PAIRED ? (c & 15) * 4 + (lane >> 4) : kcol_krow<RB>(c, lane);
+            src = (s.b_col_ok[i] && k0 + kr < t.klen) ? (const void *)(s.b[i] + (int64_t)k0 * a.ldb)
+                                                       : (const void *)kZeroPage;
+        } else {
+            constexpr int RB = C::PW * 2;
+            const int kr = kcol_krow<RB>(wave * C::B_LOADS + i, lane);
+            const int kk = k0 + kr;
+            const int64_t mrow =
+                kcol_token_row<RB>(a, t, k0 + (wave * C::B_LOADS + i) * (1024 / RB), lane,
+                                   KT::B_GATHER);
+            src = (s.b_col_ok[i] && kk < t.klen) ? (const void *)(s.b[i] + mrow * a.ldb)
+                                                  : (const void *)kZeroPage;
+        }
+        g2l16(src, dst);
+    }
+}
+
+// fragment reads ------------------------------------------------------------
+// KROW tile [R][64]: row r, 8 k values starting at logical piece q
+__device__ __forceinline__ bf16x8 frag_krow(const unsigned char *tile, int r, int q)
+{
+    const int piece = q ^ ((r >> 1) & 7);
+    return *reinterpret_cast<const bf16x8 *>(tile + r * 128 + piece * 16);
+}
+// KCOL tile [64][R] (R*2-byte k-rows): lane's column block nb (multiple of 16),
+// 8 k values starting at k8 (multiple of 8); two transposing reads
+template <int RB>
+__device__ __forceinline__ bf16x8 frag_kcol(const unsigned char *tile, int nb, int k8, int lane)
+{
+    const int col = nb + 4 * (lane & 3);
+    const int tr = (lane >> 2) & 3;
+    v4i16 half[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int kr = k8 + 4 * h + tr;
+        const int u = (col >> 4) ^ bswz(kr);
+        half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16 *)(tile + kr * RB + u * 32 + (col & 15) * 2));
+    }
+    return __builtin_bit_cast(bf16x8,
+                              __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// epilogues ------------------------------------------------------------------
+// lane (fm, fn) element i: row wm*WTM + fm*16 + (lane % 16) of the tile,
+// column wn*WTN + fn*16 + 4 (lane / 16) + i of panel p.
+template <int KIND, int BM, int WM>
+__device__ __forceinline__ void epilogue(const EngineArgs &a, const TileInfo &t,
+                                         f32x4 (&acc)[Cfg<KIND, BM, WM>::NPANEL][Cfg<KIND, BM, WM>::FM]
+                                                     [Cfg<KIND, BM, WM>::FN],
+                                         int wm, int wn, int lane)
+{
+    using C = Cfg<KIND, BM, WM>;
+    auto pack4 = [](float v0, float v1, float v2, float v3) {
+        u32x2 r;
+        bf16 *o = reinterpret_cast<bf16 *>(&r);
+        o[0] = static_cast<bf16>(v0);
+        o[1] = static_cast<bf16>(v1);
+        o[2] = static_cast<bf16>(v2);
+        o[3] = static_cast<bf16>(v3);
+        return r;
+    };
+    const int cl = 4 * (lane >> 4);
+    if constexpr (KIND == B2) {
+        // dact = g u; dh = [dact b σ(a)(1 + a(1-σ(a))), dact silu(a)]; act_g = g silu(a) b;
+        // per-row partial of Σ_i u act over this wave's columns (d_g = g-free row dot)
+        const int I = a.N;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int r = wm * C::WTM + fm * 16 + (lane & 15);
+            const bool rok = r < t.rows;
+            const int64_t p = t.m0 + (rok ? r : 0);
+            const float g = rok ? a.gates[a.sorted_slot[p]] : 0.f;
+            float dg = 0.f;
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) {
+                const int c = t.n0 + wn * C::WTN + fn * 16 + cl;
+                if (rok && c < I) {
+                    const u32x2 hav = *reinterpret_cast<const u32x2 *>(a.Hs + p * 2 * I + c);
+                    const u32x2 hbv = *reinterpret_cast<const u32x2 *>(a.Hs + p * 2 * I + I + c);
+                    const bf16 *ha = reinterpret_cast<const bf16 *>(&hav);
+                    const bf16 *hb = reinterpret_cast<const bf16 *>(&hbv);
+                    float da[4], db[4], ag[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float u = acc[0][fm][fn][i];
+                        const float av = static_cast<float>(ha[i]), bv = static_cast<float>(hb[i]);
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-av));
+                        const float sl = av * sg;
+                        const float act = sl * bv;
+                        const float dact = g * u;
+                        da[i] = dact * bv * sg * (1.0f + av * (1.0f - sg));
+                        db[i] = dact * sl;
+                        ag[i] = g * act;
+                        dg += u * act;
+                    }
+                    *reinterpret_cast<u32x2 *>(a.C + p * 2 * I + c) = pack4(da[0], da[1], da[2], da[3]);
+                    *reinterpret_cast<u32x2 *>(a.C + p * 2 * I + I + c) =
+                        pack4(db[0], db[1], db[2], db[3]);
+                    *reinterpret_cast<u32x2 *>(a.C2 + p * I + c) = pack4(ag[0], ag[1], ag[2], ag[3]);
+                }
+            }
+            // the 4 lanes sharing this row hold disjoint columns
+            dg += __shfl_xor(dg, 16, 64);
+            dg += __shfl_xor(dg, 32, 64);
+            if (rok && lane < 16)
+                a.dgp[p * a.dgp_stride + (t.n0 / C::OUT_N) * C::WAVES_N + wn] = dg;
+        }
+    } else if constexpr (KIND == B5 || KIND == B7) {
+        // weight gradient tile of expert e: rows m, columns n of dW[e] [M, N]
+        bf16 *dW = a.C + (int64_t)t.e * a.M * a.N;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int r = wm * C::WTM + fm * 16 + (lane & 15);
+            if (r >= t.rows)
+                continue;
+            const int64_t m = t.m0 + r;
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) {
+                const int c = t.n0 + wn * C::WTN + fn * 16 + cl;
+                if (c < a.N)
+                    *reinterpret_cast<u32x2 *>(dW + m * a.N + c) =
+                        pack4(acc[0][fm][fn][0], acc[0][fm][fn][1], acc[0][fm][fn][2],
+                              acc[0][fm][fn][3]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int r = wm * C::WTM + fm * 16 + (lane & 15);
+            if (r >= t.rows)
+                continue;
+            const int64_t p = t.m0 + r;
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) {
+                const int c = t.n0 + wn * C::WTN + fn * 16 + cl;
+                if (c >= a.N)
+                    continue;
+                if constexpr (KIND == F1) {
+                    float o[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        o[i] = silu_f(acc[0][fm][fn][i]) * acc[1][fm][fn][i];
+                    *reinterpret_cast<u32x2 *>(a.C + p * a.ldc + c) = pack4(o[0], o[1], o[2], o[3]);
+                    if (a.C2) {
+                        *reinterpret_cast<u32x2 *>(a.C2 + p * 2 * a.N + c) =
+                            pack4(acc[0][fm][fn][0], acc[0][fm][fn][1], acc[0][fm][fn][2],
+                                  acc[0][fm][fn][3]);
+                        *reinterpret_cast<u32x2 *>(a.C2 + p * 2 * a.N + a.N + c) =
+                            pack4(acc[1][fm][fn][0], acc[1][fm][fn][1], acc[1][fm][fn][2],
+                                  acc[1][fm][fn][3]);
+                    }
+                } else {
+                    *reinterpret_cast<u32x2 *>(a.C + p * a.ldc + c) =
+                        pack4(acc[0][fm][fn][0], acc[0][fm][fn][1], acc[0][fm][fn][2],
+                              acc[0][fm][fn][3]);
+                }
+            }
+        }
+    }
+}
+
+template <int KIND, int BM, int WM>
+__global__ __launch_bounds__(64 * NW, 1) void engine_kernel(EngineArgs a)
+{
+    using C = Cfg<KIND, BM, WM>;
+    using KT = typename C::KT;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * C::STAGE_BYTES];
+
+    const int total = total_tiles<KIND, BM, WM>(a);
+    const int per_xcd_wg = gridDim.x >> 3;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int range = (total + 7) >> 3;
+    const int hi = min((xcd + 1) * range, total);
+    const int L0 = xcd * range + slot;
+    if (L0 >= hi)
+        return;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+
+    // producer cursor: the next K step to copy
+    int pL = L0, pkb = 0;
+    TileInfo pt = decode_tile<KIND, BM, WM>(a, pL);
+    Src<KIND, BM, WM> ps;
+    make_src<KIND, BM, WM>(a, pt, wave, lane, ps);
+    bool pvalid = true;
+    auto p_skip_empty = [&]() {
+        while (pvalid && pkb >= pt.nk) {
+            pL += per_xcd_wg;
+            pkb = 0;
+            pvalid = pL < hi;
+            if (pvalid) {
+                pt = decode_tile<KIND, BM, WM>(a, pL);
+                make_src<KIND, BM, WM>(a, pt, wave, lane, ps);
+            }
+        }
+    };
+    p_skip_empty();
+    int gstage_issue = 0; // stage the producer writes next
+    int inflight = 0;     // steps copied but not yet consumed
+    auto produce = [&]() {
+        issue<KIND, BM, WM>(a, pt, ps, pkb, smem + gstage_issue * C::STAGE_BYTES, wave, lane);
+        gstage_issue = gstage_issue == NSTAGE - 1 ? 0 : gstage_issue + 1;
+        ++inflight;
+        ++pkb;
+        p_skip_empty();
+    };
+    if (pvalid)
+        produce();
+    if (pvalid)
+        produce();
+
+    f32x4 acc[C::NPANEL][C::FM][C::FN];
+    int cstage = 0;
+
+    for (int L = L0; L < hi; L += per_xcd_wg) {
+        const TileInfo t = decode_tile<KIND, BM, WM>(a, L);
+#pragma unroll
+        for (int p = 0; p < C::NPANEL; ++p)
+#pragma unroll
+            for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < C::FN; ++fn)
+                    acc[p][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        for (int kb = 0; kb < t.nk; ++kb) {
+            // this step's copies are the oldest in flight; the next step's may stay
+            if (inflight > 1)
+                wait_vm<C::NL>();
+            else
+                wait_vm<0>();
+            lds_barrier();
+            if (pvalid)
+                produce();
+            --inflight;
+            const unsigned char *sA = smem + cstage * C::STAGE_BYTES;
+            const unsigned char *sB = sA + C::A_BYTES;
+            cstage = cstage == NSTAGE - 1 ? 0 : cstage + 1;
+#pragma unroll
+            for (int kk = 0; kk < BK; kk += 32) {
+                bf16x8 af[C::FM];
+#pragma unroll
+                for (int fm = 0; fm < C::FM; ++fm) {
+                    if constexpr (KT::ALAY == KROW)
+                        af[fm] = frag_krow(sA, wm * C::WTM + fm * 16 + (lane & 15),
+                                           (kk >> 3) + (lane >> 4));
+                    else
+                        af[fm] = frag_kcol<BM * 2>(sA, wm * C::WTM + fm * 16, kk + 8 * (lane >> 4),
+                                                   lane);
+                }
+#pragma unroll
+                for (int p = 0; p < C::NPANEL; ++p) {
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; ++fn) {
+                        const int nb = p * C::PW + wn * C::WTN + fn * 16;
+                        bf16x8 bfrag;
+                        if constexpr (KT::BLAY == KROW)
+                            bfrag = frag_krow(sB, nb + (lane & 15), (kk >> 3) + (lane >> 4));
+                        else if constexpr (KT::PAIRED)
+                            bfrag = frag_kcol<C::PW * 2>(sB + p * (BK * C::PW * 2),
+                                                         wn * C::WTN + fn * 16, kk + 8 * (lane >> 4),
+                                                         lane);
+                        else
+                            bfrag = frag_kcol<C::PW * 2>(sB, nb, kk + 8 * (lane >> 4), lane);
+#pragma unroll
+                        for (int fm = 0; fm < C::FM; ++fm)
+                            acc[p][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                bfrag, af[fm], acc[p][fm][fn], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        epilogue<KIND, BM, WM>(a, t, acc, wm, wn, lane);
+    }
+}
+
+template <int KIND, int BM, int WM>
+static hipError_t launch(const EngineArgs &a, int num_cus, hipStream_t stream)
+{
+    const int grid = (num_cus + 7) / 8 * 8; // one workgroup per CU, whole XCDs
+    hipLaunchKernelGGL((engine_kernel<KIND, BM, WM>), dim3((unsigned)grid), dim3(64 * NW), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+} // namespace eng
+
+int engine_dgp_width(int I) { return ((I + 255) / 256) * (eng::NW / 2); }
+
+hipError_t launch_engine(int kind, int BM, const EngineArgs &a, int num_cus, hipStream_t stream)
+{
+    using namespace eng;
+    switch (kind) {
+    case F1: return BM == 64 ? launch<F1, 64, 1>(a, num_cus, stream) : launch<F1, 128, 1>(a, num_cus, stream);
+    case F2: return BM == 64 ? launch<F2, 64, 1>(a, num_cus, stream) : launch<F2, 128, 1>(a, num_cus, stream);
+    case B2: return launch<B2, 128, 2>(a, num_cus, stream);
+    case B4: return launch<B4, 128, 2>(a, num_cus, stream);
+    case B5: return launch<B5, 128, 2>(a, num_cus, stream);
+    case B7: return launch<B7, 128, 2>(a, num_cus, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+} // namespace moe

@@ -6,6 +6,8 @@
 
 namespace moe {
 
+typedef __bf16 bf16_t;
+
 // ---- routing -----------------------------------------------------------------
 struct RoutePlan {
     int RC;    // slots per chunk (one wave per chunk)
@@ -67,13 +69,41 @@ hipError_t launch_gemm1_swiglu(int dtype, const FwdTiles &t, const GroupedGemmAr
 hipError_t launch_gemm2(int dtype, const FwdTiles &t, const GroupedGemmArgs &a,
                         hipStream_t stream);
 
-// bf16 fast path (gemm_mfma.hip): H % 256 == 0, I % 128 == 0
-bool fast_gemm_supported(int dtype, int64_t H, int64_t I);
-hipError_t launch_fast_gemm1(const FwdTiles &t, const GroupedGemmArgs &a, hipStream_t stream);
-hipError_t launch_fast_gemm2(const FwdTiles &t, const GroupedGemmArgs &a, hipStream_t stream);
+// bf16 engine (gemm_engine.hip): forward F1/F2 and backward B2/B4/B5/B7
+struct EngineArgs {
+    const bf16_t *A;             // first operand (see the kind table in gemm_engine.hip)
+    const bf16_t *B;             // second operand
+    bf16_t *C;                   // main output
+    bf16_t *C2;                  // F1: optional saved h [TK, 2I]; B2: act_g [TK, I]
+    const bf16_t *Hs;            // B2: saved h [TK, 2I]
+    const float *gates;          // B2: topk_weights by slot
+    float *dgp;                  // B2: per-row partial dots [TK, dgp_stride]
+    const int32_t *sorted_slot;  // permuted row -> slot
+    const int32_t *offsets;      // [E + 1]
+    const int32_t *mtile_off;    // [E + 1] (token-tiled kinds)
+    const int32_t *mtile_expert; // [max M-tiles]
+    int topk, E;
+    int M, N, Kd;                // feature-tiled: M, N; token-tiled: N and Kd
+    int lda, ldb, ldc;
+    int64_t b_estride;           // expert stride of a weight operand (elements)
+    int dgp_stride;
+};
+enum { ENG_F1 = 0, ENG_F2 = 1, ENG_B2 = 2, ENG_B4 = 3, ENG_B5 = 4, ENG_B7 = 5 };
+hipError_t launch_engine(int kind, int BM, const EngineArgs &a, int num_cus, hipStream_t stream);
+int engine_dgp_width(int I); // columns of the B2 partial-dot buffer
 
 // ---- combine ---------------------------------------------------------------------
 hipError_t launch_combine(int dtype, const void *o, const int32_t *slot_pos, const float *gates,
                           void *y, int64_t T, int H, int K, hipStream_t stream);
+// backward combine: dx[t] = Σ_k dxp[slot_pos[tK+k]] and
+// d_topk[t, k] = Σ_j dgp[slot_pos[tK+k], j] (0 for a dropped slot)
+hipError_t launch_combine_bwd(const void *dxp, const float *dgp, int dgp_stride,
+                              const int32_t *slot_pos, void *dx, float *d_topk, int64_t T, int H,
+                              int K, hipStream_t stream);
+// zero `bytes` (a multiple of 16) at a 16-byte aligned pointer
+hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t stream);
+// M-tile tables from per-expert counts (one block)
+hipError_t launch_build_mtiles(const int32_t *counts, int E, int BM, int32_t *mtile_off,
+                               int32_t *mtile_expert, hipStream_t stream);
 
 } // namespace moe

@@ -202,6 +202,50 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(
     }
 }
 
+// M-tile tables (prefix of ceil(counts[e] / BM) and the owner of every M-tile)
+// from per-expert counts, for a launch whose tile height differs from, or
+// comes after, the routing step.  One 1024-thread block; E <= 1024.
+__global__ __launch_bounds__(1024) void build_mtiles_kernel(const int32_t *__restrict__ counts,
+                                                            int E, int BM,
+                                                            int32_t *__restrict__ mtile_off,
+                                                            int32_t *__restrict__ mtile_expert)
+{
+    __shared__ int32_t s_moff[1025];
+    __shared__ int32_t s_w[40];
+    const int e = threadIdx.x;
+    const int32_t mt = e < E ? (counts[e] + BM - 1) / BM : 0;
+    int32_t mtotal;
+    const int32_t moff = block_excl_scan(mt, s_w, &mtotal);
+    if (e < E) {
+        mtile_off[e] = moff;
+        s_moff[e] = moff;
+    }
+    if (e == 0) {
+        mtile_off[E] = mtotal;
+        s_moff[E] = mtotal;
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < mtotal; j += 1024) {
+        int lo = 0, hi = E;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_moff[mid] <= j)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        mtile_expert[j] = lo;
+    }
+}
+
+hipError_t launch_build_mtiles(const int32_t *counts, int E, int BM, int32_t *mtile_off,
+                               int32_t *mtile_expert, hipStream_t stream)
+{
+    hipLaunchKernelGGL(build_mtiles_kernel, dim3(1), dim3(1024), 0, stream, counts, E, BM,
+                       mtile_off, mtile_expert);
+    return hipGetLastError();
+}
+
 RoutePlan make_route_plan(int64_t TK, int E)
 {
     RoutePlan rp;
