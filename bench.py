@@ -67,7 +67,7 @@ def main():
 
     m.load_library()
     w = workload(args.workload)
-    inp = make_inputs(w, with_dy=False)
+    inp = make_inputs(w, with_dy=w.backward)
     dev = torch.device("cuda:0")
 
     def to_dev(a):
@@ -81,25 +81,41 @@ def main():
     ws_bytes, _ = m.fwd_workspace_size(prob)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
-    def step(ev=None):
-        return m.moe_ffn_fwd(d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
-                             d["down_proj"], ws=ws, stage_events=ev)
+    bws = None
+    if w.backward:
+        bws = torch.empty(max(m.bwd_workspace_size(prob), 1), dtype=torch.uint8, device=dev)
+
+    def step(ev=None, bev=None):
+        if not w.backward:
+            return m.moe_ffn_fwd(d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
+                                 d["down_proj"], ws=ws, stage_events=ev)
+        y, saved = m.moe_ffn_fwd(d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
+                                 d["down_proj"], ws=ws, stage_events=ev, save_for_backward=True)
+        m.moe_ffn_bwd(d["dy"], d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
+                      d["down_proj"], saved, ws=bws, stage_events=bev)
+        return y
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     pool = m.EventPool(args.steps)
+    bpool = m.EventPool(args.steps, n_stages=len(m.BWD_STAGES)) if w.backward else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        y = step(pool.sets[i])
+        y = step(pool.sets[i], bpool.sets[i] if bpool else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
     stage_ms = {name: float(np.mean([pool.elapsed_ms(i, s) for i in range(args.steps)]))
                 for s, name in enumerate(m.STAGES)}
     pool.close()
+    if bpool:
+        stage_ms.update({"bwd_" + name: float(np.mean([bpool.elapsed_ms(i, s)
+                                                       for i in range(args.steps)]))
+                         for s, name in enumerate(m.BWD_STAGES)})
+        bpool.close()
 
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = w.T * args.steps / elapsed
@@ -110,7 +126,7 @@ def main():
     g1_flops = 4.0 * w.T * w.K * w.H * w.I
     g1_bytes = (live.sum() * w.H * 2 * w.I * es + w.T * w.H * es + w.T * w.K * w.I * es)
     g1_s = stage_ms["gemm1"] * 1e-3
-    layer_flops = w.fwd_flops()
+    layer_flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
     layer_bytes = live.sum() * 3 * w.H * w.I * es + 2 * w.T * w.H * es + w.T * w.K * 8
     if w.name.startswith("decode"):
         roof = {"bound": "hbm", "achieved": g1_bytes / g1_s / 1e9, "peak": PEAK_HBM_GBS,
@@ -140,7 +156,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded numpy PCG64; random-init weights)",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "K": w.K,
-                   "routing": w.routing, "accumulate": "f32"},
+                   "routing": w.routing, "accumulate": "f32",
+                   "step": "forward + backward" if w.backward else "forward"},
         "layer": {"tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
                   "frac_mfma": layer_flops / (ms_per_step * 1e-3) / 1e12 /
                   (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS),

@@ -338,8 +338,9 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
             return fail(MOE_FFN_ERR_EXPERT_ID, "topk_ids holds a value outside [0, %d)", E);
     }
 
-    if (p->dtype == MOE_FFN_BF16) {
-        // bf16: the persistent engine (gemm_engine.hip), any H, I multiple of 8
+    const bool fast = moe::fast_gemm_supported(p->dtype, p->H, p->I);
+    if (p->dtype == MOE_FFN_BF16 && !fast) {
+        // bf16, ragged H or I: the persistent engine (gemm_engine.hip)
         moe::EngineArgs g1{};
         g1.A = static_cast<const moe::bf16_t *>(x);
         g1.B = static_cast<const moe::bf16_t *>(up_proj_weight);
@@ -376,7 +377,10 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
         HIP_TRY(moe::launch_engine(moe::ENG_F2, L.tiles.BM, g2, num_cus, s), "gemm2 launch");
         record(ev, MOE_FFN_STAGE_GEMM2, false, s);
     } else {
+        // bf16 with whole tiles: the dedicated forward kernels (gemm_mfma.hip);
         // fp32: the generic kernels (gemm.hip)
+        moe::FwdTiles tiles = L.tiles;
+        tiles.num_cus = num_cus;
         moe::GroupedGemmArgs g1{};
         g1.A = x;
         g1.B = up_proj_weight;
@@ -393,7 +397,9 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
         g1.E = E;
         g1.max_mtiles = (int)L.max_mtiles;
         record(ev, MOE_FFN_STAGE_GEMM1, true, s);
-        HIP_TRY(moe::launch_gemm1_swiglu(p->dtype, L.tiles, g1, s), "gemm1 launch");
+        HIP_TRY(fast ? moe::launch_fast_gemm1(tiles, g1, s)
+                     : moe::launch_gemm1_swiglu(p->dtype, L.tiles, g1, s),
+                "gemm1 launch");
         record(ev, MOE_FFN_STAGE_GEMM1, false, s);
 
         moe::GroupedGemmArgs g2 = g1;
@@ -406,7 +412,9 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
         g2.Nout = (int)p->H;
         g2.ldb = (int)p->H;
         record(ev, MOE_FFN_STAGE_GEMM2, true, s);
-        HIP_TRY(moe::launch_gemm2(p->dtype, L.tiles, g2, s), "gemm2 launch");
+        HIP_TRY(fast ? moe::launch_fast_gemm2(tiles, g2, s)
+                     : moe::launch_gemm2(p->dtype, L.tiles, g2, s),
+                "gemm2 launch");
         record(ev, MOE_FFN_STAGE_GEMM2, false, s);
     }
 

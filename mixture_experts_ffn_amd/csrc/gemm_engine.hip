@@ -157,16 +157,30 @@ struct TileInfo {
     int nk;    // K steps
 };
 
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Load of routing metadata (offsets, M-tile tables, sorted_slot) that earlier
+// launches wrote and this kernel only reads: through the constant address
+// space, so a wave-uniform address becomes a scalar load.
+__device__ __forceinline__ int ldc(const int32_t *p, int i)
+{
+    return ((const __attribute__((address_space(4))) int32_t *)p)[uni(i)];
+}
+
+// All fields are wave-uniform; readfirstlane keeps the decode on the scalar
+// unit (scalar loads, tracked by lgkmcnt) so it never waits for the copies in
+// flight on the vector-memory counter.
 template <int KIND, int BM, int WM>
 __device__ __forceinline__ TileInfo decode_tile(const EngineArgs &a, int L)
 {
     using C = Cfg<KIND, BM, WM>;
     TileInfo t;
+    L = uni(L);
     if constexpr (C::KT::TOKEN_M) {
         const int ntn = (a.N + C::OUT_N - 1) / C::OUT_N;
-        t.e = a.mtile_expert[L / ntn];
-        const int mt0 = a.mtile_off[t.e];
-        const int mt_e = a.mtile_off[t.e + 1] - mt0;
+        t.e = ldc(a.mtile_expert, L / ntn);
+        const int mt0 = ldc(a.mtile_off, t.e);
+        const int mt_e = ldc(a.mtile_off, t.e + 1) - mt0;
         const int local = L - mt0 * ntn;
         constexpr int GM = 8;
         const int grp = local / (GM * ntn);
@@ -175,8 +189,8 @@ __device__ __forceinline__ TileInfo decode_tile(const EngineArgs &a, int L)
         const int rr = local - grp * GM * ntn;
         const int n_t = rr / gm;
         const int m_t = first_m + rr % gm;
-        t.m0 = a.offsets[t.e] + m_t * BM;
-        t.rows = min(BM, a.offsets[t.e + 1] - t.m0);
+        t.m0 = ldc(a.offsets, t.e) + m_t * BM;
+        t.rows = min(BM, ldc(a.offsets, t.e + 1) - t.m0);
         t.n0 = n_t * C::OUT_N;
         t.seg0 = 0;
         t.klen = a.Kd;
@@ -188,9 +202,15 @@ __device__ __forceinline__ TileInfo decode_tile(const EngineArgs &a, int L)
         t.m0 = m_t * BM;
         t.rows = min(BM, a.M - t.m0);
         t.n0 = n_t * C::OUT_N;
-        t.seg0 = a.offsets[t.e];
-        t.klen = a.offsets[t.e + 1] - t.seg0;
+        t.seg0 = ldc(a.offsets, t.e);
+        t.klen = ldc(a.offsets, t.e + 1) - t.seg0;
     }
+    t.e = uni(t.e);
+    t.m0 = uni(t.m0);
+    t.rows = uni(t.rows);
+    t.n0 = uni(t.n0);
+    t.seg0 = uni(t.seg0);
+    t.klen = uni(t.klen);
     t.nk = (t.klen + BK - 1) / BK;
     return t;
 }
@@ -201,7 +221,7 @@ __device__ __forceinline__ int total_tiles(const EngineArgs &a)
     using C = Cfg<KIND, BM, WM>;
     const int ntn = (a.N + C::OUT_N - 1) / C::OUT_N;
     if constexpr (C::KT::TOKEN_M)
-        return a.mtile_off[a.E] * ntn;
+        return ldc(a.mtile_off, a.E) * ntn;
     else
         return a.E * ((a.M + BM - 1) / BM) * ntn;
 }
@@ -235,7 +255,7 @@ __device__ __forceinline__ int64_t kcol_token_row(const EngineArgs &a, const Til
     int idx[KPC];
 #pragma unroll
     for (int q = 0; q < KPC; ++q)
-        idx[q] = kbase + q < t.klen ? a.sorted_slot[t.seg0 + kbase + q] : 0;
+        idx[q] = kbase + q < t.klen ? ldc(a.sorted_slot, t.seg0 + kbase + q) : 0;
     int v = idx[0];
 #pragma unroll
     for (int q = 1; q < KPC; ++q)
@@ -264,7 +284,7 @@ __device__ __forceinline__ void make_src(const EngineArgs &a, const TileInfo &t,
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int rj = c * 8 + j < t.rows ? c * 8 + j : 0; // tail rows repeat row 0
-                    idx[j] = a.sorted_slot[t.m0 + rj];
+                    idx[j] = ldc(a.sorted_slot, t.m0 + rj);
                 }
                 int v = idx[0];
 #pragma unroll
@@ -538,7 +558,7 @@ __global__ __launch_bounds__(64 * NW, 1) void engine_kernel(EngineArgs a)
     using KT = typename C::KT;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * C::STAGE_BYTES];
 
-    const int total = total_tiles<KIND, BM, WM>(a);
+    const int total = uni(total_tiles<KIND, BM, WM>(a));
     const int per_xcd_wg = gridDim.x >> 3;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int range = (total + 7) >> 3;

@@ -69,6 +69,11 @@ hipError_t launch_gemm1_swiglu(int dtype, const FwdTiles &t, const GroupedGemmAr
 hipError_t launch_gemm2(int dtype, const FwdTiles &t, const GroupedGemmArgs &a,
                         hipStream_t stream);
 
+// bf16 forward fast path (gemm_mfma.hip): H % 256 == 0, I % 128 == 0
+bool fast_gemm_supported(int dtype, int64_t H, int64_t I);
+hipError_t launch_fast_gemm1(const FwdTiles &t, const GroupedGemmArgs &a, hipStream_t stream);
+hipError_t launch_fast_gemm2(const FwdTiles &t, const GroupedGemmArgs &a, hipStream_t stream);
+
 // bf16 engine (gemm_engine.hip): forward F1/F2 and backward B2/B4/B5/B7
 struct EngineArgs {
     const bf16_t *A;             // first operand (see the kind table in gemm_engine.hip)
