@@ -3,18 +3,22 @@
 
 One step = one full forward of the layer (route -> gathered up_proj GEMM with
 SwiGLU -> down_proj GEMM -> combine) on a seeded synthetic batch that is
-already resident in HBM.  Prints ONE JSON line.
+already resident in HBM; for the forward+backward workload also the backward.
+The forward runs as the library does by default (route, GEMM1, GEMM2 and
+combine as separate launches); its pipelined twin (the two grouped GEMMs and
+the combine in one launch with tile-granular release) is timed after it and
+reported as "pipelined_twin".  Prints ONE JSON line.
 
 Default workload: prefill, bf16 with fp32 accumulation, T=4096 tokens,
 H=2048, I=1408, E=64 experts, K=6, uniform routing.  Other workloads:
 --workload {tiny_f32,prefill_bf16,skewed_bf16,decode_bf16,fwdbwd_bf16}.
 
 Besides tokens/s the line carries
-* "roofline": the dominant kernel (the up_proj GEMM with SwiGLU epilogue,
-  or for the HBM-bound decode shape the same kernel against HBM bandwidth),
-  its algorithmic work per launch divided by its average launch time, where
-  the launch times come from HIP events that the library records around that
-  kernel on the call's stream during the timed steps;
+* "roofline": the dominant kernel (the pipelined forward launch, else the
+  up_proj GEMM with SwiGLU epilogue; against HBM bandwidth for the HBM-bound
+  decode shape), its algorithmic work per launch divided by its average
+  launch time, where the launch times come from HIP events that the library
+  records around that kernel on the call's stream during the timed steps;
 * "cpu_baseline": the CPU oracle on the host's cores over a bounded sample of
   the same workload (its first tokens), unless --no-cpu-baseline.
 """
@@ -85,62 +89,84 @@ def main():
     if w.backward:
         bws = torch.empty(max(m.bwd_workspace_size(prob), 1), dtype=torch.uint8, device=dev)
 
-    def step(ev=None, bev=None):
+    def step(ev=None, bev=None, pipelined=False):
         if not w.backward:
             return m.moe_ffn_fwd(d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
-                                 d["down_proj"], ws=ws, stage_events=ev)
+                                 d["down_proj"], ws=ws, stage_events=ev, pipelined=pipelined)
         y, saved = m.moe_ffn_fwd(d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
-                                 d["down_proj"], ws=ws, stage_events=ev, save_for_backward=True)
+                                 d["down_proj"], ws=ws, stage_events=ev, save_for_backward=True,
+                                 pipelined=pipelined)
         m.moe_ffn_bwd(d["dy"], d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
                       d["down_proj"], saved, ws=bws, stage_events=bev)
         return y
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def timed(pipelined):
+        """warmup, then the timed steps; per-stage mean ms from the library's events"""
+        for _ in range(args.warmup):
+            step(pipelined=pipelined)
+        torch.cuda.synchronize()
+        pool = m.EventPool(args.steps)
+        bpool = m.EventPool(args.steps, n_stages=len(m.BWD_STAGES)) if w.backward else None
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            y = step(pool.sets[i], bpool.sets[i] if bpool else None, pipelined=pipelined)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        stages = {}
+        for s, name in enumerate(m.STAGES):
+            try:  # stages a path does not run are never recorded
+                stages[name] = float(np.mean([pool.elapsed_ms(i, s) for i in range(args.steps)]))
+            except m.MoEFFNError:
+                pass
+        pool.close()
+        if bpool:
+            stages.update({"bwd_" + name: float(np.mean([bpool.elapsed_ms(i, s)
+                                                         for i in range(args.steps)]))
+                           for s, name in enumerate(m.BWD_STAGES)})
+            bpool.close()
+        return y, elapsed, stages
 
-    pool = m.EventPool(args.steps)
-    bpool = m.EventPool(args.steps, n_stages=len(m.BWD_STAGES)) if w.backward else None
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        y = step(pool.sets[i], bpool.sets[i] if bpool else None)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-
-    stage_ms = {name: float(np.mean([pool.elapsed_ms(i, s) for i in range(args.steps)]))
-                for s, name in enumerate(m.STAGES)}
-    pool.close()
-    if bpool:
-        stage_ms.update({"bwd_" + name: float(np.mean([bpool.elapsed_ms(i, s)
-                                                       for i in range(args.steps)]))
-                         for s, name in enumerate(m.BWD_STAGES)})
-        bpool.close()
+    # the library's default forward (the bulk launches) is the measured one; the
+    # pipelined twin (one launch, tile-granular release) runs after it
+    y, elapsed, stage_ms = timed(pipelined=False)
+    _, pipe_elapsed, pipe_stage_ms = timed(pipelined=True)
+    pipelined = "pipeline" in stage_ms
 
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = w.T * args.steps / elapsed
     counts = np.bincount(inp["topk_ids"].ravel(), minlength=w.E)
     live = counts > 0
     es = 2 if w.dtype == "bf16" else 4
-    # algorithmic work of the up_proj kernel per launch
-    g1_flops = 4.0 * w.T * w.K * w.H * w.I
-    g1_bytes = (live.sum() * w.H * 2 * w.I * es + w.T * w.H * es + w.T * w.K * w.I * es)
-    g1_s = stage_ms["gemm1"] * 1e-3
     layer_flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
     layer_bytes = live.sum() * 3 * w.H * w.I * es + 2 * w.T * w.H * es + w.T * w.K * 8
+    if pipelined:
+        # dominant kernel: the pipelined forward's one launch (both grouped GEMMs
+        # and the combine); algorithmic work = the forward's flops, or for the
+        # HBM-bound decode shape the forward's algorithmic bytes
+        k_flops = w.fwd_flops()
+        k_bytes = layer_bytes
+        k_ms = stage_ms["pipeline"]
+        kernel = "moe::fast::moe_fwd_bf16<BM, FAST_PIPE> (GEMM1+SwiGLU, GEMM2, combine)"
+    else:
+        # dominant kernel: the gathered up_proj GEMM with the SwiGLU epilogue
+        k_flops = 4.0 * w.T * w.K * w.H * w.I
+        k_bytes = live.sum() * w.H * 2 * w.I * es + w.T * w.H * es + w.T * w.K * w.I * es
+        k_ms = stage_ms["gemm1"]
+        kernel = ("moe::fast::moe_fwd_bf16<BM, FAST_G1> (gathered up_proj GEMM + SwiGLU)"
+                  if w.dtype == "bf16" and w.H % 256 == 0 and w.I % 128 == 0 else
+                  "up_proj GEMM + SwiGLU (engine / generic kernel)")
     if w.name.startswith("decode"):
-        roof = {"bound": "hbm", "achieved": g1_bytes / g1_s / 1e9, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": k_bytes / (k_ms * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-        roof = {"bound": "mfma", "achieved": g1_flops / g1_s / 1e12, "peak": peak,
+        roof = {"bound": "mfma", "achieved": k_flops / (k_ms * 1e-3) / 1e12, "peak": peak,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(w.name)
-    roof["kernel"] = ("moe::fast::moe_gemm_bf16<BM,true,true,...> (gathered up_proj GEMM + SwiGLU)"
-                      if w.dtype == "bf16" and w.H % 256 == 0 and w.I % 128 == 0 else
-                      "moe::grouped_gemm_kernel<...,SWIGLU=true,...> (gathered up_proj GEMM + SwiGLU)")
-    roof["avg_launch_ms"] = stage_ms["gemm1"]
+    roof["traffic"] = measured_traffic(w.name, "pipeline" if pipelined else "gemm1")
+    roof["kernel"] = kernel
+    roof["avg_launch_ms"] = k_ms
 
     out = {
         "metric": METRIC,
@@ -163,9 +189,15 @@ def main():
                   (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS),
                   "hbm_gbs_alg": layer_bytes / (ms_per_step * 1e-3) / 1e9,
                   "stage_ms": stage_ms},
+        "pipelined_twin": {"ms_per_step": pipe_elapsed / args.steps * 1e3,
+                           "tokens_per_s": w.T * args.steps / pipe_elapsed,
+                           "stage_ms": pipe_stage_ms},
         "roofline": roof,
         "cpu_baseline": None,
     }
+
+    if w.dtype == "bf16" and not w.name.startswith("decode"):
+        out["dense_reference"] = dense_reference(w, dev)
 
     if args.copy_calibration_mb:
         n = args.copy_calibration_mb * (1 << 20) // 4
@@ -180,21 +212,47 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per launch of the up_proj kernel from the committed PMC summary
-    (profiles/traffic_gemm1.txt), or None when the kernel source has changed since the
-    counters were taken or no summary exists for this workload."""
+def dense_reference(w, dev, reps=20):
+    """Context only: torch.matmul (the vendor BLAS) on the dense bf16 GEMMs of the
+    same total size, [T*K, H] x [H, 2I] and [T*K, I] x [I, H], as an achievable
+    rate for comparison with the grouped kernels."""
+    import torch
+
+    out = {}
+    for name, (M, Kd, N) in {"gemm1": (w.T * w.K, w.H, 2 * w.I),
+                             "gemm2": (w.T * w.K, w.I, w.H)}.items():
+        a = torch.randn(M, Kd, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(Kd, N, device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / reps * 1e3
+        out[name] = {"shape": [M, Kd, N], "ms": ms,
+                     "tflops": 2.0 * M * Kd * N / (ms * 1e-3) / 1e12}
+        del a, b
+    return out
+
+
+def measured_traffic(workload_name, kernel):
+    """HBM bytes per launch of the dominant kernel from the committed PMC summary
+    (profiles/traffic.txt), or None when the kernel source has changed since the
+    counters were taken or no summary exists for this workload and kernel."""
     import hashlib
 
     src = os.path.join(ROOT, "mixture_experts_ffn_amd", "csrc", "gemm_mfma.hip")
-    table = os.path.join(ROOT, "profiles", "traffic_gemm1.txt")
+    table = os.path.join(ROOT, "profiles", "traffic.txt")
     if not (os.path.exists(src) and os.path.exists(table)):
         return None
     sha = hashlib.sha1(open(src, "rb").read()).hexdigest()[:12]
     for line in open(table):
         parts = line.split()
-        if len(parts) == 4 and parts[0] == workload_name and parts[1] == f"gemm_mfma.hip:{sha}":
-            vals = dict(p.split("=") for p in parts[2:])
+        if (len(parts) == 5 and parts[0] == workload_name and parts[1] == kernel
+                and parts[2] == f"gemm_mfma.hip:{sha}"):
+            vals = dict(p.split("=") for p in parts[3:])
             return float(vals["fetch_bytes"]) + float(vals["write_bytes"])
     return None
 

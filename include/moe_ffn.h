@@ -61,7 +61,8 @@ typedef enum {
     MOE_FFN_ERR_EXPERT_ID = 6, /* a topk_ids value outside [0, E) (found on the device) */
     MOE_FFN_ERR_SAVED = 7,     /* the saved context does not belong to this problem */
     MOE_FFN_ERR_HIP = 8,       /* a HIP runtime call failed; see moe_ffn_last_error() */
-    MOE_FFN_ERR_DEVICE = 9     /* the current device is not a gfx950 GPU */
+    MOE_FFN_ERR_DEVICE = 9,    /* the current device is not a gfx950 GPU */
+    MOE_FFN_ERR_TIMEOUT = 10   /* a wait of the pipelined forward hit its watchdog */
 } moe_ffn_status;
 
 /* Problem description.  Limits: 0 <= T, 1 <= K <= 32, 1 <= E <= 1024,
@@ -76,6 +77,29 @@ typedef struct {
 #define MOE_FFN_CHECK_IDS 0x1u /* fwd: after routing, synchronise the stream and return
                                   MOE_FFN_ERR_EXPERT_ID before any GEMM runs if an id was
                                   out of range (the call is then synchronous). */
+/* fwd, bf16 with H % 256 == 0 and I % 128 == 0: run GEMM1, GEMM2 and the
+ * combine as ONE persistent launch with tile-granular release (the overlap
+ * explainer page, sections 5-6: a consumer tile starts once the producer tiles
+ * it reads have signalled, instead of at a launch boundary).  Device counters
+ * in `ws`, zeroed by the routing step of the same call, record per GEMM1 /
+ * GEMM2 M-tile how many of its N-tiles are done; a GEMM2 tile waits for all
+ * GEMM1 N-tiles of its M-tile, a combine unit for the GEMM2 M-tiles of its
+ * slots.  Every wait is bounded by a watchdog (2 s): on expiry the status
+ * word gets MOE_FFN_DEV_TIMEOUT and the kernel still runs to its end, so a
+ * stream never hangs.  The launch assumes that one workgroup per CU can be
+ * resident at once (nothing else running on the device); if not, waits may
+ * time out.  Without the flag (and for other shapes) the forward is the bulk
+ * twin: GEMM1, GEMM2 and combine as separate launches.  Both give bitwise
+ * identical outputs; the bulk twin is the default because it is currently
+ * the faster of the two on compute-bound shapes. */
+#define MOE_FFN_PIPELINE 0x2u
+/* Test hook, never for production: the pipelined forward drops the release
+ * of one GEMM1 tile and uses a 20 ms watchdog, so that the waits behind it
+ * time out (status MOE_FFN_DEV_TIMEOUT) while every kernel still ends. */
+#define MOE_FFN_TEST_DROP_RELEASE 0x100u
+/* Bits of the device status word (moe_ffn_read_status). */
+#define MOE_FFN_DEV_BAD_ID 0x1  /* an expert id was outside [0, E); its slot was dropped */
+#define MOE_FFN_DEV_TIMEOUT 0x2 /* a pipelined wait hit the watchdog; outputs are unreliable */
 
 /* Stages of the forward, for the timing hook below. */
 enum {
@@ -83,7 +107,9 @@ enum {
     MOE_FFN_STAGE_GEMM1 = 1,   /* gathered up_proj GEMM with the SwiGLU epilogue */
     MOE_FFN_STAGE_GEMM2 = 2,   /* down_proj GEMM */
     MOE_FFN_STAGE_COMBINE = 3, /* unpermute + gate-weighted sum */
-    MOE_FFN_NUM_FWD_STAGES = 4
+    MOE_FFN_STAGE_PIPELINE = 4, /* the pipelined forward's single launch (GEMM1, GEMM2 and
+                                   combine); stages 1-3 are then not recorded */
+    MOE_FFN_NUM_FWD_STAGES = 5
 };
 
 /* Stages of the backward, for the timing hook below. */
@@ -173,8 +199,8 @@ int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, cons
 /* ---- status and measurement helpers ---------------------------------------- */
 
 /* Synchronises `stream`, then reads the device status word that the last
- * forward or route call on this workspace left: 0, or 1 when an expert id was
- * out of range. */
+ * forward or route call on this workspace left: 0, or an OR of
+ * MOE_FFN_DEV_BAD_ID and MOE_FFN_DEV_TIMEOUT. */
 int moe_ffn_read_status(const void *ws, void *stream, int32_t *device_status);
 
 /* Static text for a status code. */
@@ -185,7 +211,9 @@ const char *moe_ffn_last_error(void);
 
 /* hipEvent helpers for the timing hook, so a caller needs no other HIP
  * binding: create / destroy an event and read the elapsed milliseconds
- * between two recorded events (synchronises on `end`). */
+ * between two recorded events (synchronises on `end`).  For an event that
+ * was never recorded (a stage the call's path does not run) the elapsed
+ * query returns MOE_FFN_ERR_HIP and leaves no error behind for later calls. */
 int moe_ffn_event_create(void **event);
 int moe_ffn_event_destroy(void *event);
 int moe_ffn_event_elapsed_ms(void *begin, void *end, float *ms);

@@ -51,12 +51,15 @@ _lib = None
 
 F32, BF16, I32, I64 = 0, 1, 2, 3
 CHECK_IDS = 0x1
-STAGES = ("route", "gemm1", "gemm2", "combine")
+PIPELINE = 0x2
+TEST_DROP_RELEASE = 0x100
+DEV_BAD_ID, DEV_TIMEOUT = 0x1, 0x2
+STAGES = ("route", "gemm1", "gemm2", "combine", "pipeline")
 BWD_STAGES = ("act_grad", "input_grad", "dx_combine", "w2_grad", "w1_grad")
 
 ERR_NAMES = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN",
              5: "ERR_WORKSPACE", 6: "ERR_EXPERT_ID", 7: "ERR_SAVED", 8: "ERR_HIP",
-             9: "ERR_DEVICE"}
+             9: "ERR_DEVICE", 10: "ERR_TIMEOUT"}
 
 
 class MoEFFNError(RuntimeError):
@@ -198,12 +201,16 @@ def route_workspace_size(problem: Problem) -> int:
 
 def moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *,
                 save_for_backward: bool = False, check_ids: bool = False, ws=None,
-                stage_events: StageEvents | None = None, return_ws: bool = False):
+                stage_events: StageEvents | None = None, return_ws: bool = False,
+                pipelined: bool = False, flags: int = 0):
     """y [T, H] of the MoE expert-FFN layer (see include/moe_ffn.h).
 
     With ``save_for_backward`` also returns the saved context (a uint8 device
     tensor) that the backward consumes.  ``ws`` may pass a preallocated
     workspace (uint8 tensor of at least ``fwd_workspace_size`` bytes).
+    ``pipelined`` selects the one-launch forward with tile-granular release
+    (bf16, H % 256 == 0, I % 128 == 0; other shapes ignore it);
+    ``flags`` passes further MOE_FFN_* bits through.
     """
     lib = load_library()
     _require_gpu(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
@@ -218,7 +225,7 @@ def moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *,
     elif ws.numel() < ws_bytes:
         raise MoEFFNError(5, f"workspace has {ws.numel()} bytes, {ws_bytes} needed")
     saved = torch.empty(saved_bytes, dtype=torch.uint8, device=dev) if save_for_backward else None
-    flags = CHECK_IDS if check_ids else 0
+    flags |= (CHECK_IDS if check_ids else 0) | (PIPELINE if pipelined else 0)
     ev = ctypes.byref(stage_events) if stage_events is not None else None
     with torch.cuda.device(dev):
         rc = lib.moe_ffn_fwd_ex(ctypes.byref(prob), _ptr(x), _ptr(topk_ids), _ptr(topk_weights),
@@ -317,7 +324,7 @@ def moe_ffn_route(topk_ids: torch.Tensor, E: int, H: int = 8, I: int = 8):
 
 
 def read_status(ws: torch.Tensor) -> int:
-    """Device status word of the last forward/route on `ws` (1 = an id was out of range)."""
+    """Device status word of the last forward/route on `ws` (DEV_BAD_ID | DEV_TIMEOUT bits)."""
     lib = load_library()
     st = ctypes.c_int32()
     with torch.cuda.device(ws.device):
@@ -328,7 +335,7 @@ def read_status(ws: torch.Tensor) -> int:
 class EventPool:
     """hipEvents (through the library's helpers) for the per-stage timing hook."""
 
-    def __init__(self, n_sets: int, n_stages: int = 4):
+    def __init__(self, n_sets: int, n_stages: int = 5):
         self.lib = load_library()
         self.sets = []
         for _ in range(n_sets):

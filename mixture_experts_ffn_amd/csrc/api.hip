@@ -18,6 +18,9 @@
 #include "kernels.h"
 #include "moe_ffn.h"
 
+static_assert(moe::MOE_DEV_BAD_ID == MOE_FFN_DEV_BAD_ID, "status bits");
+static_assert(moe::MOE_DEV_TIMEOUT == MOE_FFN_DEV_TIMEOUT, "status bits");
+
 namespace {
 
 thread_local char g_err[512];
@@ -90,8 +93,9 @@ int check_ptr(const void *ptr, const char *name, size_t align = 16)
 // The current device must be a gfx950 GPU.  Cached per device ordinal, with
 // its compute-unit count (the persistent kernels launch one workgroup per CU).
 int g_num_cus[64] = {0};
+int g_clock_khz[64] = {0}; // rate of the device's constant wall clock (s_memrealtime)
 
-int check_device(int *num_cus = nullptr)
+int check_device(int *num_cus = nullptr, int *clock_khz = nullptr)
 {
     static std::mutex mu;
     static signed char known[64] = {0}; // 0 unknown, 1 ok, -1 not gfx950
@@ -107,13 +111,20 @@ int check_device(int *num_cus = nullptr)
         err = hipGetDeviceProperties(&prop, dev);
         if (err != hipSuccess)
             return hip_fail(err, "hipGetDeviceProperties");
+        int khz = 0;
+        err = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+        if (err != hipSuccess)
+            return hip_fail(err, "hipDeviceGetAttribute(WallClockRate)");
         known[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
         g_num_cus[dev] = prop.multiProcessorCount;
+        g_clock_khz[dev] = khz > 0 ? khz : 100000;
     }
     if (known[dev] < 0)
         return fail(MOE_FFN_ERR_DEVICE, "device %d is not gfx950", dev);
     if (num_cus)
         *num_cus = g_num_cus[dev];
+    if (clock_khz)
+        *clock_khz = g_clock_khz[dev];
     return MOE_FFN_OK;
 }
 
@@ -137,7 +148,7 @@ struct FwdLayout {
     int64_t max_mtiles;
     // ws
     size_t status, hist, bad, counts, offsets, mtile_off, mtile_expert, sorted_slot, slot_pos;
-    size_t act, o, ws_total;
+    size_t ctr, act, o, ws_total;
     // saved
     size_t s_counts, s_offsets, s_sorted, s_slotpos, s_h, saved_total;
 };
@@ -166,6 +177,7 @@ FwdLayout fwd_layout(const moe_ffn_problem &p)
     L.mtile_expert = take(sizeof(int32_t) * (size_t)L.max_mtiles);
     L.sorted_slot = take(sizeof(int32_t) * (size_t)TK);
     L.slot_pos = take(sizeof(int32_t) * (size_t)TK);
+    L.ctr = take(sizeof(int32_t) * 2 * (size_t)L.max_mtiles);
     L.act = take(es * (size_t)TK * (size_t)p.I);
     L.o = take(es * (size_t)TK * (size_t)p.H);
     L.ws_total = off;
@@ -298,8 +310,8 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
         return fail(MOE_FFN_ERR_ALIGN, "saved is not 16-byte aligned");
     if (ws_bytes < L.ws_total)
         return fail(MOE_FFN_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, L.ws_total);
-    int num_cus = 0;
-    if ((rc = check_device(&num_cus)))
+    int num_cus = 0, clock_khz = 0;
+    if ((rc = check_device(&num_cus, &clock_khz)))
         return rc;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -311,6 +323,8 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
     rb.mtile_off = at<int32_t>(ws, L.mtile_off);
     rb.mtile_expert = at<int32_t>(ws, L.mtile_expert);
     rb.status = at<int32_t>(ws, L.status);
+    rb.ctr = at<int32_t>(ws, L.ctr);
+    rb.nctr = (int)(2 * L.max_mtiles);
     if (saved) {
         rb.counts = at<int32_t>(saved, L.s_counts);
         rb.offsets = at<int32_t>(saved, L.s_offsets);
@@ -376,11 +390,51 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
         record(ev, MOE_FFN_STAGE_GEMM2, true, s);
         HIP_TRY(moe::launch_engine(moe::ENG_F2, L.tiles.BM, g2, num_cus, s), "gemm2 launch");
         record(ev, MOE_FFN_STAGE_GEMM2, false, s);
+    } else if (fast) {
+        // bf16 with whole tiles: the tile engine of gemm_mfma.hip, as separate
+        // launches or, on request, pipelined (one launch, tile-granular release)
+        moe::FastFwdArgs a{};
+        a.x = x;
+        a.w1 = up_proj_weight;
+        a.w2 = down_proj_weight;
+        a.act = at<void>(ws, L.act);
+        a.hsave = saved ? at<void>(saved, L.s_h) : nullptr;
+        a.o = at<void>(ws, L.o);
+        a.y = y;
+        a.gates = topk_weights;
+        a.ids = topk_ids;
+        a.ids64 = p->ids_dtype == MOE_FFN_I64;
+        a.sorted_slot = rb.sorted_slot;
+        a.slot_pos = rb.slot_pos;
+        a.offsets = rb.offsets;
+        a.mtile_off = rb.mtile_off;
+        a.mtile_expert = rb.mtile_expert;
+        a.ctr = rb.ctr;
+        a.status = rb.status;
+        const int64_t watchdog_ms = (flags & MOE_FFN_TEST_DROP_RELEASE) ? 20 : 2000;
+        a.timeout_ticks = watchdog_ms * (int64_t)clock_khz;
+        a.T = (int)p->T;
+        a.H = (int)p->H;
+        a.I = (int)p->I;
+        a.E = E;
+        a.K = (int)p->K;
+        a.max_mtiles = (int)L.max_mtiles;
+        a.drop_mt = (flags & MOE_FFN_TEST_DROP_RELEASE) ? 0 : -1;
+        const int BM = L.tiles.BM;
+        if (flags & MOE_FFN_PIPELINE) {
+            record(ev, MOE_FFN_STAGE_PIPELINE, true, s);
+            HIP_TRY(moe::launch_fast_fwd(moe::FAST_PIPE, BM, a, num_cus, s), "pipeline launch");
+            record(ev, MOE_FFN_STAGE_PIPELINE, false, s);
+            return MOE_FFN_OK;
+        }
+        record(ev, MOE_FFN_STAGE_GEMM1, true, s);
+        HIP_TRY(moe::launch_fast_fwd(moe::FAST_G1, BM, a, num_cus, s), "gemm1 launch");
+        record(ev, MOE_FFN_STAGE_GEMM1, false, s);
+        record(ev, MOE_FFN_STAGE_GEMM2, true, s);
+        HIP_TRY(moe::launch_fast_fwd(moe::FAST_G2, BM, a, num_cus, s), "gemm2 launch");
+        record(ev, MOE_FFN_STAGE_GEMM2, false, s);
     } else {
-        // bf16 with whole tiles: the dedicated forward kernels (gemm_mfma.hip);
         // fp32: the generic kernels (gemm.hip)
-        moe::FwdTiles tiles = L.tiles;
-        tiles.num_cus = num_cus;
         moe::GroupedGemmArgs g1{};
         g1.A = x;
         g1.B = up_proj_weight;
@@ -397,9 +451,7 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
         g1.E = E;
         g1.max_mtiles = (int)L.max_mtiles;
         record(ev, MOE_FFN_STAGE_GEMM1, true, s);
-        HIP_TRY(fast ? moe::launch_fast_gemm1(tiles, g1, s)
-                     : moe::launch_gemm1_swiglu(p->dtype, L.tiles, g1, s),
-                "gemm1 launch");
+        HIP_TRY(moe::launch_gemm1_swiglu(p->dtype, L.tiles, g1, s), "gemm1 launch");
         record(ev, MOE_FFN_STAGE_GEMM1, false, s);
 
         moe::GroupedGemmArgs g2 = g1;
@@ -412,9 +464,7 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
         g2.Nout = (int)p->H;
         g2.ldb = (int)p->H;
         record(ev, MOE_FFN_STAGE_GEMM2, true, s);
-        HIP_TRY(fast ? moe::launch_fast_gemm2(tiles, g2, s)
-                     : moe::launch_gemm2(p->dtype, L.tiles, g2, s),
-                "gemm2 launch");
+        HIP_TRY(moe::launch_gemm2(p->dtype, L.tiles, g2, s), "gemm2 launch");
         record(ev, MOE_FFN_STAGE_GEMM2, false, s);
     }
 
@@ -472,6 +522,8 @@ int moe_ffn_route(const moe_ffn_problem *p, const void *topk_ids, int32_t *count
         return rc;
     moe::RouteBufs rb;
     rb.status = at<int32_t>(ws, R.status);
+    rb.ctr = nullptr;
+    rb.nctr = 0;
     rb.hist = at<int32_t>(ws, R.hist);
     rb.bad = at<int32_t>(ws, R.bad);
     rb.mtile_off = at<int32_t>(ws, R.mtile_off);
@@ -671,6 +723,7 @@ const char *moe_ffn_status_string(int status)
     case MOE_FFN_ERR_SAVED: return "saved context does not match the problem";
     case MOE_FFN_ERR_HIP: return "HIP runtime error";
     case MOE_FFN_ERR_DEVICE: return "current device is not gfx950";
+    case MOE_FFN_ERR_TIMEOUT: return "a pipelined wait hit its watchdog";
     default: return "unknown status";
     }
 }
@@ -698,9 +751,16 @@ int moe_ffn_event_elapsed_ms(void *begin, void *end, float *ms)
 {
     if (!begin || !end || !ms)
         return fail(MOE_FFN_ERR_NULL, "event or ms is NULL");
-    HIP_TRY(hipEventSynchronize(static_cast<hipEvent_t>(end)), "hipEventSynchronize");
-    HIP_TRY(hipEventElapsedTime(ms, static_cast<hipEvent_t>(begin), static_cast<hipEvent_t>(end)),
-            "hipEventElapsedTime");
+    // an event that was never recorded (a stage the call's path does not run)
+    // fails here; the runtime's sticky error is cleared so that it is not
+    // reported by the next, unrelated launch
+    hipError_t err = hipEventSynchronize(static_cast<hipEvent_t>(end));
+    if (err == hipSuccess)
+        err = hipEventElapsedTime(ms, static_cast<hipEvent_t>(begin), static_cast<hipEvent_t>(end));
+    if (err != hipSuccess) {
+        (void)hipGetLastError();
+        return hip_fail(err, "event elapsed time");
+    }
     return MOE_FFN_OK;
 }
 

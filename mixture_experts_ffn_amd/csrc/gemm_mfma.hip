@@ -1,13 +1,24 @@
-// gemm_mfma.hip — the forward bf16 grouped GEMMs of the MoE expert FFN,
-// pipelined for gfx950: the fast path for shapes whose H is a multiple of 256
-// and I of 128 (whole K steps and whole output tiles, so no edge handling).
-// Other bf16 shapes and the backward use the engine of gemm_engine.hip,
-// which adds zero-page edges and variable-K tiles; fp32 uses gemm.hip.
+// gemm_mfma.hip — the forward bf16 grouped GEMMs of the MoE expert FFN for
+// gfx950, and the pipelined forward that chains them with tile-granular
+// release.  Fast path for H a multiple of 256 and I of 128 (whole K steps and
+// whole output tiles); other bf16 shapes and the backward use the engine of
+// gemm_engine.hip, fp32 uses gemm.hip.
 //
-// Same two operations as gemm.hip (HyperMegaMoE issue page, section 2.1:
-// GMM1/up_proj with the SwiGLU epilogue, GMM2/down_proj), organised for the
-// CDNA4 memory pipeline:
+// The two operations (HyperMegaMoE issue page, section 2.1: GMM1/up_proj with
+// the SwiGLU epilogue, GMM2/down_proj):
+//   GEMM1: act[p, j] = silu(x[t_p] · W1[e][:, j]) · (x[t_p] · W1[e][:, I + j])
+//   GEMM2: o[p, :]   = act[p, :] · W2[e]
 //
+// One tile engine serves both, in three modes:
+//   FAST_G1, FAST_G2  one grouped GEMM per launch (the bulk forward: route,
+//                     GEMM1, GEMM2 and combine as separate launches);
+//   FAST_PIPE         one launch runs every GEMM1 tile, then every GEMM2 tile,
+//                     then the combine, with device counters in place of the
+//                     launch boundaries (the overlap explainer page, sections
+//                     5-6, and the issue page's tile-level pipelining: a
+//                     consumer starts as soon as the tiles it reads are done).
+//
+// Tile engine, organised for the CDNA4 memory pipeline:
 //  * Global -> LDS copies go straight into LDS (16 bytes per lane, no
 //    register staging), three stages deep, two K steps ahead of the matrix
 //    cores; each wave waits only for its own copies of the stage it is about
@@ -16,15 +27,21 @@
 //    index XOR-ed by (row / 2) % 8, so the 16 lanes of one 128-bit LDS read
 //    hit 16 different bank groups.  The dispatch gather x[sorted_slot / K] is
 //    just the per-lane source address of those copies.
-//  * B (weights, N-contiguous [k][n]) lands untransposed as [64][PW] with the
-//    32-byte unit index XOR-ed by a 3-bit hash of k; the MFMA fragments are
-//    read with the transposing 64-bit LDS read, two per fragment.
+//  * B (weights, N-contiguous [k][n]) lands untransposed as two panels of
+//    [64][128] with the 32-byte unit index XOR-ed by a 3-bit hash of k; the
+//    MFMA fragments are read with the transposing 64-bit LDS read.  GEMM1's
+//    panels are 128 gate and the matching 128 up columns, so SwiGLU pairs two
+//    accumulators of one lane; GEMM2's panels are 256 adjacent output columns.
 //  * The matrix-core step computes C^T = W^T · X^T (weights as the first
-//    operand), so each lane ends up owning 4 consecutive output columns of
-//    one row and the epilogue writes 8 bytes per lane.
-//  * Block tile 128 (or 64) rows x 256 weight columns, 4 waves; GEMM1's 256
-//    columns are 128 gate + 128 up columns, so SwiGLU is elementwise in
-//    registers.
+//    operand), so each lane owns 4 consecutive output columns of one row and
+//    the epilogue writes 8 bytes per lane.
+//  * Block tile BM (64 or 128) rows x 256 weight columns, 8 waves (two per
+//    SIMD: one wave's MFMAs cover the other's LDS waits), each owning all BM
+//    rows and 16 columns of each panel.
+//  * Persistent: one workgroup per CU walks an XCD-local slice of the tile
+//    order (the hardware hands workgroup b to XCD b % 8), so tiles in flight
+//    on one XCD share weight panels and token rows in its L2; the next tile's
+//    first copies overlap the current tile's last steps and its epilogue.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,31 +55,42 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int BK = 64;
 constexpr int NSTAGE = 3;
-constexpr int kFastWaves = 8; // two waves per SIMD: one's MFMAs cover the other's LDS waits
-constexpr int kWavesM128 = 1; // waves along M for 128-row tiles (each wave owns all rows)
+constexpr int NW = 8;           // waves per workgroup
+constexpr int PW = 128;         // weight columns per panel (two panels per tile)
+constexpr int WTN = PW / NW;    // columns per wave per panel
+constexpr int TILE_N1 = PW;     // GEMM1 output columns per tile
+constexpr int TILE_N2 = 2 * PW; // GEMM2 output columns per tile
 
-template <int BM_, bool SWIGLU, int NW_, int WM_> struct Cfg {
+enum { KIND_G1 = 1, KIND_G2 = 2 };
+
+template <int BM_> struct Cfg {
     static constexpr int BM = BM_;
-    static constexpr int NW = NW_; // waves per workgroup (4 or 8)
-    static constexpr int NPANEL = SWIGLU ? 2 : 1;
-    static constexpr int PW = SWIGLU ? 128 : 256; // weight columns per panel
-    static constexpr int WAVES_M = WM_;           // waves along M
-    static constexpr int WAVES_N = NW / WAVES_M;
-    static constexpr int WTM = BM / WAVES_M;        // rows per wave
-    static constexpr int WTN = PW / WAVES_N;        // columns per wave per panel
-    static constexpr int FM = WTM / 16, FN = WTN / 16;
+    static constexpr int FM = BM / 16;
     static constexpr int A_BYTES = BM * BK * 2;
-    static constexpr int B_BYTES = BK * NPANEL * PW * 2; // 32 KB
+    static constexpr int B_BYTES = BK * 2 * PW * 2; // 32 KB
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-    static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
     static constexpr int A_LOADS = A_BYTES / 1024 / NW; // per wave per stage
     static constexpr int B_LOADS = B_BYTES / 1024 / NW;
-    static_assert(A_LOADS >= 1 && B_LOADS * NW * 1024 == B_BYTES, "stage split");
-    static_assert(A_LOADS * NW * 1024 == A_BYTES, "stage split");
-    static_assert(FM >= 1 && FN >= 1, "wave tile");
+    static constexpr int NL = A_LOADS + B_LOADS;
+    static_assert(A_LOADS >= 1 && A_LOADS * NW * 1024 == A_BYTES, "stage split");
+    static_assert(B_LOADS * NW * 1024 == B_BYTES, "stage split");
+    static_assert(NSTAGE * STAGE_BYTES <= 160 * 1024, "LDS");
 };
 
 __device__ __forceinline__ int bswz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Routing metadata that earlier launches wrote and this kernel only reads:
+// loaded through the constant address space, so a wave-uniform index becomes
+// a scalar load (lgkmcnt) that never waits for the copies on vmcnt.
+__device__ __forceinline__ int ldc(const int32_t *p, int i)
+{
+    return ((const __attribute__((address_space(4))) int32_t *)p)[uni(i)];
+}
+__device__ __forceinline__ float ldcf(const float *p, int i)
+{
+    return ((const __attribute__((address_space(4))) float *)p)[uni(i)];
+}
 
 // 16-byte global -> LDS copy per lane into [l, l + 1024) (lane i at l + 16 i).
 // Issued as inline assembly so that the compiler does not track these LDS
@@ -71,14 +99,26 @@ __device__ __forceinline__ int bswz(int k) { return (k & 3) | (((k >> 3) & 1) <<
 // read.  `l` must be wave-uniform.
 __device__ __forceinline__ void g2l16(const void *g, lds_void *l)
 {
-    const uint32_t lds_addr = (uint32_t)(uintptr_t)l;
+    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
                  : "s"(lds_addr), "v"(g)
                  : "memory", "m0");
 }
 
-// wait until at most n vector-memory operations of this wave are in flight
+// The same copy as a device-coherent load (sc1: served at the device's
+// coherence point, never from a stale cache line), for data that another
+// workgroup of the same launch wrote with device-coherent stores.
+__device__ __forceinline__ void g2l16_coherent(const void *g, lds_void *l)
+{
+    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off sc1"
+                 :
+                 : "s"(lds_addr), "v"(g)
+                 : "memory", "m0");
+}
+
+// wait until at most N vector-memory operations of this wave are in flight
 template <int N> __device__ __forceinline__ void wait_vm()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -98,276 +138,514 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("" ::: "memory");
 }
 
-struct TileInfo {
-    int e, row0, rows, n0;
+// ---- release / acquire of the pipelined forward -------------------------------
+// Everything one workgroup of the pipelined launch hands to another (act rows
+// from GEMM1 to GEMM2, o rows from GEMM2 to the combine) is written with
+// device-coherent stores and read with device-coherent loads (the sc1 scope
+// bit; the encoding of device-scope relaxed atomics), so no cache holds a
+// stale or a dirty private copy of it and no whole-cache write-back or
+// invalidate is needed.  A producer waits until its stores are acknowledged
+// (vmcnt 0), the workgroup meets at a barrier, and one lane bumps the tile's
+// counter; a consumer polls the counter with device-coherent loads, bounded
+// by the watchdog, and issues its loads only after the poll has returned.
+__device__ __forceinline__ void store_coherent(void *p, u32x2 v)
+{
+    __hip_atomic_store(static_cast<uint64_t *>(p), __builtin_bit_cast(uint64_t, v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x4 load_coherent16(const void *p)
+{
+    const uint64_t *q = static_cast<const uint64_t *>(p);
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    u32x4 v;
+    v[0] = (uint32_t)lo;
+    v[1] = (uint32_t)(lo >> 32);
+    v[2] = (uint32_t)hi;
+    v[3] = (uint32_t)(hi >> 32);
+    return v;
+}
+__device__ __forceinline__ int poll(const int32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void bump(int32_t *p)
+{
+    __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave-wide wait until every lane's counter (p != nullptr) reaches `need`.
+// On timeout the status word gets MOE_DEV_TIMEOUT and the wave goes on, so
+// every wave ends.
+__device__ __forceinline__ void wait_counters(const int32_t *p, int need, const FastFwdArgs &a)
+{
+    auto pending = [&]() { return __ballot(p != nullptr && poll(p) < need) != 0ull; };
+    if (!pending())
+        return;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (pending()) {
+        if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) > a.timeout_ticks) {
+            if (__lane_id() == 0)
+                __hip_atomic_fetch_or(a.status, MOE_DEV_TIMEOUT, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    asm volatile("" ::: "memory"); // the consumer's loads stay after the poll
+}
+
+struct Tile {
+    int kind, e, row0, rows, n0, nt, mt;
 };
 
-// Logical tile L -> (expert, first permuted row, real rows, first output
-// column).  Order: expert-major; inside an expert, groups of up to 8 M-tiles
-// with N-tiles outer and M-tiles inner, so consecutive tiles share a weight
-// panel.  All operands are wave-uniform (scalar loads).
-__device__ __forceinline__ TileInfo decode_tile(const GroupedGemmArgs &args, int L, int ntn,
-                                                int BM, int out_tile)
+// Logical tile L of one grouped GEMM -> (expert, first permuted row, real
+// rows, first output column, N-tile, global M-tile).  Order: expert-major;
+// inside an expert, groups of up to 8 M-tiles with N-tiles outer and M-tiles
+// inner, so consecutive tiles share a weight panel.  Wave-uniform.
+__device__ __forceinline__ Tile decode_tile(const FastFwdArgs &a, int kind, int L, int ntn,
+                                            int BM)
 {
-    TileInfo t;
-    t.e = args.mtile_expert[L / ntn];
-    const int mt0 = args.mtile_off[t.e];
-    const int mt_e = args.mtile_off[t.e + 1] - mt0;
+    Tile t;
+    t.kind = kind;
+    L = uni(L);
+    t.e = ldc(a.mtile_expert, L / ntn);
+    const int mt0 = ldc(a.mtile_off, t.e);
+    const int mt_e = ldc(a.mtile_off, t.e + 1) - mt0;
     const int local = L - mt0 * ntn;
     constexpr int GM = 8;
     const int grp = local / (GM * ntn);
     const int first_m = grp * GM;
     const int gm = min(mt_e - first_m, GM);
     const int rr = local - grp * GM * ntn;
-    const int n_t = rr / gm;
+    t.nt = uni(rr / gm);
     const int m_t = first_m + rr % gm;
-    t.row0 = args.offsets[t.e] + m_t * BM;
-    t.rows = min(BM, args.offsets[t.e + 1] - t.row0);
-    t.n0 = n_t * out_tile;
+    t.mt = uni(mt0 + m_t);
+    t.row0 = uni(ldc(a.offsets, t.e) + m_t * BM);
+    t.rows = uni(min(BM, ldc(a.offsets, t.e + 1) - t.row0));
+    t.n0 = uni(t.nt * (kind == KIND_G1 ? TILE_N1 : TILE_N2));
+    t.e = uni(t.e);
     return t;
 }
 
-// Persistent grouped GEMM: gridDim.x workgroups (a multiple of 8, one per CU)
-// walk the logical tiles.  The hardware hands workgroups to the 8 XCDs round
-// robin, so workgroup b sits on XCD b % 8; each XCD owns one contiguous eighth
-// of the tile order and its workgroups take consecutive tiles of it, so the
-// tiles in flight on one XCD share weight panels and token rows in its L2.
-// The K loop runs continuously across a workgroup's tiles: the copies of the
-// next tile's first two K steps are in flight while the current tile's last
-// steps and its epilogue run.
-template <int BM, bool SWIGLU, bool GATHER, int NW, int WM>
-__global__ __launch_bounds__(64 * NW, 1) void moe_gemm_bf16(GroupedGemmArgs args)
+// Position of a workgroup in one phase (the tiles of one grouped GEMM): each
+// XCD owns a contiguous eighth of the tile order; its workgroups take every
+// (gridDim.x / 8)-th tile of it.
+struct Cursor {
+    int kind, L, hi;
+};
+
+template <int BM, int MODE>
+__global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16(FastFwdArgs args)
 {
-    using C = Cfg<BM, SWIGLU, NW, WM>;
+    using C = Cfg<BM>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * C::STAGE_BYTES];
 
-    const int out_tile = SWIGLU ? C::PW : C::NPANEL * C::PW; // output columns per tile
-    const int ntn = args.Nout / out_tile;
-    const int total = args.mtile_off[args.E] * ntn;
+    constexpr bool PIPE = MODE == FAST_PIPE;
+    const int H = args.H, I = args.I;
+    const int ntn1 = I / TILE_N1, ntn2 = H / TILE_N2;
+    const int mtiles = uni(ldc(args.mtile_off, args.E));
     const int per_xcd_wg = gridDim.x >> 3;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int range = (total + 7) >> 3;
-    const int hi = min((xcd + 1) * range, total);
-    int L = xcd * range + slot;
-    if (L >= hi)
-        return;
-
-    const int Kdim = args.Kdim, Nout = args.Nout, ldb = args.ldb;
-    const int nk = Kdim / BK;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-    const bf16 *__restrict__ A = static_cast<const bf16 *>(args.A);
+    const int wave = uni(tid >> 6);
+    int32_t *const ctr1 = args.ctr;                   // GEMM1 N-tiles done per M-tile
+    int32_t *const ctr2 = args.ctr + args.max_mtiles; // GEMM2 N-tiles done per M-tile
+
+    auto kind_of = [&](int k) {
+        return MODE == FAST_G1 ? (int)KIND_G1 : MODE == FAST_G2 ? (int)KIND_G2 : k;
+    };
+    auto phase_begin = [&](int kind, Cursor &c) {
+        const int total = mtiles * (kind == KIND_G1 ? ntn1 : ntn2);
+        const int range = (total + 7) >> 3;
+        c.kind = kind;
+        c.L = xcd * range + slot;
+        c.hi = min((xcd + 1) * range, total);
+        return c.L < c.hi;
+    };
+    auto advance = [&](Cursor &c) {
+        c.L += per_xcd_wg;
+        if (c.L < c.hi)
+            return true;
+        if (PIPE && c.kind == KIND_G1)
+            return phase_begin(KIND_G2, c);
+        return false;
+    };
+    auto decode = [&](const Cursor &c) {
+        const int kind = kind_of(c.kind);
+        return decode_tile(args, kind, c.L, kind == KIND_G1 ? ntn1 : ntn2, BM);
+    };
 
     // per-lane copy sources of one tile
     struct Src {
         const bf16 *a[C::A_LOADS];
         const bf16 *b[C::B_LOADS];
+        int ldb;
+        bool coherent_a; // A rows written by this launch (pipelined GEMM2)
     };
-    auto make_src = [&](const TileInfo &t, Src &sr) {
+    auto make_src = [&](const Tile &t, Src &sr) {
+        const bool g1 = kind_of(t.kind) == KIND_G1;
 #pragma unroll
         for (int i = 0; i < C::A_LOADS; ++i) {
             // chunk c covers rows 8c .. 8c+7; this lane fills 16-byte unit `lane`
             const int c = wave * C::A_LOADS + i;
             const int r = c * 8 + (lane >> 3);
             const int piece = (lane & 7) ^ ((r >> 1) & 7);
-            int64_t grow;
-            if constexpr (GATHER) {
+            if (g1) {
                 // the 8 row indices of the chunk are wave-uniform: scalar loads
-                int idx[8];
+                int v = 0;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int rj = c * 8 + j < t.rows ? c * 8 + j : 0; // tail rows copy row 0
-                    idx[j] = args.sorted_slot[t.row0 + rj];
+                    const int idx = ldc(args.sorted_slot, t.row0 + rj);
+                    v = (lane >> 3) == j ? idx : v;
                 }
-                int v = idx[0];
-#pragma unroll
-                for (int j = 1; j < 8; ++j)
-                    v = (lane >> 3) == j ? idx[j] : v;
-                grow = v / args.topk;
+                const int64_t grow = v / args.K;
+                sr.a[i] = static_cast<const bf16 *>(args.x) + grow * H + piece * 8;
             } else {
-                grow = t.row0 + (r < t.rows ? r : 0);
+                const int64_t grow = t.row0 + (r < t.rows ? r : 0);
+                sr.a[i] = static_cast<const bf16 *>(args.act) + grow * I + piece * 8;
             }
-            sr.a[i] = A + grow * Kdim + piece * 8;
         }
-        const bf16 *W = static_cast<const bf16 *>(args.B) + (int64_t)t.e * Kdim * ldb;
+        const bf16 *W = g1 ? static_cast<const bf16 *>(args.w1) + (int64_t)t.e * H * (2 * I)
+                           : static_cast<const bf16 *>(args.w2) + (int64_t)t.e * I * H;
+        sr.ldb = g1 ? 2 * I : H;
+        sr.coherent_a = PIPE && !g1;
+        const int pstride = g1 ? I : PW; // column offset of the second panel
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i) {
-            // chunk c covers 1024 bytes = 4 (SwiGLU panels) or 2 k-rows of one panel
+            // chunk c covers 1024 bytes = 4 k-rows of one 128-column panel
             const int c = wave * C::B_LOADS + i;
-            int panel, kr, pp;
-            if constexpr (SWIGLU) {
-                panel = c >> 4;
-                kr = (c & 15) * 4 + (lane >> 4);
-                pp = lane & 15;
-            } else {
-                panel = 0;
-                kr = c * 2 + (lane >> 5);
-                pp = lane & 31;
-            }
+            const int panel = c >> 4;
+            const int kr = (c & 15) * 4 + (lane >> 4);
+            const int pp = lane & 15;
             const int u = (pp >> 1) ^ bswz(kr);
-            const int col = t.n0 + panel * Nout + (2 * u + (pp & 1)) * 8;
-            sr.b[i] = W + (int64_t)kr * ldb + col;
+            const int col = t.n0 + panel * pstride + (2 * u + (pp & 1)) * 8;
+            sr.b[i] = W + (int64_t)kr * sr.ldb + col;
         }
     };
     auto issue = [&](const Src &sr, int kb, unsigned char *sbase) {
         const int k0 = kb * BK;
+        if (PIPE && sr.coherent_a) {
 #pragma unroll
-        for (int i = 0; i < C::A_LOADS; ++i)
-            g2l16(sr.a[i] + k0, (lds_void *)(sbase + (wave * C::A_LOADS + i) * 1024));
+            for (int i = 0; i < C::A_LOADS; ++i)
+                g2l16_coherent(sr.a[i] + k0, (lds_void *)(sbase + (wave * C::A_LOADS + i) * 1024));
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::A_LOADS; ++i)
+                g2l16(sr.a[i] + k0, (lds_void *)(sbase + (wave * C::A_LOADS + i) * 1024));
+        }
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i)
-            g2l16(sr.b[i] + (int64_t)k0 * ldb,
+            g2l16(sr.b[i] + (int64_t)k0 * sr.ldb,
                   (lds_void *)(sbase + C::A_BYTES + (wave * C::B_LOADS + i) * 1024));
     };
 
-    f32x4 acc[C::NPANEL][C::FM][C::FN];
+    f32x4 acc[2][C::FM];
     const int fr = lane & 15;                      // A: row within a 16-row block
     const int fk = lane >> 4;                      // A: piece in a 32-k step; B: 8-k group
     const int tq = lane & 3, tr = (lane >> 2) & 3; // B transposing read: column part / row
 
+    // One K step (BK = 64) of this wave's BM x (2 x 16) block: 4*FM MFMAs fed by
+    // 2*FM 128-bit A reads and 8 transposing 64-bit B reads.  The LDS pipe and
+    // the matrix cores are close to balanced here, so the order is pinned: the
+    // first MFMA group's operands, then one read per MFMA until all reads are
+    // out, then the remaining MFMAs.
     auto compute = [&](const unsigned char *sA) {
         const unsigned char *sB = sA + C::A_BYTES;
+        bf16x8 af[2][C::FM];
+        bf16x8 bfr[2][2]; // [k half][panel]
+        const int nb = wave * WTN + 4 * tq; // column this lane reads
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 32) {
-            bf16x8 af[C::FM];
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int kk = h2 * 32;
 #pragma unroll
             for (int fm = 0; fm < C::FM; ++fm) {
-                const int r = wm * C::WTM + fm * 16 + fr;
+                const int r = fm * 16 + fr;
                 const int piece = ((kk >> 3) + fk) ^ ((r >> 1) & 7);
-                af[fm] = *reinterpret_cast<const bf16x8 *>(sA + r * 128 + piece * 16);
+                af[h2][fm] = *reinterpret_cast<const bf16x8 *>(sA + r * 128 + piece * 16);
             }
 #pragma unroll
-            for (int p = 0; p < C::NPANEL; ++p) {
-                const unsigned char *sP = sB + p * (BK * C::PW * 2);
+            for (int p = 0; p < 2; ++p) {
+                const unsigned char *sP = sB + p * (BK * PW * 2);
+                v4i16 half[2];
 #pragma unroll
-                for (int fn = 0; fn < C::FN; ++fn) {
-                    const int nb = wn * C::WTN + fn * 16 + 4 * tq; // column this lane reads
-                    v4i16 half[2];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int kr = kk + 8 * fk + 4 * h + tr;
-                        const int u = (nb >> 4) ^ bswz(kr);
-                        const unsigned char *addr = sP + kr * (C::PW * 2) + u * 32 + (nb & 15) * 2;
-                        half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(addr));
-                    }
-                    const v8i16 both = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5,
-                                                               6, 7);
-                    const bf16x8 bfrag = __builtin_bit_cast(bf16x8, both);
-#pragma unroll
-                    for (int fm = 0; fm < C::FM; ++fm)
-                        acc[p][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            bfrag, af[fm], acc[p][fm][fn], 0, 0, 0);
+                for (int h = 0; h < 2; ++h) {
+                    const int kr = kk + 8 * fk + 4 * h + tr;
+                    const int u = (nb >> 4) ^ bswz(kr);
+                    const unsigned char *addr = sP + kr * (PW * 2) + u * 32 + (nb & 15) * 2;
+                    half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(addr));
                 }
+                bfr[h2][p] = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
             }
         }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int fm = 0; fm < C::FM; ++fm)
+                    acc[p][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[h2][p], af[h2][fm],
+                                                                         acc[p][fm], 0, 0, 0);
+        constexpr int NDS = 2 * (C::FM + 4), NMF = 4 * C::FM, FIRST = C::FM + 2;
+        constexpr int PAIRS = NDS - FIRST;
+        static_assert(PAIRS <= NMF, "read schedule");
+        __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
+#pragma unroll
+        for (int i = 0; i < PAIRS; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
     };
 
     // epilogue: lane owns row (lane & 15) and columns 4*(lane >> 4) + [0, 4)
-    auto epilogue = [&](const TileInfo &t) {
-        bf16 *__restrict__ Cout = static_cast<bf16 *>(args.C);
-        bf16 *__restrict__ Hs = static_cast<bf16 *>(args.Hsave);
+    // of this wave's 16 columns in each panel
+    auto epilogue = [&](const Tile &t) {
+        const int cw = wave * WTN + 4 * (lane >> 4);
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
-            const int r = wm * C::WTM + fm * 16 + (lane & 15);
+            const int r = fm * 16 + (lane & 15);
             if (r >= t.rows)
                 continue;
             const int64_t p = t.row0 + r;
+            if (kind_of(t.kind) == KIND_G1) {
+                bf16 *__restrict__ Cout = static_cast<bf16 *>(args.act);
+                bf16 *__restrict__ Hs = static_cast<bf16 *>(args.hsave);
+                const int c = t.n0 + cw;
+                u32x2 outv, gv, uv;
+                bf16 *o = reinterpret_cast<bf16 *>(&outv);
+                bf16 *go = reinterpret_cast<bf16 *>(&gv);
+                bf16 *uo = reinterpret_cast<bf16 *>(&uv);
 #pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn) {
-                const int c = t.n0 + wn * C::WTN + fn * 16 + 4 * (lane >> 4);
-                if constexpr (SWIGLU) {
-                    u32x2 outv, gv, uv;
-                    bf16 *o = reinterpret_cast<bf16 *>(&outv);
-                    bf16 *go = reinterpret_cast<bf16 *>(&gv);
-                    bf16 *uo = reinterpret_cast<bf16 *>(&uv);
+                for (int i = 0; i < 4; ++i) {
+                    const float g = acc[0][fm][i], u = acc[1][fm][i];
+                    o[i] = static_cast<bf16>(silu_f(g) * u);
+                    go[i] = static_cast<bf16>(g);
+                    uo[i] = static_cast<bf16>(u);
+                }
+                if (PIPE)
+                    store_coherent(Cout + p * I + c, outv);
+                else
+                    *reinterpret_cast<u32x2 *>(Cout + p * I + c) = outv;
+                if (Hs) {
+                    *reinterpret_cast<u32x2 *>(Hs + p * 2 * I + c) = gv;
+                    *reinterpret_cast<u32x2 *>(Hs + p * 2 * I + I + c) = uv;
+                }
+            } else {
+                bf16 *__restrict__ Cout = static_cast<bf16 *>(args.o);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float g = acc[0][fm][fn][i], u = acc[1][fm][fn][i];
-                        o[i] = static_cast<bf16>(silu_f(g) * u);
-                        go[i] = static_cast<bf16>(g);
-                        uo[i] = static_cast<bf16>(u);
-                    }
-                    *reinterpret_cast<u32x2 *>(Cout + p * Nout + c) = outv;
-                    if (Hs) {
-                        *reinterpret_cast<u32x2 *>(Hs + p * 2 * Nout + c) = gv;
-                        *reinterpret_cast<u32x2 *>(Hs + p * 2 * Nout + Nout + c) = uv;
-                    }
-                } else {
+                for (int pn = 0; pn < 2; ++pn) {
                     u32x2 outv;
                     bf16 *o = reinterpret_cast<bf16 *>(&outv);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        o[i] = static_cast<bf16>(acc[0][fm][fn][i]);
-                    *reinterpret_cast<u32x2 *>(Cout + p * Nout + c) = outv;
+                        o[i] = static_cast<bf16>(acc[pn][fm][i]);
+                    if (PIPE)
+                        store_coherent(Cout + p * H + t.n0 + pn * PW + cw, outv);
+                    else
+                        *reinterpret_cast<u32x2 *>(Cout + p * H + t.n0 + pn * PW + cw) = outv;
                 }
             }
         }
     };
 
-    constexpr int NL = C::A_LOADS + C::B_LOADS;
-    TileInfo cur = decode_tile(args, L, ntn, BM, out_tile);
-    Src scur, snext;
-    make_src(cur, scur);
-    int Lnext = L + per_xcd_wg;
-    bool has_next = Lnext < hi;
-    TileInfo nxt = cur;
-    if (has_next) {
-        nxt = decode_tile(args, Lnext, ntn, BM, out_tile);
-        make_src(nxt, snext);
-    }
-    // prologue: the first two K steps (nk >= 2 on this path)
-    issue(scur, 0, smem);
-    issue(scur, 1, smem + C::STAGE_BYTES);
-    int s_cur = 0; // stage of the current step (global step index % 3)
-    while (true) {
-#pragma unroll
-        for (int p = 0; p < C::NPANEL; ++p)
-#pragma unroll
-            for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-                for (int fn = 0; fn < C::FN; ++fn)
-                    acc[p][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kb = 0; kb < nk; ++kb) {
-            // wait for this wave's copies of the current step (the next step's
-            // may stay in flight), publish the stage, then start the copies of
-            // the step after next into the stage the previous step used
-            if (kb + 1 < nk || has_next)
-                wait_vm<NL>();
-            else
-                wait_vm<0>();
-            lds_barrier();
-            const int s_next = s_cur == 0 ? 2 : s_cur - 1; // (step + 2) % 3
-            if (kb + 2 < nk)
-                issue(scur, kb + 2, smem + s_next * C::STAGE_BYTES);
-            else if (has_next)
-                issue(snext, kb + 2 - nk, smem + s_next * C::STAGE_BYTES);
-            compute(smem + s_cur * C::STAGE_BYTES);
-            s_cur = s_cur == 2 ? 0 : s_cur + 1;
-        }
-        epilogue(cur);
-        if (!has_next)
-            break;
-        cur = nxt;
-        scur = snext;
-        Lnext += per_xcd_wg;
-        has_next = Lnext < hi;
+    // counter that a finished tile releases (-1: none; the test hook drops one)
+    auto release_index = [&](const Tile &t) {
+        if (!PIPE)
+            return -1;
+        if (t.kind == KIND_G1)
+            return (t.mt == args.drop_mt && t.nt == 0) ? -1 : t.mt;
+        return args.max_mtiles + t.mt;
+    };
+    auto release_now = [&](int idx) {
+        if (idx < 0)
+            return;
+        wait_vm<0>();
+        lds_barrier();
+        if (tid == 0)
+            bump(args.ctr + idx);
+    };
+    // a GEMM2 tile reads the act rows of its M-tile: every GEMM1 N-tile of it
+    auto wait_ready = [&](const Tile &t) {
+        if (!PIPE || t.kind != KIND_G2)
+            return;
+        wait_counters(ctr1 + t.mt, ntn1, args);
+    };
+
+    Cursor cc;
+    bool have = false;
+    if (MODE != FAST_G2)
+        have = phase_begin(KIND_G1, cc);
+    if (!have && MODE != FAST_G1)
+        have = phase_begin(KIND_G2, cc);
+
+    if (have) {
+        Tile cur = decode(cc);
+        Tile nxt = cur;
+        Src scur, snext;
+        make_src(cur, scur);
+        Cursor nc = cc;
+        bool has_next = advance(nc);
         if (has_next) {
-            nxt = decode_tile(args, Lnext, ntn, BM, out_tile);
+            nxt = decode(nc);
             make_src(nxt, snext);
+        }
+        // copies run ahead into the next tile only within one GEMM: a GEMM2
+        // tile may read this very tile's output
+        bool chain = has_next && nxt.kind == cur.kind;
+        wait_ready(cur);
+        issue(scur, 0, smem);
+        issue(scur, 1, smem + C::STAGE_BYTES);
+        int s_cur = 0; // stage of the current step (global step index % 3)
+        int owed = -1; // release of the previous tile, made once its stores are done
+        while (true) {
+            const int nk = (kind_of(cur.kind) == KIND_G1 ? H : I) / BK;
+#pragma unroll
+            for (int p = 0; p < 2; ++p)
+#pragma unroll
+                for (int fm = 0; fm < C::FM; ++fm)
+                    acc[p][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < nk; ++kb) {
+                // wait for this wave's copies of the current step (the next
+                // step's may stay in flight), publish the stage, then start the
+                // copies of the step after next into the stage the previous
+                // step used
+                if (kb + 1 < nk || chain)
+                    wait_vm<C::NL>();
+                else
+                    wait_vm<0>();
+                // by step 1 of a tile the previous tile's epilogue stores are
+                // acknowledged (older than the copies still allowed in flight)
+                const bool rel = PIPE && kb == 1 && owed >= 0;
+                if (rel)
+                    wait_vm<0>();
+                lds_barrier();
+                if (rel) {
+                    if (tid == 0)
+                        bump(args.ctr + owed);
+                    owed = -1;
+                }
+                const int s_next = s_cur == 0 ? 2 : s_cur - 1; // (step + 2) % 3
+                if (kb + 2 < nk) {
+                    issue(scur, kb + 2, smem + s_next * C::STAGE_BYTES);
+                } else if (chain) {
+                    if (kb + 2 == nk)
+                        wait_ready(nxt);
+                    issue(snext, kb + 2 - nk, smem + s_next * C::STAGE_BYTES);
+                }
+                compute(smem + s_cur * C::STAGE_BYTES);
+                s_cur = s_cur == 2 ? 0 : s_cur + 1;
+            }
+            epilogue(cur);
+            const int done = release_index(cur);
+            if (!has_next) {
+                release_now(done);
+                break;
+            }
+            const bool chained = chain;
+            cur = nxt;
+            scur = snext;
+            has_next = advance(nc);
+            if (has_next) {
+                nxt = decode(nc);
+                make_src(nxt, snext);
+            }
+            chain = has_next && nxt.kind == cur.kind;
+            if (chained) {
+                owed = done;
+            } else {
+                // a new GEMM: release now, then refill the pipeline.  Stages
+                // s_cur and s_cur + 1 held steps nk-3 and nk-2 of the finished
+                // tile, which every wave left behind at its last barrier.
+                release_now(done);
+                wait_ready(cur);
+                issue(scur, 0, smem + s_cur * C::STAGE_BYTES);
+                issue(scur, 1, smem + (s_cur == 2 ? 0 : s_cur + 1) * C::STAGE_BYTES);
+            }
+        }
+    }
+
+    if constexpr (PIPE) {
+        // Combine (issue page, section 2.1 "Combine"): a unit is a block of BT
+        // tokens (its BT*K slots fit one wave) times 512 columns (one 16-byte
+        // chunk per lane).  It waits for the GEMM2 M-tiles holding its slots,
+        // then sums each token's K rows in k order in fp32 and rounds once (the
+        // arithmetic of the bulk combine kernel); the rows of a token are
+        // loaded 8 at a time so their latencies overlap.
+        const int K = args.K, T = args.T;
+        const int BT = 64 / K;
+        const int nch = H / 8;                 // 16-byte chunks per row
+        const int ntb = (T + BT - 1) / BT;
+        const int ncb = (nch + 63) / 64;
+        const int nunits = ntb * ncb;
+        const int TW = gridDim.x * NW;
+        bf16 *__restrict__ y = static_cast<bf16 *>(args.y);
+        const bf16 *o = static_cast<const bf16 *>(args.o);
+        for (int u = blockIdx.x * NW + wave; u < nunits; u += TW) {
+            const int tb = u / ncb, cb = u - (u / ncb) * ncb;
+            const int t0 = tb * BT;
+            const int t = t0 + lane / K;
+            const int32_t *dep = nullptr;
+            if (lane < BT * K && t < T) {
+                const int64_t s = (int64_t)t0 * K + lane;
+                const int p = args.slot_pos[s];
+                if (p >= 0) {
+                    const int e = args.ids64 ? (int)static_cast<const int64_t *>(args.ids)[s]
+                                             : static_cast<const int32_t *>(args.ids)[s];
+                    dep = ctr2 + args.mtile_off[e] + (p - args.offsets[e]) / BM;
+                }
+            }
+            wait_counters(dep, ntn2, args);
+            const int c = cb * 64 + lane;
+            const bool live = c < nch;
+            const int64_t col = (int64_t)(live ? c : 0) * 8;
+            const int t1 = min(t0 + BT, T);
+            for (int tt = t0; tt < t1; ++tt) {
+                float accv[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    accv[j] = 0.f;
+                for (int k0 = 0; k0 < K; k0 += 8) {
+                    int pk[8];
+                    u32x4 v[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int k = min(k0 + j, K - 1);
+                        pk[j] = k0 + j < K ? ldc(args.slot_pos, tt * K + k) : -1;
+                        v[j] = load_coherent16(o + (int64_t)max(pk[j], 0) * H + col);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        if (pk[j] < 0)
+                            continue;
+                        const float g = ldcf(args.gates, tt * K + k0 + j);
+                        const bf16 *vv = reinterpret_cast<const bf16 *>(&v[j]);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            accv[i] += g * static_cast<float>(vv[i]);
+                    }
+                }
+                if (live) {
+                    u32x4 out;
+                    bf16 *oo = reinterpret_cast<bf16 *>(&out);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        oo[i] = static_cast<bf16>(accv[i]);
+                    *reinterpret_cast<u32x4 *>(y + (int64_t)tt * H + col) = out;
+                }
+            }
         }
     }
 }
 
-template <int BM, bool SWIGLU, bool GATHER, int NW = kFastWaves,
-          int WM = (BM == 128 ? kWavesM128 : 1)>
-static hipError_t launch(const GroupedGemmArgs &a, int num_cus, hipStream_t stream)
+template <int BM, int MODE>
+static hipError_t launch(const FastFwdArgs &a, int num_cus, hipStream_t stream)
 {
-    auto kern = moe_gemm_bf16<BM, SWIGLU, GATHER, NW, WM>;
-    if (a.max_mtiles <= 0)
-        return hipSuccess;
     const int grid = (num_cus + 7) / 8 * 8; // one workgroup per CU, whole XCDs
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((moe_fwd_bf16<BM, MODE>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
@@ -375,22 +653,25 @@ static hipError_t launch(const GroupedGemmArgs &a, int num_cus, hipStream_t stre
 
 bool fast_gemm_supported(int dtype, int64_t H, int64_t I)
 {
-    return dtype == 1 && H % 256 == 0 && I % 128 == 0 && H % fast::BK == 0 &&
-           I % fast::BK == 0;
+    return dtype == 1 && H % fast::TILE_N2 == 0 && I % fast::TILE_N1 == 0;
 }
 
-hipError_t launch_fast_gemm1(const FwdTiles &t, const GroupedGemmArgs &a, hipStream_t stream)
+hipError_t launch_fast_fwd(int mode, int BM, const FastFwdArgs &a, int num_cus, hipStream_t stream)
 {
-    if (t.BM == 64)
-        return fast::launch<64, true, true>(a, t.num_cus, stream);
-    return fast::launch<128, true, true>(a, t.num_cus, stream);
-}
-
-hipError_t launch_fast_gemm2(const FwdTiles &t, const GroupedGemmArgs &a, hipStream_t stream)
-{
-    if (t.BM == 64)
-        return fast::launch<64, false, false>(a, t.num_cus, stream);
-    return fast::launch<128, false, false>(a, t.num_cus, stream);
+    if (a.T <= 0)
+        return hipSuccess;
+    const bool b64 = BM == 64;
+    switch (mode) {
+    case FAST_G1:
+        return b64 ? fast::launch<64, FAST_G1>(a, num_cus, stream)
+                   : fast::launch<128, FAST_G1>(a, num_cus, stream);
+    case FAST_G2:
+        return b64 ? fast::launch<64, FAST_G2>(a, num_cus, stream)
+                   : fast::launch<128, FAST_G2>(a, num_cus, stream);
+    default:
+        return b64 ? fast::launch<64, FAST_PIPE>(a, num_cus, stream)
+                   : fast::launch<128, FAST_PIPE>(a, num_cus, stream);
+    }
 }
 
 } // namespace moe

@@ -25,7 +25,12 @@ struct RouteBufs {
     int32_t *status;      // [1]
     int32_t *sorted_slot; // [TK]
     int32_t *slot_pos;    // [TK]
+    int32_t *ctr;         // optional: release counters of the pipelined forward, zeroed here
+    int nctr;             // their number
 };
+
+// bits of the device status word
+enum { MOE_DEV_BAD_ID = 1, MOE_DEV_TIMEOUT = 2 };
 
 RoutePlan make_route_plan(int64_t TK, int E);
 hipError_t launch_route(const void *ids, bool ids64, int64_t TK, int E, int BM,
@@ -71,8 +76,32 @@ hipError_t launch_gemm2(int dtype, const FwdTiles &t, const GroupedGemmArgs &a,
 
 // bf16 forward fast path (gemm_mfma.hip): H % 256 == 0, I % 128 == 0
 bool fast_gemm_supported(int dtype, int64_t H, int64_t I);
-hipError_t launch_fast_gemm1(const FwdTiles &t, const GroupedGemmArgs &a, hipStream_t stream);
-hipError_t launch_fast_gemm2(const FwdTiles &t, const GroupedGemmArgs &a, hipStream_t stream);
+struct FastFwdArgs {
+    const void *x;               // [T, H]
+    const void *w1;              // [E, H, 2I]
+    const void *w2;              // [E, I, H]
+    void *act;                   // [TK, I]
+    void *hsave;                 // optional [TK, 2I]
+    void *o;                     // [TK, H]
+    void *y;                     // [T, H] (pipelined mode)
+    const float *gates;          // [T, K] (pipelined mode)
+    const void *ids;             // [T, K] int32 or int64 (pipelined mode)
+    const int32_t *sorted_slot;  // [TK]
+    const int32_t *slot_pos;     // [TK]
+    const int32_t *offsets;      // [E + 1]
+    const int32_t *mtile_off;    // [E + 1]
+    const int32_t *mtile_expert; // [max_mtiles]
+    int32_t *ctr;                // pipelined: [2 * max_mtiles] zeroed counters
+    int32_t *status;             // device status word (MOE_DEV_* bits)
+    int64_t timeout_ticks;       // watchdog of every wait, in s_memrealtime ticks
+    int T, H, I, E, K;
+    int ids64;
+    int max_mtiles;
+    int drop_mt;                 // test hook: M-tile whose first GEMM1 release is dropped (-1)
+};
+enum { FAST_G1 = 0, FAST_G2 = 1, FAST_PIPE = 2 };
+hipError_t launch_fast_fwd(int mode, int BM, const FastFwdArgs &a, int num_cus,
+                           hipStream_t stream);
 
 // bf16 engine (gemm_engine.hip): forward F1/F2 and backward B2/B4/B5/B7
 struct EngineArgs {

@@ -16,7 +16,8 @@
 //               and writes its column of hist[E][NB] plus a bad-id flag.
 //   2. scan:    one 1024-thread block turns hist into per-(expert, chunk)
 //               exclusive bases, then scans counts and M-tile counts over
-//               experts and writes the status word.
+//               experts, writes the status word and zeroes the release
+//               counters of the pipelined forward that follows.
 //   3. scatter: one wave per chunk walks its slots in order, 64 at a time;
 //               lanes holding the same expert find each other with ballots
 //               over the id bits, so the rank inside the round is a popcount
@@ -97,8 +98,11 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ 
                                                           int32_t *__restrict__ offsets,
                                                           int32_t *__restrict__ mtile_off,
                                                           int32_t *__restrict__ mtile_expert,
-                                                          int32_t *__restrict__ status)
+                                                          int32_t *__restrict__ status,
+                                                          int32_t *__restrict__ ctr, int nctr)
 {
+    for (int j = threadIdx.x; j < nctr; j += 1024)
+        ctr[j] = 0;
     __shared__ int32_t s_cnt[1024];
     __shared__ int32_t s_moff[1025];
     __shared__ int32_t s_w[40];
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ 
         offsets[E] = total;
         mtile_off[E] = mtotal;
         s_moff[E] = mtotal;
-        status[0] = anybad ? 1 : 0;
+        status[0] = anybad ? MOE_DEV_BAD_ID : 0;
     }
     __syncthreads();
     // owner expert of every M-tile: the last e with s_moff[e] <= j
@@ -278,7 +282,7 @@ hipError_t launch_route(const void *ids, bool ids64, int64_t TK, int E, int BM,
     const int nb_scan = TK > 0 ? rp.NB : 0;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, rb.hist, rb.bad, E,
                        nb_scan, BM, rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert,
-                       rb.status);
+                       rb.status, rb.ctr, rb.ctr ? rb.nctr : 0);
     if (TK > 0) {
         if (ids64)
             hipLaunchKernelGGL(route_scatter_kernel<int64_t>, dim3(rp.NB), dim3(64), lds, stream,
