@@ -20,24 +20,28 @@
 //
 // Tile engine, organised for the CDNA4 memory pipeline:
 //  * Global -> LDS copies go straight into LDS (16 bytes per lane, no
-//    register staging), three stages deep, two K steps ahead of the matrix
-//    cores; each wave waits only for its own copies of the stage it is about
-//    to use, then one barrier per K step publishes the stage.
-//  * A (token rows, K-contiguous) lands as [BM][64] with the 16-byte piece
-//    index XOR-ed by (row / 2) % 8, so the 16 lanes of one 128-bit LDS read
-//    hit 16 different bank groups.  The dispatch gather x[sorted_slot / K] is
+//    register staging), NSTAGE stages deep, NSTAGE - 1 K steps ahead of the
+//    matrix cores; each wave waits only for its own copies of the stage it is
+//    about to use, then one barrier per K step publishes the stage.
+//  * A (token rows, K-contiguous) lands as [BM][BK] with the 16-byte piece
+//    index XOR-ed by a function of the row, so the 16 lanes of one 128-bit
+//    LDS read hit 16 different bank groups.  The dispatch gather x[sorted_slot / K] is
 //    just the per-lane source address of those copies.
 //  * B (weights, N-contiguous [k][n]) lands untransposed as two panels of
-//    [64][128] with the 32-byte unit index XOR-ed by a 3-bit hash of k; the
+//    [BK][128] with the 32-byte unit index XOR-ed by a 3-bit hash of k; the
 //    MFMA fragments are read with the transposing 64-bit LDS read.  GEMM1's
 //    panels are 128 gate and the matching 128 up columns, so SwiGLU pairs two
 //    accumulators of one lane; GEMM2's panels are 256 adjacent output columns.
 //  * The matrix-core step computes C^T = W^T · X^T (weights as the first
 //    operand), so each lane owns 4 consecutive output columns of one row and
 //    the epilogue writes 8 bytes per lane.
-//  * Block tile BM (64 or 128) rows x 256 weight columns, 8 waves (two per
-//    SIMD: one wave's MFMAs cover the other's LDS waits), each owning all BM
-//    rows and 16 columns of each panel.
+//  * Block tile BM rows x 256 weight columns, 8 waves (two per SIMD: one
+//    wave's MFMAs cover the other's LDS waits): for BM = 64 or 128 each wave
+//    owns all BM rows and 16 columns of each panel (BK = 64, 3 stages); for
+//    BM = 256 the waves are 2 x 4 and each owns 128 rows and 32 columns of
+//    each panel (BK = 32, 4 stages), a third fewer LDS reads and copied bytes
+//    per flop.  A wave whose 128 rows lie past an expert's count skips its
+//    MFMAs, so tall tiles waste no more matrix-core time than short ones.
 //  * Persistent: one workgroup per CU walks an XCD-local slice of the tile
 //    order (the hardware hands workgroup b to XCD b % 8), so tiles in flight
 //    on one XCD share weight panels and token rows in its L2; the next tile's
@@ -53,31 +57,51 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-constexpr int BK = 64;
-constexpr int NSTAGE = 3;
 constexpr int NW = 8;           // waves per workgroup
 constexpr int PW = 128;         // weight columns per panel (two panels per tile)
-constexpr int WTN = PW / NW;    // columns per wave per panel
 constexpr int TILE_N1 = PW;     // GEMM1 output columns per tile
 constexpr int TILE_N2 = 2 * PW; // GEMM2 output columns per tile
 
 enum { KIND_G1 = 1, KIND_G2 = 2 };
 
+// Block tile BM x (2 x 128): BM = 64 or 128 with BK = 64, a 3-stage ring and
+// all 8 waves side by side along N; BM = 256 with BK = 32, a 4-stage ring and
+// the waves as 2 (M) x 4 (N), so each wave owns 128 rows x 32 columns per
+// panel and needs a third fewer LDS reads and copied bytes per flop.
 template <int BM_> struct Cfg {
     static constexpr int BM = BM_;
-    static constexpr int FM = BM / 16;
+    static constexpr int BK = BM == 256 ? 32 : 64;   // K per step
+    static constexpr int NSTAGE = BM == 256 ? 4 : 3; // LDS ring depth
+    static constexpr int WM = BM == 256 ? 2 : 1;     // waves along M
+    static constexpr int WN = NW / WM;               // waves along N
+    static constexpr int WTM = BM / WM;              // rows per wave
+    static constexpr int WTN = PW / WN;              // columns per wave per panel
+    static constexpr int FM = WTM / 16, FN = WTN / 16;
+    static constexpr int KH = BK / 32;               // 32-deep MFMA steps per K step
+    static constexpr int PIECES = BK / 8;            // 16-byte pieces per A row
+    static constexpr int RPC = 1024 / (BK * 2);      // A rows per 1 KB copy chunk
+    static constexpr int CPP = BK / 4;               // 1 KB B chunks per panel (4 k-rows each)
     static constexpr int A_BYTES = BM * BK * 2;
-    static constexpr int B_BYTES = BK * 2 * PW * 2; // 32 KB
+    static constexpr int B_BYTES = BK * 2 * PW * 2;
     static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
     static constexpr int A_LOADS = A_BYTES / 1024 / NW; // per wave per stage
     static constexpr int B_LOADS = B_BYTES / 1024 / NW;
     static constexpr int NL = A_LOADS + B_LOADS;
     static_assert(A_LOADS >= 1 && A_LOADS * NW * 1024 == A_BYTES, "stage split");
-    static_assert(B_LOADS * NW * 1024 == B_BYTES, "stage split");
+    static_assert(B_LOADS >= 1 && B_LOADS * NW * 1024 == B_BYTES, "stage split");
     static_assert(NSTAGE * STAGE_BYTES <= 160 * 1024, "LDS");
+    static_assert(FN >= 1 && KH >= 1, "wave tile");
 };
 
 __device__ __forceinline__ int bswz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+
+// swizzled 16-byte piece of A row r: rows of 8 pieces (128 B) XOR by
+// (r / 2) % 8, rows of 4 pieces (64 B) by (r / 4) % 4, so the 16 rows that one
+// 128-bit fragment read touches fall in 16 different bank groups
+template <int PIECES> __device__ __forceinline__ int aswz(int r, int piece)
+{
+    return PIECES == 8 ? piece ^ ((r >> 1) & 7) : piece ^ ((r >> 2) & 3);
+}
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Routing metadata that earlier launches wrote and this kernel only reads:
@@ -169,9 +193,11 @@ __device__ __forceinline__ int poll(const int32_t *p)
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// one increment per wave (lane 0 only)
 __device__ __forceinline__ void bump(int32_t *p)
 {
-    __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__lane_id() == 0)
+        __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wave-wide wait until every lane's counter (p != nullptr) reaches `need`.
@@ -239,6 +265,7 @@ template <int BM, int MODE>
 __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16(FastFwdArgs args)
 {
     using C = Cfg<BM>;
+    constexpr int BK = C::BK, NSTAGE = C::NSTAGE;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * C::STAGE_BYTES];
 
     constexpr bool PIPE = MODE == FAST_PIPE;
@@ -249,6 +276,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16(FastFwdArgs args)
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = uni(tid >> 6);
+    const int wm = wave / C::WN, wn = wave % C::WN; // this wave's block of the tile
     int32_t *const ctr1 = args.ctr;                   // GEMM1 N-tiles done per M-tile
     int32_t *const ctr2 = args.ctr + args.max_mtiles; // GEMM2 N-tiles done per M-tile
 
@@ -287,18 +315,19 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16(FastFwdArgs args)
         const bool g1 = kind_of(t.kind) == KIND_G1;
 #pragma unroll
         for (int i = 0; i < C::A_LOADS; ++i) {
-            // chunk c covers rows 8c .. 8c+7; this lane fills 16-byte unit `lane`
+            // chunk c covers rows RPC*c .. RPC*c + RPC-1; this lane fills 16-byte
+            // unit `lane` of it
             const int c = wave * C::A_LOADS + i;
-            const int r = c * 8 + (lane >> 3);
-            const int piece = (lane & 7) ^ ((r >> 1) & 7);
+            const int r = c * C::RPC + lane / C::PIECES;
+            const int piece = aswz<C::PIECES>(r, lane % C::PIECES);
             if (g1) {
-                // the 8 row indices of the chunk are wave-uniform: scalar loads
+                // the chunk's row indices are wave-uniform: scalar loads
                 int v = 0;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int rj = c * 8 + j < t.rows ? c * 8 + j : 0; // tail rows copy row 0
+                for (int j = 0; j < C::RPC; ++j) {
+                    const int rj = c * C::RPC + j < t.rows ? c * C::RPC + j : 0; // tail rows copy row 0
                     const int idx = ldc(args.sorted_slot, t.row0 + rj);
-                    v = (lane >> 3) == j ? idx : v;
+                    v = lane / C::PIECES == j ? idx : v;
                 }
                 const int64_t grow = v / args.K;
                 sr.a[i] = static_cast<const bf16 *>(args.x) + grow * H + piece * 8;
@@ -316,8 +345,8 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16(FastFwdArgs args)
         for (int i = 0; i < C::B_LOADS; ++i) {
             // chunk c covers 1024 bytes = 4 k-rows of one 128-column panel
             const int c = wave * C::B_LOADS + i;
-            const int panel = c >> 4;
-            const int kr = (c & 15) * 4 + (lane >> 4);
+            const int panel = c / C::CPP;
+            const int kr = (c % C::CPP) * 4 + (lane >> 4);
             const int pp = lane & 15;
             const int u = (pp >> 1) ^ bswz(kr);
             const int col = t.n0 + panel * pstride + (2 * u + (pp & 1)) * 8;
@@ -341,55 +370,60 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16(FastFwdArgs args)
                   (lds_void *)(sbase + C::A_BYTES + (wave * C::B_LOADS + i) * 1024));
     };
 
-    f32x4 acc[2][C::FM];
+    f32x4 acc[2][C::FM][C::FN];
     const int fr = lane & 15;                      // A: row within a 16-row block
     const int fk = lane >> 4;                      // A: piece in a 32-k step; B: 8-k group
     const int tq = lane & 3, tr = (lane >> 2) & 3; // B transposing read: column part / row
 
-    // One K step (BK = 64) of this wave's BM x (2 x 16) block: 4*FM MFMAs fed by
-    // 2*FM 128-bit A reads and 8 transposing 64-bit B reads.  The LDS pipe and
-    // the matrix cores are close to balanced here, so the order is pinned: the
-    // first MFMA group's operands, then one read per MFMA until all reads are
-    // out, then the remaining MFMAs.
+    // One K step of this wave's WTM x (2 x WTN) block: 2*FN*FM MFMAs per 32 k,
+    // fed by FM 128-bit A reads and 4*FN transposing 64-bit B reads.  The LDS
+    // pipe and the matrix cores are close to balanced, so the order is pinned:
+    // the first MFMA group's operands, then one read per MFMA until all reads
+    // are out, then the remaining MFMAs.
     auto compute = [&](const unsigned char *sA) {
         const unsigned char *sB = sA + C::A_BYTES;
-        bf16x8 af[2][C::FM];
-        bf16x8 bfr[2][2]; // [k half][panel]
-        const int nb = wave * WTN + 4 * tq; // column this lane reads
+        bf16x8 af[C::KH][C::FM];
+        bf16x8 bfr[C::KH][2][C::FN]; // [k half][panel][16-column block]
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
+        for (int h2 = 0; h2 < C::KH; ++h2) {
             const int kk = h2 * 32;
 #pragma unroll
             for (int fm = 0; fm < C::FM; ++fm) {
-                const int r = fm * 16 + fr;
-                const int piece = ((kk >> 3) + fk) ^ ((r >> 1) & 7);
-                af[h2][fm] = *reinterpret_cast<const bf16x8 *>(sA + r * 128 + piece * 16);
+                const int r = wm * C::WTM + fm * 16 + fr;
+                const int piece = aswz<C::PIECES>(r, (kk >> 3) + fk);
+                af[h2][fm] = *reinterpret_cast<const bf16x8 *>(sA + r * (BK * 2) + piece * 16);
             }
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
                 const unsigned char *sP = sB + p * (BK * PW * 2);
-                v4i16 half[2];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int kr = kk + 8 * fk + 4 * h + tr;
-                    const int u = (nb >> 4) ^ bswz(kr);
-                    const unsigned char *addr = sP + kr * (PW * 2) + u * 32 + (nb & 15) * 2;
-                    half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(addr));
+                for (int fn = 0; fn < C::FN; ++fn) {
+                    const int nb = wn * C::WTN + fn * 16 + 4 * tq; // column this lane reads
+                    v4i16 half[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int kr = kk + 8 * fk + 4 * h + tr;
+                        const int u = (nb >> 4) ^ bswz(kr);
+                        const unsigned char *addr = sP + kr * (PW * 2) + u * 32 + (nb & 15) * 2;
+                        half[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(addr));
+                    }
+                    bfr[h2][p][fn] = __builtin_bit_cast(
+                        bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
                 }
-                bfr[h2][p] = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
             }
         }
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
+        for (int h2 = 0; h2 < C::KH; ++h2)
 #pragma unroll
             for (int p = 0; p < 2; ++p)
 #pragma unroll
-                for (int fm = 0; fm < C::FM; ++fm)
-                    acc[p][fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[h2][p], af[h2][fm],
-                                                                         acc[p][fm], 0, 0, 0);
-        constexpr int NDS = 2 * (C::FM + 4), NMF = 4 * C::FM, FIRST = C::FM + 2;
-        constexpr int PAIRS = NDS - FIRST;
+                for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+                    for (int fm = 0; fm < C::FM; ++fm)
+                        acc[p][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            bfr[h2][p][fn], af[h2][fm], acc[p][fm][fn], 0, 0, 0);
+        constexpr int NDS = C::KH * (C::FM + 4 * C::FN), NMF = C::KH * 2 * C::FN * C::FM;
+        constexpr int FIRST = C::FM + 2, PAIRS = NDS - FIRST;
         static_assert(PAIRS <= NMF, "read schedule");
         __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
 #pragma unroll
@@ -401,79 +435,75 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16(FastFwdArgs args)
     };
 
     // epilogue: lane owns row (lane & 15) and columns 4*(lane >> 4) + [0, 4)
-    // of this wave's 16 columns in each panel
+    // of each 16x16 block of this wave
     auto epilogue = [&](const Tile &t) {
-        const int cw = wave * WTN + 4 * (lane >> 4);
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
-            const int r = fm * 16 + (lane & 15);
+            const int r = wm * C::WTM + fm * 16 + (lane & 15);
             if (r >= t.rows)
                 continue;
             const int64_t p = t.row0 + r;
-            if (kind_of(t.kind) == KIND_G1) {
-                bf16 *__restrict__ Cout = static_cast<bf16 *>(args.act);
-                bf16 *__restrict__ Hs = static_cast<bf16 *>(args.hsave);
-                const int c = t.n0 + cw;
-                u32x2 outv, gv, uv;
-                bf16 *o = reinterpret_cast<bf16 *>(&outv);
-                bf16 *go = reinterpret_cast<bf16 *>(&gv);
-                bf16 *uo = reinterpret_cast<bf16 *>(&uv);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float g = acc[0][fm][i], u = acc[1][fm][i];
-                    o[i] = static_cast<bf16>(silu_f(g) * u);
-                    go[i] = static_cast<bf16>(g);
-                    uo[i] = static_cast<bf16>(u);
-                }
-                if (PIPE)
-                    store_coherent(Cout + p * I + c, outv);
-                else
-                    *reinterpret_cast<u32x2 *>(Cout + p * I + c) = outv;
-                if (Hs) {
-                    *reinterpret_cast<u32x2 *>(Hs + p * 2 * I + c) = gv;
-                    *reinterpret_cast<u32x2 *>(Hs + p * 2 * I + I + c) = uv;
-                }
-            } else {
-                bf16 *__restrict__ Cout = static_cast<bf16 *>(args.o);
-#pragma unroll
-                for (int pn = 0; pn < 2; ++pn) {
-                    u32x2 outv;
+            for (int fn = 0; fn < C::FN; ++fn) {
+                const int cw = wn * C::WTN + fn * 16 + 4 * (lane >> 4);
+                if (kind_of(t.kind) == KIND_G1) {
+                    bf16 *__restrict__ Cout = static_cast<bf16 *>(args.act);
+                    bf16 *__restrict__ Hs = static_cast<bf16 *>(args.hsave);
+                    const int c = t.n0 + cw;
+                    u32x2 outv, gv, uv;
                     bf16 *o = reinterpret_cast<bf16 *>(&outv);
+                    bf16 *go = reinterpret_cast<bf16 *>(&gv);
+                    bf16 *uo = reinterpret_cast<bf16 *>(&uv);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        o[i] = static_cast<bf16>(acc[pn][fm][i]);
+                    for (int i = 0; i < 4; ++i) {
+                        const float g = acc[0][fm][fn][i], u = acc[1][fm][fn][i];
+                        o[i] = static_cast<bf16>(silu_f(g) * u);
+                        go[i] = static_cast<bf16>(g);
+                        uo[i] = static_cast<bf16>(u);
+                    }
                     if (PIPE)
-                        store_coherent(Cout + p * H + t.n0 + pn * PW + cw, outv);
+                        store_coherent(Cout + p * I + c, outv);
                     else
-                        *reinterpret_cast<u32x2 *>(Cout + p * H + t.n0 + pn * PW + cw) = outv;
+                        *reinterpret_cast<u32x2 *>(Cout + p * I + c) = outv;
+                    if (Hs) {
+                        *reinterpret_cast<u32x2 *>(Hs + p * 2 * I + c) = gv;
+                        *reinterpret_cast<u32x2 *>(Hs + p * 2 * I + I + c) = uv;
+                    }
+                } else {
+                    bf16 *__restrict__ Cout = static_cast<bf16 *>(args.o);
+#pragma unroll
+                    for (int pn = 0; pn < 2; ++pn) {
+                        u32x2 outv;
+                        bf16 *o = reinterpret_cast<bf16 *>(&outv);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            o[i] = static_cast<bf16>(acc[pn][fm][fn][i]);
+                        if (PIPE)
+                            store_coherent(Cout + p * H + t.n0 + pn * PW + cw, outv);
+                        else
+                            *reinterpret_cast<u32x2 *>(Cout + p * H + t.n0 + pn * PW + cw) = outv;
+                    }
                 }
             }
         }
     };
 
-    // counter that a finished tile releases (-1: none; the test hook drops one)
+    // Counter that a finished tile releases (-1: none).  Every wave bumps it
+    // once its own stores of the tile are acknowledged, so a tile is complete
+    // at NW bumps per N-tile; the test hook drops one wave's bump.
     auto release_index = [&](const Tile &t) {
         if (!PIPE)
             return -1;
         if (t.kind == KIND_G1)
-            return (t.mt == args.drop_mt && t.nt == 0) ? -1 : t.mt;
+            return (t.mt == args.drop_mt && t.nt == 0 && wave == 0) ? -1 : t.mt;
         return args.max_mtiles + t.mt;
-    };
-    auto release_now = [&](int idx) {
-        if (idx < 0)
-            return;
-        wait_vm<0>();
-        lds_barrier();
-        if (tid == 0)
-            bump(args.ctr + idx);
     };
     // a GEMM2 tile reads the act rows of its M-tile: every GEMM1 N-tile of it
     auto wait_ready = [&](const Tile &t) {
         if (!PIPE || t.kind != KIND_G2)
             return;
-        wait_counters(ctr1 + t.mt, ntn1, args);
+        wait_counters(ctr1 + t.mt, NW * ntn1, args);
     };
-
     Cursor cc;
     bool have = false;
     if (MODE != FAST_G2)
@@ -495,53 +525,64 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16(FastFwdArgs args)
         // copies run ahead into the next tile only within one GEMM: a GEMM2
         // tile may read this very tile's output
         bool chain = has_next && nxt.kind == cur.kind;
+        // first NSTAGE-1 steps (every tile has at least that many K steps)
         wait_ready(cur);
-        issue(scur, 0, smem);
-        issue(scur, 1, smem + C::STAGE_BYTES);
-        int s_cur = 0; // stage of the current step (global step index % 3)
+#pragma unroll
+        for (int st = 0; st < NSTAGE - 1; ++st)
+            issue(scur, st, smem + st * C::STAGE_BYTES);
+        int s_cur = 0; // stage of the current step (global step index % NSTAGE)
         int owed = -1; // release of the previous tile, made once its stores are done
         while (true) {
             const int nk = (kind_of(cur.kind) == KIND_G1 ? H : I) / BK;
+            // a wave whose rows all lie past the expert's count skips the MFMAs
+            const bool active = wm * C::WTM < cur.rows;
 #pragma unroll
             for (int p = 0; p < 2; ++p)
 #pragma unroll
                 for (int fm = 0; fm < C::FM; ++fm)
-                    acc[p][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; ++fn)
+                        acc[p][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
             for (int kb = 0; kb < nk; ++kb) {
-                // wait for this wave's copies of the current step (the next
-                // step's may stay in flight), publish the stage, then start the
-                // copies of the step after next into the stage the previous
-                // step used
-                if (kb + 1 < nk || chain)
+                // wait for this wave's copies of the current step (copy groups
+                // issued after it may stay in flight), publish the stage, then
+                // start the copies of step kb + NSTAGE - 1 into the stage the
+                // previous step used
+                const int ahead = min(NSTAGE - 2, nk - 1 - kb + (chain ? NSTAGE - 1 : 0));
+                if (ahead >= 2)
+                    wait_vm<2 * C::NL>();
+                else if (ahead == 1)
                     wait_vm<C::NL>();
                 else
                     wait_vm<0>();
-                // by step 1 of a tile the previous tile's epilogue stores are
-                // acknowledged (older than the copies still allowed in flight)
-                const bool rel = PIPE && kb == 1 && owed >= 0;
-                if (rel)
-                    wait_vm<0>();
-                lds_barrier();
-                if (rel) {
-                    if (tid == 0)
-                        bump(args.ctr + owed);
+                // by step NSTAGE - 2 of a tile every copy group still allowed in
+                // flight was issued after the previous tile's epilogue stores,
+                // so those are acknowledged: release that tile
+                if (PIPE && kb == NSTAGE - 2 && owed >= 0) {
+                    bump(args.ctr + owed);
                     owed = -1;
                 }
-                const int s_next = s_cur == 0 ? 2 : s_cur - 1; // (step + 2) % 3
-                if (kb + 2 < nk) {
-                    issue(scur, kb + 2, smem + s_next * C::STAGE_BYTES);
+                lds_barrier();
+                const int s_next = s_cur == 0 ? NSTAGE - 1 : s_cur - 1; // (step + NSTAGE - 1) % NSTAGE
+                const int step = kb + NSTAGE - 1;
+                if (step < nk) {
+                    issue(scur, step, smem + s_next * C::STAGE_BYTES);
                 } else if (chain) {
-                    if (kb + 2 == nk)
+                    if (step == nk)
                         wait_ready(nxt);
-                    issue(snext, kb + 2 - nk, smem + s_next * C::STAGE_BYTES);
+                    issue(snext, step - nk, smem + s_next * C::STAGE_BYTES);
                 }
-                compute(smem + s_cur * C::STAGE_BYTES);
-                s_cur = s_cur == 2 ? 0 : s_cur + 1;
+                if (active)
+                    compute(smem + s_cur * C::STAGE_BYTES);
+                s_cur = s_cur == NSTAGE - 1 ? 0 : s_cur + 1;
             }
             epilogue(cur);
             const int done = release_index(cur);
             if (!has_next) {
-                release_now(done);
+                if (done >= 0) {
+                    wait_vm<0>();
+                    bump(args.ctr + done);
+                }
                 break;
             }
             const bool chained = chain;
@@ -556,13 +597,19 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16(FastFwdArgs args)
             if (chained) {
                 owed = done;
             } else {
-                // a new GEMM: release now, then refill the pipeline.  Stages
-                // s_cur and s_cur + 1 held steps nk-3 and nk-2 of the finished
-                // tile, which every wave left behind at its last barrier.
-                release_now(done);
+                // A new GEMM: release the finished tile, then refill the
+                // pipeline.  Every stage but the last step's was left behind by
+                // all waves at the last barrier: s_cur, s_cur + 1, ... (mod
+                // NSTAGE).  Each wave releases before it waits for the new
+                // tile's inputs, so no wait depends on a release behind it.
+                if (done >= 0) {
+                    wait_vm<0>();
+                    bump(args.ctr + done);
+                }
                 wait_ready(cur);
-                issue(scur, 0, smem + s_cur * C::STAGE_BYTES);
-                issue(scur, 1, smem + (s_cur == 2 ? 0 : s_cur + 1) * C::STAGE_BYTES);
+#pragma unroll
+                for (int st = 0; st < NSTAGE - 1; ++st)
+                    issue(scur, st, smem + ((s_cur + st) % NSTAGE) * C::STAGE_BYTES);
             }
         }
     }
@@ -597,7 +644,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16(FastFwdArgs args)
                     dep = ctr2 + args.mtile_off[e] + (p - args.offsets[e]) / BM;
                 }
             }
-            wait_counters(dep, ntn2, args);
+            wait_counters(dep, NW * ntn2, args);
             const int c = cb * 64 + lane;
             const bool live = c < nch;
             const int64_t col = (int64_t)(live ? c : 0) * 8;
@@ -656,21 +703,26 @@ bool fast_gemm_supported(int dtype, int64_t H, int64_t I)
     return dtype == 1 && H % fast::TILE_N2 == 0 && I % fast::TILE_N1 == 0;
 }
 
+template <int MODE>
+static hipError_t launch_bm(int BM, const FastFwdArgs &a, int num_cus, hipStream_t stream)
+{
+    if (BM == 64)
+        return fast::launch<64, MODE>(a, num_cus, stream);
+    if (BM == 128)
+        return fast::launch<128, MODE>(a, num_cus, stream);
+    return fast::launch<256, MODE>(a, num_cus, stream);
+}
+
 hipError_t launch_fast_fwd(int mode, int BM, const FastFwdArgs &a, int num_cus, hipStream_t stream)
 {
     if (a.T <= 0)
         return hipSuccess;
-    const bool b64 = BM == 64;
+    if (BM != 64 && BM != 128 && BM != 256)
+        return hipErrorInvalidValue;
     switch (mode) {
-    case FAST_G1:
-        return b64 ? fast::launch<64, FAST_G1>(a, num_cus, stream)
-                   : fast::launch<128, FAST_G1>(a, num_cus, stream);
-    case FAST_G2:
-        return b64 ? fast::launch<64, FAST_G2>(a, num_cus, stream)
-                   : fast::launch<128, FAST_G2>(a, num_cus, stream);
-    default:
-        return b64 ? fast::launch<64, FAST_PIPE>(a, num_cus, stream)
-                   : fast::launch<128, FAST_PIPE>(a, num_cus, stream);
+    case FAST_G1: return launch_bm<FAST_G1>(BM, a, num_cus, stream);
+    case FAST_G2: return launch_bm<FAST_G2>(BM, a, num_cus, stream);
+    default: return launch_bm<FAST_PIPE>(BM, a, num_cus, stream);
     }
 }
 
