@@ -198,6 +198,8 @@ def main():
 
     if w.dtype == "bf16" and not w.name.startswith("decode"):
         out["dense_reference"] = dense_reference(w, dev)
+    if w.name.startswith("decode"):
+        out["hbm_reference"] = hbm_reference(dev)
 
     if args.copy_calibration_mb:
         n = args.copy_calibration_mb * (1 << 20) // 4
@@ -235,6 +237,26 @@ def dense_reference(w, dev, reps=20):
                      "tflops": 2.0 * M * Kd * N / (ms * 1e-3) / 1e12}
         del a, b
     return out
+
+
+def hbm_reference(dev, mib=2048, reps=10):
+    """Context only: a large device-to-device copy (torch's copy kernel), as an
+    achievable HBM rate for comparison with the weight-streaming decode GEMMs."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.empty(n, device=dev, dtype=torch.float32).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / reps * 1e3
+    del src, dst
+    return {"bytes_moved": 2 * n * 4, "ms": ms, "gbs": 2 * n * 4 / (ms * 1e-3) / 1e9}
 
 
 def measured_traffic(workload_name, kernel):

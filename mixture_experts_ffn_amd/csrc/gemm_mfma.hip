@@ -623,7 +623,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16(FastFwdArgs args)
         // loaded 8 at a time so their latencies overlap.
         const int K = args.K, T = args.T;
         const int BT = 64 / K;
-        const int nch = H / 8;                 // 16-byte chunks per row
+        const int nch = H / 8; // 16-byte chunks per row
         const int ntb = (T + BT - 1) / BT;
         const int ncb = (nch + 63) / 64;
         const int nunits = ntb * ncb;
