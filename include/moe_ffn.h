@@ -97,9 +97,17 @@ typedef struct {
  * of one GEMM1 tile and uses a 20 ms watchdog, so that the waits behind it
  * time out (status MOE_FFN_DEV_TIMEOUT) while every kernel still ends. */
 #define MOE_FFN_TEST_DROP_RELEASE 0x100u
+/* bwd: read the saved context's header on the host first (synchronising the
+ * stream) and return MOE_FFN_ERR_SAVED, before anything is launched, if it was
+ * not written by a forward of this problem.  Without the flag the same check
+ * runs on the device: on a mismatch the backward reads nothing else from
+ * `saved`, every output is zero and the workspace status word gets
+ * MOE_FFN_DEV_BAD_SAVED. */
+#define MOE_FFN_CHECK_SAVED 0x4u
 /* Bits of the device status word (moe_ffn_read_status). */
-#define MOE_FFN_DEV_BAD_ID 0x1  /* an expert id was outside [0, E); its slot was dropped */
-#define MOE_FFN_DEV_TIMEOUT 0x2 /* a pipelined wait hit the watchdog; outputs are unreliable */
+#define MOE_FFN_DEV_BAD_ID 0x1    /* an expert id was outside [0, E); its slot was dropped */
+#define MOE_FFN_DEV_TIMEOUT 0x2   /* a pipelined wait hit the watchdog; outputs are unreliable */
+#define MOE_FFN_DEV_BAD_SAVED 0x4 /* bwd: the saved context did not belong to this problem */
 
 /* Stages of the forward, for the timing hook below. */
 enum {
@@ -133,8 +141,9 @@ typedef struct {
 /* ---- forward ------------------------------------------------------------ */
 
 /* Sizes of the forward workspace and of the saved context that the backward
- * needs (route arrays and the pre-activation h = x·up_proj_weight in the
- * problem dtype).  Pure host function; no device is touched. */
+ * needs (a header naming the problem, the route arrays and the pre-activation
+ * h = x·up_proj_weight in the problem dtype).  Pure host function; no device
+ * is touched. */
 int moe_ffn_fwd_workspace_size(const moe_ffn_problem *p, uint32_t flags, size_t *ws_bytes,
                                size_t *saved_bytes);
 
@@ -199,8 +208,9 @@ int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, cons
 /* ---- status and measurement helpers ---------------------------------------- */
 
 /* Synchronises `stream`, then reads the device status word that the last
- * forward or route call on this workspace left: 0, or an OR of
- * MOE_FFN_DEV_BAD_ID and MOE_FFN_DEV_TIMEOUT. */
+ * forward, route or backward call on this workspace left: 0, or an OR of
+ * MOE_FFN_DEV_BAD_ID and MOE_FFN_DEV_TIMEOUT (forward, route) or
+ * MOE_FFN_DEV_BAD_SAVED (backward). */
 int moe_ffn_read_status(const void *ws, void *stream, int32_t *device_status);
 
 /* Static text for a status code. */

@@ -53,7 +53,8 @@ F32, BF16, I32, I64 = 0, 1, 2, 3
 CHECK_IDS = 0x1
 PIPELINE = 0x2
 TEST_DROP_RELEASE = 0x100
-DEV_BAD_ID, DEV_TIMEOUT = 0x1, 0x2
+CHECK_SAVED = 0x4
+DEV_BAD_ID, DEV_TIMEOUT, DEV_BAD_SAVED = 0x1, 0x2, 0x4
 STAGES = ("route", "gemm1", "gemm2", "combine", "pipeline")
 BWD_STAGES = ("act_grad", "input_grad", "dx_combine", "w2_grad", "w1_grad")
 
@@ -248,11 +249,15 @@ def bwd_workspace_size(problem: Problem, flags: int = 0) -> int:
 
 
 def moe_ffn_bwd(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved, *,
-                ws=None, stage_events: StageEvents | None = None):
+                ws=None, stage_events: StageEvents | None = None, check_saved: bool = False,
+                return_ws: bool = False):
     """Gradients (dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights) of the layer.
 
     `saved` is the context returned by ``moe_ffn_fwd(..., save_for_backward=True)`` for the
     same inputs.  Outputs are freshly allocated and overwritten (never accumulated).
+    ``check_saved`` verifies on the host (synchronously) that `saved` belongs to this
+    problem; otherwise the check runs on the device and a mismatch yields zeros and the
+    DEV_BAD_SAVED status bit (``read_status`` of the workspace, see ``return_ws``).
     """
     lib = load_library()
     _require_gpu(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved)
@@ -268,12 +273,15 @@ def moe_ffn_bwd(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
     if ws is None:
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     ev = ctypes.byref(stage_events) if stage_events is not None else None
+    flags = CHECK_SAVED if check_saved else 0
     with torch.cuda.device(dev):
         rc = lib.moe_ffn_bwd_ex(ctypes.byref(prob), _ptr(dy), _ptr(x), _ptr(topk_ids),
                                 _ptr(topk_weights), _ptr(up_proj_weight), _ptr(down_proj_weight),
                                 _ptr(saved), _ptr(dx), _ptr(d_up), _ptr(d_down), _ptr(d_topk),
-                                _ptr(ws), ws.numel(), 0, _stream(dev), ev)
+                                _ptr(ws), ws.numel(), flags, _stream(dev), ev)
     _check(rc)
+    if return_ws:
+        return dx, d_up, d_down, d_topk, ws
     return dx, d_up, d_down, d_topk
 
 

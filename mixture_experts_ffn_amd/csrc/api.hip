@@ -20,6 +20,7 @@
 
 static_assert(moe::MOE_DEV_BAD_ID == MOE_FFN_DEV_BAD_ID, "status bits");
 static_assert(moe::MOE_DEV_TIMEOUT == MOE_FFN_DEV_TIMEOUT, "status bits");
+static_assert(moe::MOE_DEV_BAD_SAVED == MOE_FFN_DEV_BAD_SAVED, "status bits");
 
 namespace {
 
@@ -155,7 +156,7 @@ struct FwdLayout {
     size_t status, hist, bad, counts, offsets, mtile_off, mtile_expert, sorted_slot, slot_pos;
     size_t ctr, act, o, ws_total;
     // saved
-    size_t s_counts, s_offsets, s_sorted, s_slotpos, s_h, saved_total;
+    size_t s_hdr, s_counts, s_offsets, s_sorted, s_slotpos, s_h, saved_total;
 };
 
 FwdLayout fwd_layout(const moe_ffn_problem &p)
@@ -187,6 +188,7 @@ FwdLayout fwd_layout(const moe_ffn_problem &p)
     L.o = take(es * (size_t)TK * (size_t)p.H);
     L.ws_total = off;
     off = 0;
+    L.s_hdr = take(sizeof(moe::SavedHeader));
     L.s_counts = take(sizeof(int32_t) * (size_t)E);
     L.s_offsets = take(sizeof(int32_t) * (size_t)(E + 1));
     L.s_sorted = take(sizeof(int32_t) * (size_t)TK);
@@ -230,7 +232,7 @@ struct BwdLayout {
     int BM;
     int64_t max_mtiles;
     int dgp_width;
-    size_t mtile_off, mtile_expert, dh, act_g, dgp, dxp, total;
+    size_t status, counts, offsets, mtile_off, mtile_expert, dh, act_g, dgp, dxp, total;
 };
 
 BwdLayout bwd_layout(const moe_ffn_problem &p)
@@ -247,6 +249,9 @@ BwdLayout bwd_layout(const moe_ffn_problem &p)
         off = align_up(off + (bytes ? bytes : 1));
         return at;
     };
+    B.status = take(sizeof(int32_t));
+    B.counts = take(sizeof(int32_t) * (size_t)E);
+    B.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
     B.mtile_off = take(sizeof(int32_t) * (size_t)(E + 1));
     B.mtile_expert = take(sizeof(int32_t) * (size_t)B.max_mtiles);
     B.dh = take(2 * (size_t)TK * (size_t)(2 * p.I));
@@ -255,6 +260,20 @@ BwdLayout bwd_layout(const moe_ffn_problem &p)
     B.dxp = take(2 * (size_t)TK * (size_t)p.H);
     B.total = off;
     return B;
+}
+
+// FNV-1a over the problem's sizes and dtypes: the identity a saved context
+// carries from the forward to the backward
+uint64_t problem_hash(const moe_ffn_problem &p)
+{
+    const int64_t v[7] = {p.T, p.H, p.I, p.E, p.K, p.dtype, p.ids_dtype};
+    uint64_t h = 1469598103934665603ull;
+    for (int64_t x : v)
+        for (int b = 0; b < 8; ++b) {
+            h ^= (uint64_t)((x >> (8 * b)) & 0xff);
+            h *= 1099511628211ull;
+        }
+    return h;
 }
 
 template <typename P> P *at(void *base, size_t off)
@@ -330,6 +349,8 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
     rb.status = at<int32_t>(ws, L.status);
     rb.ctr = at<int32_t>(ws, L.ctr);
     rb.nctr = (int)(2 * L.max_mtiles);
+    rb.saved_hdr = saved ? at<moe::SavedHeader>(saved, L.s_hdr) : nullptr;
+    rb.problem_hash = problem_hash(*p);
     if (saved) {
         rb.counts = at<int32_t>(saved, L.s_counts);
         rb.offsets = at<int32_t>(saved, L.s_offsets);
@@ -529,6 +550,8 @@ int moe_ffn_route(const moe_ffn_problem *p, const void *topk_ids, int32_t *count
     rb.status = at<int32_t>(ws, R.status);
     rb.ctr = nullptr;
     rb.nctr = 0;
+    rb.saved_hdr = nullptr;
+    rb.problem_hash = 0;
     rb.hist = at<int32_t>(ws, R.hist);
     rb.bad = at<int32_t>(ws, R.bad);
     rb.mtile_off = at<int32_t>(ws, R.mtile_off);
@@ -565,7 +588,6 @@ int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, cons
                    void *ws, size_t ws_bytes, uint32_t flags, void *stream,
                    const moe_ffn_stage_events *ev)
 {
-    (void)flags;
     g_err[0] = 0;
     int rc = validate_problem(p);
     if (rc)
@@ -602,8 +624,22 @@ int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, cons
     }
     const int E = (int)p->E, I = (int)p->I, H = (int)p->H;
     void *sv = const_cast<void *>(saved);
-    const int32_t *counts = at<int32_t>(sv, L.s_counts);
-    const int32_t *offsets = at<int32_t>(sv, L.s_offsets);
+    const moe::SavedHeader *hdr = at<moe::SavedHeader>(sv, L.s_hdr);
+    const uint64_t phash = problem_hash(*p);
+    if (flags & MOE_FFN_CHECK_SAVED) {
+        moe::SavedHeader h_host{};
+        HIP_TRY(hipMemcpyAsync(&h_host, hdr, sizeof h_host, hipMemcpyDeviceToHost, s),
+                "saved header copy");
+        HIP_TRY(hipStreamSynchronize(s), "stream sync");
+        if (h_host.magic != moe::kSavedMagic || h_host.version != moe::kSavedVersion ||
+            h_host.problem != phash)
+            return fail(MOE_FFN_ERR_SAVED, "saved context was not written by a forward of this problem");
+    }
+    const int32_t *saved_counts = at<int32_t>(sv, L.s_counts);
+    const int32_t *saved_offsets = at<int32_t>(sv, L.s_offsets);
+    int32_t *counts = at<int32_t>(ws, B.counts);
+    int32_t *offsets = at<int32_t>(ws, B.offsets);
+    int32_t *bstatus = at<int32_t>(ws, B.status);
     const int32_t *sorted_slot = at<int32_t>(sv, L.s_sorted);
     const int32_t *slot_pos = at<int32_t>(sv, L.s_slotpos);
     const moe::bf16_t *h = at<moe::bf16_t>(sv, L.s_h);
@@ -614,7 +650,10 @@ int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, cons
     float *dgp = at<float>(ws, B.dgp);
     moe::bf16_t *dxp = at<moe::bf16_t>(ws, B.dxp);
 
-    HIP_TRY(moe::launch_build_mtiles(counts, E, B.BM, mtile_off, mtile_expert, s), "mtiles");
+    HIP_TRY(moe::launch_bwd_setup(hdr, phash, saved_counts, saved_offsets, E, p->T * p->K, B.BM,
+                                  counts, offsets, mtile_off, mtile_expert, bstatus, s),
+            "backward set-up launch");
+    (void)counts;
 
     moe::EngineArgs base{};
     base.sorted_slot = sorted_slot;
@@ -659,8 +698,8 @@ int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, cons
     record(ev, MOE_FFN_STAGE_BWD_INPUT_GRAD, false, s);
 
     record(ev, MOE_FFN_STAGE_BWD_COMBINE, true, s);
-    HIP_TRY(moe::launch_combine_bwd(dxp, dgp, B.dgp_width, slot_pos, dx, d_topk_weights, p->T, H,
-                                    (int)p->K, s),
+    HIP_TRY(moe::launch_combine_bwd(dxp, dgp, B.dgp_width, slot_pos, bstatus, dx, d_topk_weights,
+                                    p->T, H, (int)p->K, s),
             "dx combine launch");
     record(ev, MOE_FFN_STAGE_BWD_COMBINE, false, s);
 

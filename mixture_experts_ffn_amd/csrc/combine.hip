@@ -53,16 +53,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ o,
 // Backward combine (issue page, section 2.2 "Combine(dX)"): one workgroup per
 // token sums its K rows of dx_perm in k order (no gate: it is already inside
 // dh) and finishes d_topk_weights[t, k] by summing that row's partial dots in a
-// fixed order.  Deterministic; a dropped slot (slot_pos = -1) gives 0.
+// fixed order.  Deterministic; a dropped slot (slot_pos = -1) gives 0, and a
+// saved context that failed the backward set-up's check gives all zeros
+// (slot_pos is then not read).
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16 *__restrict__ dxp,
                                                           const float *__restrict__ dgp,
                                                           int dgp_stride,
                                                           const int32_t *__restrict__ slot_pos,
+                                                          const int32_t *__restrict__ status,
                                                           bf16 *__restrict__ dx,
                                                           float *__restrict__ d_topk, int H, int K)
 {
     const int64_t t = blockIdx.x;
     const int nch = H / 8;
+    if (status[0] & MOE_DEV_BAD_SAVED) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int c = threadIdx.x; c < nch; c += 256)
+            *reinterpret_cast<u32x4 *>(dx + t * H + (int64_t)c * 8) = z;
+        if (threadIdx.x < K)
+            d_topk[t * K + threadIdx.x] = 0.f;
+        return;
+    }
     for (int c = threadIdx.x; c < nch; c += 256) {
         float acc[8];
 #pragma unroll
@@ -98,13 +109,13 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16 *__restrict
 }
 
 hipError_t launch_combine_bwd(const void *dxp, const float *dgp, int dgp_stride,
-                              const int32_t *slot_pos, void *dx, float *d_topk, int64_t T, int H,
-                              int K, hipStream_t stream)
+                              const int32_t *slot_pos, const int32_t *status, void *dx,
+                              float *d_topk, int64_t T, int H, int K, hipStream_t stream)
 {
     if (T <= 0)
         return hipSuccess;
     hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)T), dim3(256), 0, stream,
-                       static_cast<const bf16 *>(dxp), dgp, dgp_stride, slot_pos,
+                       static_cast<const bf16 *>(dxp), dgp, dgp_stride, slot_pos, status,
                        static_cast<bf16 *>(dx), d_topk, H, K);
     return hipGetLastError();
 }

@@ -57,22 +57,23 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-constexpr int NW = 8;           // waves per workgroup
 constexpr int PW = 128;         // weight columns per panel (two panels per tile)
 constexpr int TILE_N1 = PW;     // GEMM1 output columns per tile
 constexpr int TILE_N2 = 2 * PW; // GEMM2 output columns per tile
 
 enum { KIND_G1 = 1, KIND_G2 = 2 };
+constexpr int kWaves = 8; // waves per workgroup
 
 // Block tile BM x (2 x 128): BM = 64 or 128 with BK = 64, a 3-stage ring and
 // all 8 waves side by side along N; BM = 256 with BK = 32, a 4-stage ring and
 // the waves as 2 (M) x 4 (N), so each wave owns 128 rows x 32 columns per
 // panel and needs a third fewer LDS reads and copied bytes per flop.
-template <int BM_> struct Cfg {
+template <int BM_, int NW_ = 8> struct Cfg {
     static constexpr int BM = BM_;
+    static constexpr int NW = NW_;                   // waves per workgroup
     static constexpr int BK = BM == 256 ? 32 : 64;   // K per step
     static constexpr int NSTAGE = BM == 256 ? 4 : 3; // LDS ring depth
-    static constexpr int WM = BM == 256 ? 2 : 1;     // waves along M
+    static constexpr int WM = BM == 256 && NW == 8 ? 2 : 1; // waves along M
     static constexpr int WN = NW / WM;               // waves along N
     static constexpr int WTM = BM / WM;              // rows per wave
     static constexpr int WTN = PW / WN;              // columns per wave per panel
@@ -261,10 +262,11 @@ struct Cursor {
     int kind, L, hi;
 };
 
-template <int BM, int MODE>
-__global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16(FastFwdArgs args)
+template <int BM, int MODE, int NWAVES>
+__global__ __launch_bounds__(64 * NWAVES, 1) void moe_fwd_bf16(FastFwdArgs args)
 {
-    using C = Cfg<BM>;
+    using C = Cfg<BM, NWAVES>;
+    constexpr int NW = C::NW;
     constexpr int BK = C::BK, NSTAGE = C::NSTAGE;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * C::STAGE_BYTES];
 
@@ -687,12 +689,12 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16(FastFwdArgs args)
     }
 }
 
-template <int BM, int MODE>
+template <int BM, int MODE, int NWAVES = kWaves>
 static hipError_t launch(const FastFwdArgs &a, int num_cus, hipStream_t stream)
 {
     const int grid = (num_cus + 7) / 8 * 8; // one workgroup per CU, whole XCDs
-    hipLaunchKernelGGL((moe_fwd_bf16<BM, MODE>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
-                       a);
+    hipLaunchKernelGGL((moe_fwd_bf16<BM, MODE, NWAVES>), dim3((unsigned)grid), dim3(64 * NWAVES),
+                       0, stream, a);
     return hipGetLastError();
 }
 

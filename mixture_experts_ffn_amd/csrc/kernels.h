@@ -9,6 +9,16 @@ namespace moe {
 typedef __bf16 bf16_t;
 
 // ---- routing -----------------------------------------------------------------
+// Header at the front of the saved context: the forward's routing step writes
+// it, the backward checks it before it trusts any of the saved arrays.
+struct SavedHeader {
+    uint32_t magic;
+    uint32_t version;
+    uint64_t problem; // hash of (T, H, I, E, K, dtype, ids_dtype)
+};
+constexpr uint32_t kSavedMagic = 0x46454f4du; // "MOEF"
+constexpr uint32_t kSavedVersion = 1u;
+
 struct RoutePlan {
     int RC;    // slots per chunk (one wave per chunk)
     int NB;    // number of chunks
@@ -27,10 +37,13 @@ struct RouteBufs {
     int32_t *slot_pos;    // [TK]
     int32_t *ctr;         // optional: release counters of the pipelined forward, zeroed here
     int nctr;             // their number
+    SavedHeader *saved_hdr; // optional: header of the saved context, written here
+    uint64_t problem_hash;
 };
 
 // bits of the device status word
-enum { MOE_DEV_BAD_ID = 1, MOE_DEV_TIMEOUT = 2 };
+enum { MOE_DEV_BAD_ID = 1, MOE_DEV_TIMEOUT = 2, MOE_DEV_BAD_SAVED = 4 };
+
 
 RoutePlan make_route_plan(int64_t TK, int E);
 hipError_t launch_route(const void *ids, bool ids64, int64_t TK, int E, int BM,
@@ -131,13 +144,19 @@ hipError_t launch_combine(int dtype, const void *o, const int32_t *slot_pos, con
                           void *y, int64_t T, int H, int K, hipStream_t stream);
 // backward combine: dx[t] = Σ_k dxp[slot_pos[tK+k]] and
 // d_topk[t, k] = Σ_j dgp[slot_pos[tK+k], j] (0 for a dropped slot)
+// (all zeros when *status has MOE_DEV_BAD_SAVED)
 hipError_t launch_combine_bwd(const void *dxp, const float *dgp, int dgp_stride,
-                              const int32_t *slot_pos, void *dx, float *d_topk, int64_t T, int H,
-                              int K, hipStream_t stream);
+                              const int32_t *slot_pos, const int32_t *status, void *dx,
+                              float *d_topk, int64_t T, int H, int K, hipStream_t stream);
 // zero `bytes` (a multiple of 16) at a 16-byte aligned pointer
 hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t stream);
-// M-tile tables from per-expert counts (one block)
-hipError_t launch_build_mtiles(const int32_t *counts, int E, int BM, int32_t *mtile_off,
-                               int32_t *mtile_expert, hipStream_t stream);
+// Backward set-up (one block): checks the saved context's header and the
+// consistency of its counts/offsets; copies them into the workspace (all zero,
+// and MOE_DEV_BAD_SAVED in *status, if the check fails) and builds the M-tile
+// tables from the copies.
+hipError_t launch_bwd_setup(const SavedHeader *hdr, uint64_t problem_hash, const int32_t *counts,
+                            const int32_t *offsets, int E, int64_t TK, int BM, int32_t *counts_out,
+                            int32_t *offsets_out, int32_t *mtile_off, int32_t *mtile_expert,
+                            int32_t *status, hipStream_t stream);
 
 } // namespace moe

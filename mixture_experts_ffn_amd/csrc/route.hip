@@ -99,8 +99,15 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ 
                                                           int32_t *__restrict__ mtile_off,
                                                           int32_t *__restrict__ mtile_expert,
                                                           int32_t *__restrict__ status,
-                                                          int32_t *__restrict__ ctr, int nctr)
+                                                          int32_t *__restrict__ ctr, int nctr,
+                                                          SavedHeader *__restrict__ hdr,
+                                                          uint64_t problem_hash)
 {
+    if (hdr && threadIdx.x == 0) {
+        hdr->magic = kSavedMagic;
+        hdr->version = kSavedVersion;
+        hdr->problem = problem_hash;
+    }
     for (int j = threadIdx.x; j < nctr; j += 1024)
         ctr[j] = 0;
     __shared__ int32_t s_cnt[1024];
@@ -206,18 +213,51 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(
     }
 }
 
-// M-tile tables (prefix of ceil(counts[e] / BM) and the owner of every M-tile)
-// from per-expert counts, for a launch whose tile height differs from, or
-// comes after, the routing step.  One 1024-thread block; E <= 1024.
-__global__ __launch_bounds__(1024) void build_mtiles_kernel(const int32_t *__restrict__ counts,
-                                                            int E, int BM,
-                                                            int32_t *__restrict__ mtile_off,
-                                                            int32_t *__restrict__ mtile_expert)
+// Backward set-up.  The saved context is trusted only if its header names
+// this problem and its offsets are a consistent prefix sum of its counts
+// within [0, TK]; then counts and offsets are copied into the workspace and
+// the M-tile tables (prefix of ceil(counts[e] / BM) and the owner of every
+// M-tile) are built from the copies.  Otherwise the copies are all zero (no
+// kernel after this one reads a saved array beyond them) and the status word
+// says so.  One 1024-thread block; E <= 1024.
+__global__ __launch_bounds__(1024) void bwd_setup_kernel(
+    const SavedHeader *__restrict__ hdr, uint64_t problem_hash, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ offsets, int E, int64_t TK, int BM,
+    int32_t *__restrict__ counts_out, int32_t *__restrict__ offsets_out,
+    int32_t *__restrict__ mtile_off, int32_t *__restrict__ mtile_expert,
+    int32_t *__restrict__ status)
 {
     __shared__ int32_t s_moff[1025];
     __shared__ int32_t s_w[40];
+    __shared__ int s_hdr_ok;
+    if (threadIdx.x == 0)
+        s_hdr_ok = hdr->magic == kSavedMagic && hdr->version == kSavedVersion &&
+                   hdr->problem == problem_hash;
+    __syncthreads();
     const int e = threadIdx.x;
-    const int32_t mt = e < E ? (counts[e] + BM - 1) / BM : 0;
+    int32_t c = 0, off = 0;
+    int bad = 0;
+    if (s_hdr_ok && e < E) {
+        c = counts[e];
+        off = offsets[e];
+        const int32_t next = offsets[e + 1];
+        bad = c < 0 || off < 0 || next - off != c || (int64_t)next > TK || (e == 0 && off != 0);
+    }
+    bad = __syncthreads_or(bad);
+    const bool ok = s_hdr_ok && !bad;
+    if (!ok) {
+        c = 0;
+        off = 0;
+    }
+    if (e < E) {
+        counts_out[e] = c;
+        offsets_out[e] = off;
+    }
+    if (e == 0) {
+        offsets_out[E] = ok ? offsets[E] : 0;
+        status[0] = ok ? 0 : MOE_DEV_BAD_SAVED;
+    }
+    const int32_t mt = e < E ? (c + BM - 1) / BM : 0;
     int32_t mtotal;
     const int32_t moff = block_excl_scan(mt, s_w, &mtotal);
     if (e < E) {
@@ -242,11 +282,13 @@ __global__ __launch_bounds__(1024) void build_mtiles_kernel(const int32_t *__res
     }
 }
 
-hipError_t launch_build_mtiles(const int32_t *counts, int E, int BM, int32_t *mtile_off,
-                               int32_t *mtile_expert, hipStream_t stream)
+hipError_t launch_bwd_setup(const SavedHeader *hdr, uint64_t problem_hash, const int32_t *counts,
+                            const int32_t *offsets, int E, int64_t TK, int BM, int32_t *counts_out,
+                            int32_t *offsets_out, int32_t *mtile_off, int32_t *mtile_expert,
+                            int32_t *status, hipStream_t stream)
 {
-    hipLaunchKernelGGL(build_mtiles_kernel, dim3(1), dim3(1024), 0, stream, counts, E, BM,
-                       mtile_off, mtile_expert);
+    hipLaunchKernelGGL(bwd_setup_kernel, dim3(1), dim3(1024), 0, stream, hdr, problem_hash, counts,
+                       offsets, E, TK, BM, counts_out, offsets_out, mtile_off, mtile_expert, status);
     return hipGetLastError();
 }
 
@@ -282,7 +324,7 @@ hipError_t launch_route(const void *ids, bool ids64, int64_t TK, int E, int BM,
     const int nb_scan = TK > 0 ? rp.NB : 0;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, rb.hist, rb.bad, E,
                        nb_scan, BM, rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert,
-                       rb.status, rb.ctr, rb.ctr ? rb.nctr : 0);
+                       rb.status, rb.ctr, rb.ctr ? rb.nctr : 0, rb.saved_hdr, rb.problem_hash);
     if (TK > 0) {
         if (ids64)
             hipLaunchKernelGGL(route_scatter_kernel<int64_t>, dim3(rp.NB), dim3(64), lds, stream,

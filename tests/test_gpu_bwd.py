@@ -136,3 +136,34 @@ def test_bwd_rejects_fp32(gpu_lib):
         gpu_lib.moe_ffn_bwd(d["dy"], d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
                             d["down_proj"], saved)
     assert ei.value.status == 3
+
+
+def test_bwd_checks_the_saved_context(gpu_lib):
+    # a saved context written by the forward of another problem (T = 200) but
+    # big enough for this one (T = 300)
+    wa = Workload("bsa", 324, T=200, H=256, I=128, E=8, K=2)
+    wb = Workload("bsb", 325, T=300, H=256, I=128, E=8, K=2)
+    da, db = to_device(make_inputs(wa, with_dy=True)), to_device(make_inputs(wb, with_dy=True))
+    say("[bwd] foreign saved context")
+    _, saved_b = gpu_lib.moe_ffn_fwd(db["x"], db["topk_ids"], db["topk_weights"], db["up_proj"],
+                                     db["down_proj"], save_for_backward=True)
+    _, saved_a = gpu_lib.moe_ffn_fwd(da["x"], da["topk_ids"], da["topk_weights"], da["up_proj"],
+                                     da["down_proj"], save_for_backward=True)
+    foreign = torch.zeros_like(saved_b)
+    foreign[:saved_a.numel()] = saved_a
+    torch.cuda.synchronize()
+    args = (db["dy"], db["x"], db["topk_ids"], db["topk_weights"], db["up_proj"], db["down_proj"])
+    with pytest.raises(gpu_lib.MoEFFNError) as ei:
+        gpu_lib.moe_ffn_bwd(*args, foreign, check_saved=True)
+    assert ei.value.status == 7
+    # without the host check: nothing faults, all outputs are zero, the status says why
+    *grads, ws = gpu_lib.moe_ffn_bwd(*args, foreign, return_ws=True)
+    torch.cuda.synchronize()
+    assert gpu_lib.read_status(ws) == gpu_lib.DEV_BAD_SAVED
+    for g in grads:
+        assert not g.float().abs().sum().item()
+    # the matching context passes both checks and the status is clean
+    *grads, ws = gpu_lib.moe_ffn_bwd(*args, saved_b, check_saved=True, return_ws=True)
+    torch.cuda.synchronize()
+    assert gpu_lib.read_status(ws) == 0
+    assert grads[1].float().abs().sum().item() > 0
