@@ -5,9 +5,12 @@ One step = one full forward of the layer (route -> gathered up_proj GEMM with
 SwiGLU -> down_proj GEMM -> combine) on a seeded synthetic batch that is
 already resident in HBM; for the forward+backward workload also the backward.
 The forward runs as the library does by default (route, GEMM1, GEMM2 and
-combine as separate launches); its pipelined twin (the two grouped GEMMs and
-the combine in one launch with tile-granular release) is timed after it and
-reported as "pipelined_twin".  Prints ONE JSON line.
+combine as separate launches).  The step is timed eagerly (with per-stage HIP
+events) and as a HIP graph replay of the same calls (every kernel runs every
+step; only the host-side launch work is gone); the headline is the replay when
+its output equals the eager output bit for bit.  The pipelined twin (the two
+grouped GEMMs and the combine in one launch with tile-granular release) is
+timed after it and reported as "pipelined_twin".  Prints ONE JSON line.
 
 Default workload: prefill, bf16 with fp32 accumulation, T=4096 tokens,
 H=2048, I=1408, E=64 experts, K=6, uniform routing.  Other workloads:
@@ -129,12 +132,40 @@ def main():
 
     # the library's default forward (the bulk launches) is the measured one; the
     # pipelined twin (one launch, tile-granular release) runs after it
+    def graphed():
+        """The default step captured once into a HIP graph and replayed: the same
+        kernels every step, without per-launch host work.  Returns the replayed
+        output (checked against the eager step) and the time of the replays."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            yg = step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        return yg, time.perf_counter() - t0
+
     y, elapsed, stage_ms = timed(pipelined=False)
     _, pipe_elapsed, pipe_stage_ms = timed(pipelined=True)
+    y_graph, graph_elapsed = graphed()
+    graph_ok = bool(torch.equal(y_graph, y))
     pipelined = "pipeline" in stage_ms
 
-    ms_per_step = elapsed / args.steps * 1e3
-    tokens_per_s = w.T * args.steps / elapsed
+    eager_ms = elapsed / args.steps * 1e3
+    # the headline: graph replay of the default step when it reproduces the
+    # eager output bit for bit, else the eager step
+    step_s = graph_elapsed if graph_ok else elapsed
+    ms_per_step = step_s / args.steps * 1e3
+    tokens_per_s = w.T * args.steps / step_s
     counts = np.bincount(inp["topk_ids"].ravel(), minlength=w.E)
     live = counts > 0
     es = 2 if w.dtype == "bf16" else 4
@@ -189,6 +220,11 @@ def main():
                   (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS),
                   "hbm_gbs_alg": layer_bytes / (ms_per_step * 1e-3) / 1e9,
                   "stage_ms": stage_ms},
+        "launch": "hip_graph_replay" if graph_ok else "eager",
+        "eager": {"ms_per_step": eager_ms, "tokens_per_s": w.T * args.steps / elapsed},
+        "graph_replay": {"ms_per_step": graph_elapsed / args.steps * 1e3,
+                         "tokens_per_s": w.T * args.steps / graph_elapsed,
+                         "output_equals_eager": graph_ok},
         "pipelined_twin": {"ms_per_step": pipe_elapsed / args.steps * 1e3,
                            "tokens_per_s": w.T * args.steps / pipe_elapsed,
                            "stage_ms": pipe_stage_ms},
