@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="steps timed one by one after evicting the caches (512 MiB written "
+                         "between steps, outside the timed region); 0 to skip")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one elementwise copy of this many MiB (for scaling HBM "
                          "byte counters against a kernel of known traffic)")
@@ -103,19 +106,29 @@ def main():
                       d["down_proj"], saved, ws=bws, stage_events=bev)
         return y
 
+    def stats(ms):
+        ms = np.asarray(ms, np.float64)
+        return {"median": float(np.median(ms)), "min": float(ms.min()),
+                "p90": float(np.percentile(ms, 90)), "n": int(ms.size)}
+
     def timed(pipelined):
-        """warmup, then the timed steps; per-stage mean ms from the library's events"""
+        """warmup, then the timed steps; per-stage mean ms from the library's events
+        and per-step times from events around each step (same stream)"""
         for _ in range(args.warmup):
             step(pipelined=pipelined)
         torch.cuda.synchronize()
         pool = m.EventPool(args.steps)
         bpool = m.EventPool(args.steps, n_stages=len(m.BWD_STAGES)) if w.backward else None
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        marks[0].record()
         for i in range(args.steps):
             y = step(pool.sets[i], bpool.sets[i] if bpool else None, pipelined=pipelined)
+            marks[i + 1].record()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
+        per_step = stats([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
         stages = {}
         for s, name in enumerate(m.STAGES):
             try:  # stages a path does not run are never recorded
@@ -128,7 +141,33 @@ def main():
                                                          for i in range(args.steps)]))
                            for s, name in enumerate(m.BWD_STAGES)})
             bpool.close()
-        return y, elapsed, stages
+        return y, elapsed, stages, per_step
+
+    def cold(n):
+        """steps timed one by one, each after writing 512 MiB (more than the 256 MB
+        last-level cache) outside the timed region"""
+        scratch = torch.empty(512 * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        ms = []
+        for _ in range(n):
+            scratch.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            step()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        del scratch
+        return stats(ms)
+
+    # the first call of the process (code-object load, first-touch of the
+    # workspace), timed on its own
+    fa, fb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    fa.record()
+    step()
+    fb.record()
+    torch.cuda.synchronize()
+    first_call_ms = fa.elapsed_time(fb)
 
     # the library's default forward (the bulk launches) is the measured one; the
     # pipelined twin (one launch, tile-granular release) runs after it
@@ -154,8 +193,9 @@ def main():
         torch.cuda.synchronize()
         return yg, time.perf_counter() - t0
 
-    y, elapsed, stage_ms = timed(pipelined=False)
-    _, pipe_elapsed, pipe_stage_ms = timed(pipelined=True)
+    y, elapsed, stage_ms, step_stats = timed(pipelined=False)
+    _, pipe_elapsed, pipe_stage_ms, _ = timed(pipelined=True)
+    cold_stats = cold(args.cold_steps) if args.cold_steps > 0 else None
     y_graph, graph_elapsed = graphed()
     graph_ok = bool(torch.equal(y_graph, y))
     pipelined = "pipeline" in stage_ms
@@ -221,7 +261,9 @@ def main():
                   "hbm_gbs_alg": layer_bytes / (ms_per_step * 1e-3) / 1e9,
                   "stage_ms": stage_ms},
         "launch": "hip_graph_replay" if graph_ok else "eager",
-        "eager": {"ms_per_step": eager_ms, "tokens_per_s": w.T * args.steps / elapsed},
+        "eager": {"ms_per_step": eager_ms, "tokens_per_s": w.T * args.steps / elapsed,
+                  "step_ms": step_stats, "first_call_ms": first_call_ms,
+                  "cold_step_ms": cold_stats},
         "graph_replay": {"ms_per_step": graph_elapsed / args.steps * 1e3,
                          "tokens_per_s": w.T * args.steps / graph_elapsed,
                          "output_equals_eager": graph_ok},
@@ -334,7 +376,16 @@ def cpu_baseline(w, inp, y_gpu, target_s):
     yo, dt = run(n)
     got = y_gpu[:n].float().cpu().numpy().astype(np.float64)
     err = float(np.abs(got - yo).max() / max(np.abs(yo).max(), 1e-300))
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": n / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "cpu_model": model,
             "sample": f"first {n} of {w.T} tokens of the same batch (all {w.E} experts' weights), "
                       f"{dt:.1f} s, fp64 accumulation",
             "max_rel_err_gpu_vs_oracle_on_sample": err}
