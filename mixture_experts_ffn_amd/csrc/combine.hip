@@ -16,6 +16,9 @@
 
 namespace moe {
 
+// Grid: (token, block of 256 16-byte chunks).  Each thread owns one chunk of
+// one token's output row; its K source rows are loaded 8 at a time before
+// they are accumulated in k order, so their latencies overlap.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ o,
                                                       const int32_t *__restrict__ slot_pos,
@@ -25,29 +28,39 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ o,
     constexpr int VEC = 16 / (int)sizeof(T);
     const int64_t t = blockIdx.x;
     const int nch = H / VEC;
-    for (int c = threadIdx.x; c < nch; c += 256) {
-        float acc[VEC];
+    const int c = blockIdx.y * 256 + threadIdx.x;
+    if (c >= nch)
+        return;
+    float acc[VEC];
 #pragma unroll
-        for (int j = 0; j < VEC; ++j)
-            acc[j] = 0.f;
-        for (int k = 0; k < K; ++k) {
-            const int32_t p = slot_pos[t * K + k];
-            if (p < 0)
+    for (int j = 0; j < VEC; ++j)
+        acc[j] = 0.f;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+        int32_t pk[8];
+        u32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            pk[i] = k0 + i < K ? slot_pos[t * K + k0 + i] : -1;
+            const int64_t row = pk[i] > 0 ? pk[i] : 0;
+            v[i] = *reinterpret_cast<const u32x4 *>(o + row * H + (int64_t)c * VEC);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (pk[i] < 0)
                 continue;
-            const float g = gates[t * K + k];
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(o + (int64_t)p * H + (int64_t)c * VEC);
-            const T *vv = reinterpret_cast<const T *>(&v);
+            const float g = gates[t * K + k0 + i];
+            const T *vv = reinterpret_cast<const T *>(&v[i]);
 #pragma unroll
             for (int j = 0; j < VEC; ++j)
                 acc[j] += g * to_f32<T>(vv[j]);
         }
-        u32x4 out;
-        T *oo = reinterpret_cast<T *>(&out);
-#pragma unroll
-        for (int j = 0; j < VEC; ++j)
-            oo[j] = from_f32<T>(acc[j]);
-        *reinterpret_cast<u32x4 *>(y + t * H + (int64_t)c * VEC) = out;
     }
+    u32x4 out;
+    T *oo = reinterpret_cast<T *>(&out);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+        oo[j] = from_f32<T>(acc[j]);
+    *reinterpret_cast<u32x4 *>(y + t * H + (int64_t)c * VEC) = out;
 }
 
 // Backward combine (issue page, section 2.2 "Combine(dX)"): one workgroup per
@@ -143,12 +156,14 @@ hipError_t launch_combine(int dtype, const void *o, const int32_t *slot_pos, con
 {
     if (T <= 0)
         return hipSuccess;
+    const int vec = dtype == 1 ? 8 : 4;
+    const unsigned cblocks = (unsigned)((H / vec + 255) / 256);
     if (dtype == 1)
-        hipLaunchKernelGGL(combine_kernel<bf16>, dim3((unsigned)T), dim3(256), 0, stream,
+        hipLaunchKernelGGL(combine_kernel<bf16>, dim3((unsigned)T, cblocks), dim3(256), 0, stream,
                            static_cast<const bf16 *>(o), slot_pos, gates, static_cast<bf16 *>(y), H,
                            K);
     else
-        hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)T), dim3(256), 0, stream,
+        hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)T, cblocks), dim3(256), 0, stream,
                            static_cast<const float *>(o), slot_pos, gates, static_cast<float *>(y),
                            H, K);
     return hipGetLastError();
