@@ -77,30 +77,37 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16 *__restrict
                                                           bf16 *__restrict__ dx,
                                                           float *__restrict__ d_topk, int H, int K)
 {
+    // grid: (token, block of 256 16-byte chunks); the first chunk block of a
+    // token also finishes its d_topk_weights
     const int64_t t = blockIdx.x;
     const int nch = H / 8;
-    if (status[0] & MOE_DEV_BAD_SAVED) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        for (int c = threadIdx.x; c < nch; c += 256)
-            *reinterpret_cast<u32x4 *>(dx + t * H + (int64_t)c * 8) = z;
-        if (threadIdx.x < K)
-            d_topk[t * K + threadIdx.x] = 0.f;
-        return;
-    }
-    for (int c = threadIdx.x; c < nch; c += 256) {
+    const int c = blockIdx.y * 256 + threadIdx.x;
+    const bool bad = status[0] & MOE_DEV_BAD_SAVED;
+    if (c < nch) {
         float acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             acc[j] = 0.f;
-        for (int k = 0; k < K; ++k) {
-            const int32_t p = slot_pos[t * K + k];
-            if (p < 0)
-                continue;
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(dxp + (int64_t)p * H + (int64_t)c * 8);
-            const bf16 *vv = reinterpret_cast<const bf16 *>(&v);
+        if (!bad) {
+            for (int k0 = 0; k0 < K; k0 += 8) {
+                int32_t pk[8];
+                u32x4 v[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                acc[j] += static_cast<float>(vv[j]);
+                for (int i = 0; i < 8; ++i) {
+                    pk[i] = k0 + i < K ? slot_pos[t * K + k0 + i] : -1;
+                    const int64_t row = pk[i] > 0 ? pk[i] : 0;
+                    v[i] = *reinterpret_cast<const u32x4 *>(dxp + row * H + (int64_t)c * 8);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    if (pk[i] < 0)
+                        continue;
+                    const bf16 *vv = reinterpret_cast<const bf16 *>(&v[i]);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        acc[j] += static_cast<float>(vv[j]);
+                }
+            }
         }
         u32x4 out;
         bf16 *oo = reinterpret_cast<bf16 *>(&out);
@@ -109,14 +116,16 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16 *__restrict
             oo[j] = static_cast<bf16>(acc[j]);
         *reinterpret_cast<u32x4 *>(dx + t * H + (int64_t)c * 8) = out;
     }
-    // d_topk: wave 0, one lane per k
-    if (threadIdx.x < K) {
+    // d_topk: one lane per k
+    if (blockIdx.y == 0 && threadIdx.x < K) {
         const int k = threadIdx.x;
-        const int32_t p = slot_pos[t * K + k];
         float d = 0.f;
-        if (p >= 0)
-            for (int j = 0; j < dgp_stride; ++j)
-                d += dgp[(int64_t)p * dgp_stride + j];
+        if (!bad) {
+            const int32_t p = slot_pos[t * K + k];
+            if (p >= 0)
+                for (int j = 0; j < dgp_stride; ++j)
+                    d += dgp[(int64_t)p * dgp_stride + j];
+        }
         d_topk[t * K + k] = d;
     }
 }
@@ -127,7 +136,8 @@ hipError_t launch_combine_bwd(const void *dxp, const float *dgp, int dgp_stride,
 {
     if (T <= 0)
         return hipSuccess;
-    hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)T), dim3(256), 0, stream,
+    const unsigned cblocks = (unsigned)((H / 8 + 255) / 256);
+    hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)T, cblocks), dim3(256), 0, stream,
                        static_cast<const bf16 *>(dxp), dgp, dgp_stride, slot_pos, status,
                        static_cast<bf16 *>(dx), d_topk, H, K);
     return hipGetLastError();
