@@ -629,38 +629,64 @@ __global__ __launch_bounds__(64 * NW, 1) void engine_kernel(EngineArgs a)
             const unsigned char *sA = smem + cstage * C::STAGE_BYTES;
             const unsigned char *sB = sA + C::A_BYTES;
             cstage = cstage == NSTAGE - 1 ? 0 : cstage + 1;
+            // all fragments of the K step first, then the MFMAs; the LDS pipe
+            // and the matrix cores are close to balanced, so the interleave is
+            // pinned: the first MFMA group's operands, then one read per MFMA
+            constexpr int KH = BK / 32;
+            bf16x8 af[KH][C::FM];
+            bf16x8 bf[KH][C::NPANEL][C::FN];
 #pragma unroll
-            for (int kk = 0; kk < BK; kk += 32) {
-                bf16x8 af[C::FM];
+            for (int h2 = 0; h2 < KH; ++h2) {
+                const int kk = h2 * 32;
 #pragma unroll
                 for (int fm = 0; fm < C::FM; ++fm) {
                     if constexpr (KT::ALAY == KROW)
-                        af[fm] = frag_krow(sA, wm * C::WTM + fm * 16 + (lane & 15),
-                                           (kk >> 3) + (lane >> 4));
+                        af[h2][fm] = frag_krow(sA, wm * C::WTM + fm * 16 + (lane & 15),
+                                               (kk >> 3) + (lane >> 4));
                     else
-                        af[fm] = frag_kcol<BM * 2>(sA, wm * C::WTM + fm * 16, kk + 8 * (lane >> 4),
-                                                   lane);
+                        af[h2][fm] = frag_kcol<BM * 2>(sA, wm * C::WTM + fm * 16,
+                                                       kk + 8 * (lane >> 4), lane);
                 }
 #pragma unroll
                 for (int p = 0; p < C::NPANEL; ++p) {
 #pragma unroll
                     for (int fn = 0; fn < C::FN; ++fn) {
                         const int nb = p * C::PW + wn * C::WTN + fn * 16;
-                        bf16x8 bfrag;
                         if constexpr (KT::BLAY == KROW)
-                            bfrag = frag_krow(sB, nb + (lane & 15), (kk >> 3) + (lane >> 4));
+                            bf[h2][p][fn] = frag_krow(sB, nb + (lane & 15), (kk >> 3) + (lane >> 4));
                         else if constexpr (KT::PAIRED)
-                            bfrag = frag_kcol<C::PW * 2>(sB + p * (BK * C::PW * 2),
-                                                         wn * C::WTN + fn * 16, kk + 8 * (lane >> 4),
-                                                         lane);
+                            bf[h2][p][fn] = frag_kcol<C::PW * 2>(sB + p * (BK * C::PW * 2),
+                                                                 wn * C::WTN + fn * 16,
+                                                                 kk + 8 * (lane >> 4), lane);
                         else
-                            bfrag = frag_kcol<C::PW * 2>(sB, nb, kk + 8 * (lane >> 4), lane);
+                            bf[h2][p][fn] = frag_kcol<C::PW * 2>(sB, nb, kk + 8 * (lane >> 4), lane);
+                    }
+                }
+            }
+#pragma unroll
+            for (int h2 = 0; h2 < KH; ++h2)
+#pragma unroll
+                for (int p = 0; p < C::NPANEL; ++p)
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
                         for (int fm = 0; fm < C::FM; ++fm)
                             acc[p][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                bfrag, af[fm], acc[p][fm][fn], 0, 0, 0);
-                    }
+                                bf[h2][p][fn], af[h2][fm], acc[p][fm][fn], 0, 0, 0);
+            {
+                constexpr int RA = KT::ALAY == KROW ? 1 : 2, RB = KT::BLAY == KROW ? 1 : 2;
+                constexpr int NDS = KH * (C::FM * RA + C::NPANEL * C::FN * RB);
+                constexpr int NMF = KH * C::NPANEL * C::FN * C::FM;
+                constexpr int FIRST = C::FM * RA + RB;
+                constexpr int PAIRS = NDS - FIRST < NMF ? NDS - FIRST : NMF;
+                __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
+#pragma unroll
+                for (int i = 0; i < PAIRS; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
+                __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, NDS - FIRST - PAIRS, 0);
             }
         }
         epilogue<KIND, BM, WM>(a, t, acc, wm, wn, lane);
