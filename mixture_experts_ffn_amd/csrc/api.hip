@@ -92,7 +92,7 @@ int check_ptr(const void *ptr, const char *name, size_t align = 16)
 }
 
 // The current device must be a gfx950 GPU.  Cached per device ordinal, with
-// its compute-unit count (the persistent kernels launch one workgroup per CU).
+// its compute-unit count (the persistent kernels size their grids by it).
 int g_num_cus[64] = {0};
 int g_clock_khz[64] = {0}; // rate of the device's constant wall clock (s_memrealtime)
 
@@ -142,7 +142,9 @@ moe::FwdTiles pick_tiles(const moe_ffn_problem &p)
     } else {
         const double avg_rows = (double)(p.T * p.K) / (double)p.E;
         const bool fast = moe::fast_gemm_supported(p.dtype, p.H, p.I);
-        t.BM = avg_rows <= 64.0 ? 64 : (avg_rows <= 512.0 || !fast) ? 128 : 256;
+        // 128-row tiles (two workgroups per CU) up to 1024 rows per expert on
+        // average; longer segments amortise a 256-row tile's copies better
+        t.BM = avg_rows <= 64.0 ? 64 : (avg_rows <= 1024.0 || !fast) ? 128 : 256;
     }
     return t;
 }

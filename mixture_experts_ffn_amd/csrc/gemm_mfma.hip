@@ -35,17 +35,25 @@
 //  * The matrix-core step computes C^T = W^T · X^T (weights as the first
 //    operand), so each lane owns 4 consecutive output columns of one row and
 //    the epilogue writes 8 bytes per lane.
-//  * Block tile BM rows x 256 weight columns, 8 waves (two per SIMD: one
-//    wave's MFMAs cover the other's LDS waits): for BM = 64 or 128 each wave
-//    owns all BM rows and 16 columns of each panel (BK = 64, 3 stages); for
-//    BM = 256 the waves are 2 x 4 and each owns 128 rows and 32 columns of
-//    each panel (BK = 32, 4 stages), a third fewer LDS reads and copied bytes
-//    per flop.  A wave whose 128 rows lie past an expert's count skips its
-//    MFMAs, so tall tiles waste no more matrix-core time than short ones.
-//  * Persistent: one workgroup per CU walks an XCD-local slice of the tile
-//    order (the hardware hands workgroup b to XCD b % 8), so tiles in flight
-//    on one XCD share weight panels and token rows in its L2; the next tile's
-//    first copies overlap the current tile's last steps and its epilogue.
+//  * Block tile BM rows x 256 weight columns, two waves per SIMD (one wave's
+//    MFMAs cover the other's LDS waits):
+//      BM = 64:  one workgroup of 8 waves per CU, each wave all 64 rows and 16
+//                columns of each panel (BK = 64, 3 stages);
+//      BM = 128: TWO workgroups of 4 waves per CU, each wave all 128 rows and
+//                32 columns of each panel (BK = 32, 3 stages, 72 KB each).
+//                The per-K-step barrier then holds only one of the two waves
+//                on a SIMD, so the two drift apart and one's MFMAs fill the
+//                other's read and barrier waits; each wave also reads 40 %
+//                fewer LDS bytes per MFMA than with 8 waves of 16 columns;
+//      BM = 256: one workgroup of 8 waves per CU as 2 x 4, each wave 128 rows
+//                and 32 columns of each panel (BK = 32, 4 stages).
+//    A wave whose 128 rows lie past an expert's count skips its MFMAs, so
+//    tall tiles waste no more matrix-core time than short ones.
+//  * Persistent: the workgroups resident on the CUs walk XCD-local slices of
+//    the tile order (the hardware hands workgroup b to XCD b % 8), so tiles
+//    in flight on one XCD share weight panels and token rows in its L2; the
+//    next tile's first copies overlap the current tile's last steps and its
+//    epilogue.
 #include "common.h"
 #include "kernels.h"
 
@@ -62,16 +70,19 @@ constexpr int TILE_N1 = PW;     // GEMM1 output columns per tile
 constexpr int TILE_N2 = 2 * PW; // GEMM2 output columns per tile
 
 enum { KIND_G1 = 1, KIND_G2 = 2 };
-constexpr int kWaves = 8; // waves per workgroup
+// waves per workgroup for a block tile of BM rows: 128-row tiles run as two
+// 4-wave workgroups per CU, the others as one 8-wave workgroup
+constexpr int waves_for(int BM) { return BM == 128 ? 4 : 8; }
 
-// Block tile BM x (2 x 128): BM = 64 or 128 with BK = 64, a 3-stage ring and
-// all 8 waves side by side along N; BM = 256 with BK = 32, a 4-stage ring and
-// the waves as 2 (M) x 4 (N), so each wave owns 128 rows x 32 columns per
+// Block tile BM x (2 x 128): BM = 64 with 8 waves, BK = 64 and a 3-stage ring;
+// BM = 128 with 4 waves, BK = 32 and a 3-stage ring (two workgroups share a
+// CU); waves side by side along N.  BM = 256 with 8 waves as 2 (M) x 4 (N),
+// BK = 32 and a 4-stage ring, so each wave owns 128 rows x 32 columns per
 // panel and needs a third fewer LDS reads and copied bytes per flop.
 template <int BM_, int NW_ = 8> struct Cfg {
     static constexpr int BM = BM_;
     static constexpr int NW = NW_;                   // waves per workgroup
-    static constexpr int BK = BM == 256 ? 32 : 64;   // K per step
+    static constexpr int BK = BM == 256 || NW == 4 ? 32 : 64; // K per step
     static constexpr int NSTAGE = BM == 256 ? 4 : 3; // LDS ring depth
     static constexpr int WM = BM == 256 && NW == 8 ? 2 : 1; // waves along M
     static constexpr int WN = NW / WM;               // waves along N
@@ -263,7 +274,7 @@ struct Cursor {
 };
 
 template <int BM, int MODE, int NWAVES>
-__global__ __launch_bounds__(64 * NWAVES, 1) void moe_fwd_bf16(FastFwdArgs args)
+__global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdArgs args)
 {
     using C = Cfg<BM, NWAVES>;
     constexpr int NW = C::NW;
@@ -689,10 +700,11 @@ __global__ __launch_bounds__(64 * NWAVES, 1) void moe_fwd_bf16(FastFwdArgs args)
     }
 }
 
-template <int BM, int MODE, int NWAVES = kWaves>
+template <int BM, int MODE, int NWAVES = waves_for(BM)>
 static hipError_t launch(const FastFwdArgs &a, int num_cus, hipStream_t stream)
 {
-    const int grid = (num_cus + 7) / 8 * 8; // one workgroup per CU, whole XCDs
+    // 8 / NWAVES workgroups per CU (8 waves per CU), whole XCDs
+    const int grid = (num_cus + 7) / 8 * 8 * (8 / NWAVES);
     hipLaunchKernelGGL((moe_fwd_bf16<BM, MODE, NWAVES>), dim3((unsigned)grid), dim3(64 * NWAVES),
                        0, stream, a);
     return hipGetLastError();
