@@ -17,20 +17,22 @@
 //
 // Operand layouts in memory decide the LDS layout and the fragment read:
 //  * KROW: the operand's M (or N) rows are contiguous along K (x, act, dY,
-//    dh rows; W2 rows for B2; W1 rows for B4).  LDS tile [R][64] with the
-//    16-byte piece index XOR-ed by (row / 2) % 8; fragments are one 128-bit
-//    LDS read.
+//    dh rows; W2 rows for B2; W1 rows for B4).  LDS tile [R][BK] with the
+//    16-byte piece index XOR-ed by (row / 2) % 8 (BK = 64); fragments are one
+//    128-bit LDS read.
 //  * KCOL: memory rows are K indices, contiguous along M (or N) (W1/W2 in
 //    the forward; act_g, dY, x, dh rows in the weight gradients).  LDS tile
-//    [64][R] untransposed with the 32-byte unit index XOR-ed by a 3-bit hash
+//    [BK][R] untransposed with the 32-byte unit index XOR-ed by a 3-bit hash
 //    of k; fragments are two transposing 64-bit LDS reads.
 //  Both swizzles were measured conflict-free.  Copies go global -> LDS
 //  directly (16 bytes per lane); pieces outside the problem (K or N edges,
 //  rows past an expert's count in the weight gradients) copy from a zero
 //  page, so no tile needs a special path.
 //
-// Pipeline: one 512-thread workgroup per CU, 3-stage LDS ring, copies two K
-// steps ahead.  A producer cursor walks the workgroup's tile sequence two
+// Pipeline: 8 waves per CU, 3-stage LDS ring, copies two K steps ahead; one
+// 8-wave workgroup with BK = 64 (144 KB), or for the weight gradients two
+// 4-wave workgroups with BK = 32 (72 KB each), whose per-step barriers hold
+// only one of the two waves on a SIMD.  A producer cursor walks the workgroup's tile sequence two
 // steps ahead of the consumer, across tile boundaries and over tiles without
 // K steps (empty experts), so the next tile's first copies overlap the
 // current tile's tail and epilogue.  Each wave waits only for its own copies
@@ -50,9 +52,16 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-constexpr int BK = 64;
-constexpr int NSTAGE = 3;
-constexpr int NW = 8; // waves per workgroup: two per SIMD
+constexpr int NSTAGE = 3; // LDS ring depth
+
+// Swizzled 16-byte piece of KROW row r (rows of PIECES pieces): 128-byte rows
+// XOR by (r / 2) % 8, 64-byte rows by (r / 4) % 4, so the 16 rows one 128-bit
+// fragment read touches fall in 16 different bank groups.
+template <int PIECES> __device__ __forceinline__ int krow_piece(int r, int q)
+{
+    static_assert(PIECES == 8 || PIECES == 4, "KROW row length");
+    return PIECES == 8 ? q ^ ((r >> 1) & 7) : q ^ ((r >> 2) & 3);
+}
 
 // A page of zeros that out-of-problem pieces copy from.
 __device__ __attribute__((aligned(256))) const uint32_t kZeroPage[64] = {0};
@@ -88,8 +97,27 @@ template <> struct KindTraits<B7> {
     static constexpr int ALAY = KCOL, BLAY = KCOL;
 };
 
+// Workgroup shape per kind.  The weight gradients (KCOL A: k-rows of 256
+// bytes or more in every copy) run as two 4-wave workgroups per CU with
+// BK = 32, so each SIMD holds one wave of each and one workgroup's per-step
+// barrier holds only its own wave.  The kinds with KROW operands keep one
+// 8-wave workgroup with BK = 64: their copies fetch BK * 2 bytes per row, and
+// 64-byte row pieces (half a cache line) measured slower than the gain.
+template <int KIND> struct Shape {
+    static constexpr bool SPLIT = KindTraits<KIND>::ALAY == KCOL;
+    static constexpr int NW = SPLIT ? 4 : 8;   // waves per workgroup
+    static constexpr int BK = SPLIT ? 32 : 64; // K per step
+    static constexpr int WGPC = SPLIT ? 2 : 1; // workgroups per CU
+};
+
 template <int KIND, int BM_, int WM_> struct Cfg {
     using KT = KindTraits<KIND>;
+    static constexpr int NW = Shape<KIND>::NW;
+    static constexpr int BK = Shape<KIND>::BK;
+    static constexpr int WGPC = Shape<KIND>::WGPC;
+    static constexpr int KPIECES = BK / 8;         // KROW: 16-byte pieces per row
+    static constexpr int KRPC = 1024 / (BK * 2);   // KROW: rows per 1 KB copy chunk
+    static constexpr int KCPP = BK / 4;            // paired KCOL: chunks per 128-column panel
     static constexpr int BM = BM_;
     static constexpr int BNT = 256;                      // B columns staged per tile
     static constexpr int PW = KT::PAIRED ? 128 : 256;    // columns per panel
@@ -198,7 +226,15 @@ __device__ __forceinline__ TileInfo decode_tile(const EngineArgs &a, int L)
         const int mtm = (a.M + BM - 1) / BM, ntn = (a.N + C::OUT_N - 1) / C::OUT_N;
         t.e = L / (mtm * ntn);
         const int local = L - t.e * mtm * ntn;
-        const int n_t = local / mtm, m_t = local % mtm;
+        // groups of GM feature tiles, N outer: the 32 tiles in flight on one
+        // XCD then span 8 M-tiles x 4 N-tiles of one expert (their operand
+        // blocks fit its L2) instead of 32 M-tiles of one N-tile
+        constexpr int GM = 8;
+        const int grp = local / (GM * ntn);
+        const int first_m = grp * GM;
+        const int gm = min(mtm - first_m, GM);
+        const int rr = local - grp * GM * ntn;
+        const int n_t = rr / gm, m_t = first_m + rr % gm;
         t.m0 = m_t * BM;
         t.rows = min(BM, a.M - t.m0);
         t.n0 = n_t * C::OUT_N;
@@ -211,7 +247,7 @@ __device__ __forceinline__ TileInfo decode_tile(const EngineArgs &a, int L)
     t.n0 = uni(t.n0);
     t.seg0 = uni(t.seg0);
     t.klen = uni(t.klen);
-    t.nk = (t.klen + BK - 1) / BK;
+    t.nk = (t.klen + C::BK - 1) / C::BK;
     return t;
 }
 
@@ -274,22 +310,23 @@ __device__ __forceinline__ void make_src(const EngineArgs &a, const TileInfo &t,
     for (int i = 0; i < C::A_LOADS; ++i) {
         const int c = wave * C::A_LOADS + i;
         if constexpr (KT::ALAY == KROW) {
-            // chunk c: rows 8c .. 8c+7 of the tile, 16-byte unit `lane`
-            const int r = c * 8 + (lane >> 3);
-            const int piece = (lane & 7) ^ ((r >> 1) & 7);
+            // chunk c: rows KRPC c .. KRPC c + KRPC-1 of the tile, 16-byte unit `lane`
+            constexpr int KRPC = C::KRPC, KPIECES = C::KPIECES;
+            const int r = c * KRPC + lane / KPIECES;
+            const int piece = krow_piece<KPIECES>(r, lane % KPIECES);
             int64_t mrow;
             if constexpr (KT::A_GATHER) {
-                // the chunk's 8 row indices are wave-uniform: scalar loads
-                int idx[8];
+                // the chunk's KRPC row indices are wave-uniform: scalar loads
+                int idx[KRPC];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int rj = c * 8 + j < t.rows ? c * 8 + j : 0; // tail rows repeat row 0
+                for (int j = 0; j < KRPC; ++j) {
+                    const int rj = c * KRPC + j < t.rows ? c * KRPC + j : 0; // tail rows repeat row 0
                     idx[j] = ldc(a.sorted_slot, t.m0 + rj);
                 }
                 int v = idx[0];
 #pragma unroll
-                for (int j = 1; j < 8; ++j)
-                    v = (lane >> 3) == j ? idx[j] : v;
+                for (int j = 1; j < KRPC; ++j)
+                    v = lane / KPIECES == j ? idx[j] : v;
                 mrow = v / a.topk;
             } else {
                 mrow = t.m0 + (r < t.rows ? r : 0);
@@ -315,8 +352,8 @@ __device__ __forceinline__ void make_src(const EngineArgs &a, const TileInfo &t,
         const int c = wave * C::B_LOADS + i;
         if constexpr (KT::BLAY == KROW) {
             // weight rows n of expert e (B2: W2[e][n][:], B4: W1[e][n][:])
-            const int r = c * 8 + (lane >> 3);
-            const int piece = (lane & 7) ^ ((r >> 1) & 7);
+            const int r = c * C::KRPC + lane / C::KPIECES;
+            const int piece = krow_piece<C::KPIECES>(r, lane % C::KPIECES);
             const int n = t.n0 + r;
             const int nc = n < a.N ? n : 0; // tail columns repeat column 0; never stored
             s.b[i] = a.B + (int64_t)t.e * a.b_estride + (int64_t)nc * a.ldb + piece * 8;
@@ -325,8 +362,8 @@ __device__ __forceinline__ void make_src(const EngineArgs &a, const TileInfo &t,
         } else {
             int panel, kr, pp;
             if constexpr (KT::PAIRED) { // two 128-column panels: 256-byte k-rows
-                panel = c >> 4;
-                kr = (c & 15) * 4 + (lane >> 4);
+                panel = c / C::KCPP;
+                kr = (c % C::KCPP) * 4 + (lane >> 4);
                 pp = lane & 15;
             } else { // one 256-column panel: 512-byte k-rows
                 panel = 0;
@@ -359,7 +396,7 @@ __device__ __forceinline__ void issue(const EngineArgs &a, const TileInfo &t,
 {
     using C = Cfg<KIND, BM, WM>;
     using KT = typename C::KT;
-    const int k0 = kb * BK;
+    const int k0 = kb * C::BK;
     // ---- A
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) {
@@ -389,7 +426,7 @@ __device__ __forceinline__ void issue(const EngineArgs &a, const TileInfo &t,
         } else if constexpr (KT::TOKEN_M) {
             constexpr int RB = C::PW * 2;
             const int c = wave * C::B_LOADS + i;
-            const int kr = KT::PAIRED ? (c & 15) * 4 + (lane >> 4) : kcol_krow<RB>(c, lane);
+            const int kr = KT::PAIRED ? (c % C::KCPP) * 4 + (lane >> 4) : kcol_krow<RB>(c, lane);
             src = (s.b_col_ok[i] && k0 + kr < t.klen) ? (const void *)(s.b[i] + (int64_t)k0 * a.ldb)
                                                        : (const void *)kZeroPage;
         } else {
@@ -407,13 +444,13 @@ __device__ __forceinline__ void issue(const EngineArgs &a, const TileInfo &t,
 }
 
 // fragment reads ------------------------------------------------------------
-// KROW tile [R][64]: row r, 8 k values starting at logical piece q
+// KROW tile [R][BK]: row r, 8 k values starting at logical piece q
+template <int BK>
 __device__ __forceinline__ bf16x8 frag_krow(const unsigned char *tile, int r, int q)
 {
-    const int piece = q ^ ((r >> 1) & 7);
-    return *reinterpret_cast<const bf16x8 *>(tile + r * 128 + piece * 16);
+    return *reinterpret_cast<const bf16x8 *>(tile + r * (BK * 2) + krow_piece<BK / 8>(r, q) * 16);
 }
-// KCOL tile [64][R] (R*2-byte k-rows): lane's column block nb (multiple of 16),
+// KCOL tile [BK][R] (R*2-byte k-rows): lane's column block nb (multiple of 16),
 // 8 k values starting at k8 (multiple of 8); two transposing reads
 template <int RB>
 __device__ __forceinline__ bf16x8 frag_kcol(const unsigned char *tile, int nb, int k8, int lane)
@@ -552,10 +589,11 @@ __device__ __forceinline__ void epilogue(const EngineArgs &a, const TileInfo &t,
 }
 
 template <int KIND, int BM, int WM>
-__global__ __launch_bounds__(64 * NW, 1) void engine_kernel(EngineArgs a)
+__global__ __launch_bounds__(64 * Shape<KIND>::NW, Shape<KIND>::WGPC) void engine_kernel(EngineArgs a)
 {
     using C = Cfg<KIND, BM, WM>;
     using KT = typename C::KT;
+    constexpr int BK = C::BK;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * C::STAGE_BYTES];
 
     const int total = uni(total_tiles<KIND, BM, WM>(a));
@@ -641,7 +679,7 @@ __global__ __launch_bounds__(64 * NW, 1) void engine_kernel(EngineArgs a)
 #pragma unroll
                 for (int fm = 0; fm < C::FM; ++fm) {
                     if constexpr (KT::ALAY == KROW)
-                        af[h2][fm] = frag_krow(sA, wm * C::WTM + fm * 16 + (lane & 15),
+                        af[h2][fm] = frag_krow<BK>(sA, wm * C::WTM + fm * 16 + (lane & 15),
                                                (kk >> 3) + (lane >> 4));
                     else
                         af[h2][fm] = frag_kcol<BM * 2>(sA, wm * C::WTM + fm * 16,
@@ -653,7 +691,7 @@ __global__ __launch_bounds__(64 * NW, 1) void engine_kernel(EngineArgs a)
                     for (int fn = 0; fn < C::FN; ++fn) {
                         const int nb = p * C::PW + wn * C::WTN + fn * 16;
                         if constexpr (KT::BLAY == KROW)
-                            bf[h2][p][fn] = frag_krow(sB, nb + (lane & 15), (kk >> 3) + (lane >> 4));
+                            bf[h2][p][fn] = frag_krow<BK>(sB, nb + (lane & 15), (kk >> 3) + (lane >> 4));
                         else if constexpr (KT::PAIRED)
                             bf[h2][p][fn] = frag_kcol<C::PW * 2>(sB + p * (BK * C::PW * 2),
                                                                  wn * C::WTN + fn * 16,
@@ -696,15 +734,16 @@ __global__ __launch_bounds__(64 * NW, 1) void engine_kernel(EngineArgs a)
 template <int KIND, int BM, int WM>
 static hipError_t launch(const EngineArgs &a, int num_cus, hipStream_t stream)
 {
-    const int grid = (num_cus + 7) / 8 * 8; // one workgroup per CU, whole XCDs
-    hipLaunchKernelGGL((engine_kernel<KIND, BM, WM>), dim3((unsigned)grid), dim3(64 * NW), 0,
+    using S = Shape<KIND>;
+    const int grid = (num_cus + 7) / 8 * 8 * S::WGPC; // whole XCDs
+    hipLaunchKernelGGL((engine_kernel<KIND, BM, WM>), dim3((unsigned)grid), dim3(64 * S::NW), 0,
                        stream, a);
     return hipGetLastError();
 }
 
 } // namespace eng
 
-int engine_dgp_width(int I) { return ((I + 255) / 256) * (eng::NW / 2); }
+int engine_dgp_width(int I) { return ((I + 255) / 256) * eng::Cfg<eng::B2, 128, 2>::WAVES_N; }
 
 hipError_t launch_engine(int kind, int BM, const EngineArgs &a, int num_cus, hipStream_t stream)
 {
