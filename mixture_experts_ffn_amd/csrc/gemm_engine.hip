@@ -493,21 +493,43 @@ __device__ __forceinline__ void epilogue(const EngineArgs &a, const TileInfo &t,
         // dact = g u; dh = [dact b σ(a)(1 + a(1-σ(a))), dact silu(a)]; act_g = g silu(a) b;
         // per-row partial of Σ_i u act over this wave's columns (d_g = g-free row dot)
         const int I = a.N;
+        // Every load of the epilogue is issued, unconditionally (rows and
+        // columns outside the tile read its first row / column instead), before
+        // any store: the tile then pays two memory round trips (slot, then gate
+        // and the saved h) instead of a dependent chain per 16-row block and a
+        // load-store round trip per 16x16 block.
+        int slot[C::FM];
+        u32x2 hav[C::FM][C::FN], hbv[C::FM][C::FN];
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int r = wm * C::WTM + fm * 16 + (lane & 15);
+            const int64_t p = t.m0 + (r < t.rows ? r : 0);
+            slot[fm] = a.sorted_slot[p];
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) {
+                const int c = t.n0 + wn * C::WTN + fn * 16 + cl;
+                const int cc = c < I ? c : t.n0;
+                hav[fm][fn] = *reinterpret_cast<const u32x2 *>(a.Hs + p * 2 * I + cc);
+                hbv[fm][fn] = *reinterpret_cast<const u32x2 *>(a.Hs + p * 2 * I + I + cc);
+            }
+        }
+        float gv[C::FM];
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+            gv[fm] = a.gates[slot[fm]];
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
             const int r = wm * C::WTM + fm * 16 + (lane & 15);
             const bool rok = r < t.rows;
             const int64_t p = t.m0 + (rok ? r : 0);
-            const float g = rok ? a.gates[a.sorted_slot[p]] : 0.f;
+            const float g = rok ? gv[fm] : 0.f;
             float dg = 0.f;
 #pragma unroll
             for (int fn = 0; fn < C::FN; ++fn) {
                 const int c = t.n0 + wn * C::WTN + fn * 16 + cl;
                 if (rok && c < I) {
-                    const u32x2 hav = *reinterpret_cast<const u32x2 *>(a.Hs + p * 2 * I + c);
-                    const u32x2 hbv = *reinterpret_cast<const u32x2 *>(a.Hs + p * 2 * I + I + c);
-                    const bf16 *ha = reinterpret_cast<const bf16 *>(&hav);
-                    const bf16 *hb = reinterpret_cast<const bf16 *>(&hbv);
+                    const bf16 *ha = reinterpret_cast<const bf16 *>(&hav[fm][fn]);
+                    const bf16 *hb = reinterpret_cast<const bf16 *>(&hbv[fm][fn]);
                     float da[4], db[4], ag[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
