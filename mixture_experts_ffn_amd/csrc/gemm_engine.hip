@@ -275,27 +275,59 @@ template <int KIND, int BM, int WM> struct Src {
     bool b_col_ok[C::B_LOADS];
 };
 
+// Row indices of the gathered token-row KCOL operand of a weight gradient
+// (B7: x rows, B5: dY rows) for one K step: the sorted_slot entries of the
+// k-rows this wave copies, read with scalar loads (wave-uniform addresses,
+// lgkmcnt) one producer step before the copies that use them, so their
+// latency hides behind a K step instead of stalling the copy issue.
+template <int KIND, int BM, int WM> struct GatherIdx {
+    using C = Cfg<KIND, BM, WM>;
+    using KT = typename C::KT;
+    static constexpr bool ON_A = KT::A_GATHER && KT::ALAY == KCOL;
+    static constexpr bool ON_B = KT::B_GATHER && KT::BLAY == KCOL && !KT::TOKEN_M;
+    static constexpr int NCH = ON_A ? C::A_LOADS : ON_B ? C::B_LOADS : 1; // chunks per wave
+    static constexpr int RB = ON_A ? BM * 2 : C::PW * 2;                   // bytes per k-row
+    static constexpr int KPC = 1024 / RB;                                  // k-rows per chunk
+    // index (i, q) at element i * KPC + q; a vector value, so it stays in registers
+    typedef int vec __attribute__((ext_vector_type(NCH * KPC)));
+    vec v;
+};
+
+template <int KIND, int BM, int WM>
+__device__ __forceinline__ void fetch_gather(const EngineArgs &a, const TileInfo &t, int kb,
+                                             int wave, GatherIdx<KIND, BM, WM> &g)
+{
+    using G = GatherIdx<KIND, BM, WM>;
+    if constexpr (G::ON_A || G::ON_B) {
+        const int k0 = kb * Cfg<KIND, BM, WM>::BK;
+#pragma unroll
+        for (int i = 0; i < G::NCH; ++i) {
+            const int kbase = k0 + (wave * G::NCH + i) * G::KPC;
+#pragma unroll
+            for (int q = 0; q < G::KPC; ++q) // rows past the expert's count: 0 (their pieces copy zeros)
+                g.v[i * G::KPC + q] = kbase + q < t.klen ? ldc(a.sorted_slot, t.seg0 + kbase + q) : 0;
+        }
+    }
+}
+
 // Memory row of the lane's k-row for a token-row KCOL operand (weight
 // gradients): k-rows kbase .. kbase + KPC - 1 of the chunk are permuted rows
-// seg0 + k; gathered operands read the chunk's KPC row indices with scalar
-// loads (wave-uniform addresses), so the vector-memory counter holds only the
-// copies.  Rows past the expert's count return 0 (their pieces copy zeros).
+// seg0 + k; a gathered operand maps them through the prefetched indices.
 template <int RB>
-__device__ __forceinline__ int64_t kcol_token_row(const EngineArgs &a, const TileInfo &t,
-                                                  int kbase, int lane, bool gather)
+__device__ __forceinline__ int64_t kcol_token_row(const TileInfo &t, int kbase, int lane)
+{
+    return (int64_t)t.seg0 + kbase + lane / (RB / 16);
+}
+template <int RB, typename G>
+__device__ __forceinline__ int64_t kcol_gather_row(const EngineArgs &a, int lane, const G &g, int i)
 {
     constexpr int KPC = 1024 / RB;
+    static_assert(KPC == G::KPC, "chunk geometry");
     const int j = lane / (RB / 16);
-    if (!gather)
-        return (int64_t)t.seg0 + kbase + j;
-    int idx[KPC];
-#pragma unroll
-    for (int q = 0; q < KPC; ++q)
-        idx[q] = kbase + q < t.klen ? ldc(a.sorted_slot, t.seg0 + kbase + q) : 0;
-    int v = idx[0];
+    int v = g.v[i * KPC];
 #pragma unroll
     for (int q = 1; q < KPC; ++q)
-        v = j == q ? idx[q] : v;
+        v = j == q ? g.v[i * KPC + q] : v;
     return (int64_t)(v / a.topk);
 }
 
@@ -392,10 +424,11 @@ template <int RB> __device__ __forceinline__ int kcol_krow(int c, int lane)
 template <int KIND, int BM, int WM>
 __device__ __forceinline__ void issue(const EngineArgs &a, const TileInfo &t,
                                       const Src<KIND, BM, WM> &s, int kb, unsigned char *sbase,
-                                      int wave, int lane)
+                                      int wave, int lane, const GatherIdx<KIND, BM, WM> &g)
 {
     using C = Cfg<KIND, BM, WM>;
     using KT = typename C::KT;
+    using G = GatherIdx<KIND, BM, WM>;
     const int k0 = kb * C::BK;
     // ---- A
 #pragma unroll
@@ -408,9 +441,11 @@ __device__ __forceinline__ void issue(const EngineArgs &a, const TileInfo &t,
             constexpr int RB = BM * 2;
             const int kr = kcol_krow<RB>(wave * C::A_LOADS + i, lane);
             const int kk = k0 + kr;
-            const int64_t mrow =
-                kcol_token_row<RB>(a, t, k0 + (wave * C::A_LOADS + i) * (1024 / RB), lane,
-                                   KT::A_GATHER);
+            int64_t mrow;
+            if constexpr (G::ON_A)
+                mrow = kcol_gather_row<RB>(a, lane, g, i);
+            else
+                mrow = kcol_token_row<RB>(t, k0 + (wave * C::A_LOADS + i) * (1024 / RB), lane);
             src = (s.a_col_ok[i] && kk < t.klen) ? (const void *)(s.a[i] + mrow * a.lda)
                                                   : (const void *)kZeroPage;
         }
@@ -433,9 +468,11 @@ __device__ __forceinline__ void issue(const EngineArgs &a, const TileInfo &t,
             constexpr int RB = C::PW * 2;
             const int kr = kcol_krow<RB>(wave * C::B_LOADS + i, lane);
             const int kk = k0 + kr;
-            const int64_t mrow =
-                kcol_token_row<RB>(a, t, k0 + (wave * C::B_LOADS + i) * (1024 / RB), lane,
-                                   KT::B_GATHER);
+            int64_t mrow;
+            if constexpr (G::ON_B)
+                mrow = kcol_gather_row<RB>(a, lane, g, i);
+            else
+                mrow = kcol_token_row<RB>(t, k0 + (wave * C::B_LOADS + i) * (1024 / RB), lane);
             src = (s.b_col_ok[i] && kk < t.klen) ? (const void *)(s.b[i] + mrow * a.ldb)
                                                   : (const void *)kZeroPage;
         }
@@ -649,19 +686,30 @@ __global__ __launch_bounds__(64 * Shape<KIND>::NW, Shape<KIND>::WGPC) void engin
         }
     };
     p_skip_empty();
+    // row indices of the producer's next step (gathered weight-gradient operands);
+    // in the K loop they are fetched after the step's MFMAs, so the barrier
+    // wait covers their latency before the next step's first LDS wait
+    GatherIdx<KIND, BM, WM> pg;
+    auto fetch = [&]() {
+        if (pvalid)
+            fetch_gather<KIND, BM, WM>(a, pt, pkb, wave, pg);
+    };
     int gstage_issue = 0; // stage the producer writes next
     int inflight = 0;     // steps copied but not yet consumed
     auto produce = [&]() {
-        issue<KIND, BM, WM>(a, pt, ps, pkb, smem + gstage_issue * C::STAGE_BYTES, wave, lane);
+        issue<KIND, BM, WM>(a, pt, ps, pkb, smem + gstage_issue * C::STAGE_BYTES, wave, lane, pg);
         gstage_issue = gstage_issue == NSTAGE - 1 ? 0 : gstage_issue + 1;
         ++inflight;
         ++pkb;
         p_skip_empty();
     };
+    fetch();
     if (pvalid)
         produce();
+    fetch();
     if (pvalid)
         produce();
+    fetch();
 
     f32x4 acc[C::NPANEL][C::FM][C::FN];
     int cstage = 0;
@@ -747,6 +795,10 @@ __global__ __launch_bounds__(64 * Shape<KIND>::NW, Shape<KIND>::WGPC) void engin
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, NDS - FIRST - PAIRS, 0);
+            }
+            if constexpr (GatherIdx<KIND, BM, WM>::ON_A || GatherIdx<KIND, BM, WM>::ON_B) {
+                __builtin_amdgcn_sched_barrier(0);
+                fetch();
             }
         }
         epilogue<KIND, BM, WM>(a, t, acc, wm, wn, lane);
