@@ -11,21 +11,44 @@
 // mtile_off[E+1], the prefix sum of ceil(counts[e] / BM) M-tiles that the
 // grouped GEMMs walk, with mtile_expert[j], the expert owning M-tile j.
 //
-// Three launches, no global atomics and no memset:
-//   1. hist:    one wave per chunk of RC slots counts ids per expert in LDS
-//               and writes its column of hist[E][NB] plus a bad-id flag.
-//   2. scan:    one 1024-thread block turns hist into per-(expert, chunk)
-//               exclusive bases, then scans counts and M-tile counts over
-//               experts, writes the status word and zeroes the release
-//               counters of the pipelined forward that follows.
-//   3. scatter: one wave per chunk walks its slots in order, 64 at a time;
-//               lanes holding the same expert find each other with ballots
-//               over the id bits, so the rank inside the round is a popcount
-//               and the order stays stable.
+// No global atomics and no memset.  The slots are cut into chunks of RC
+// (512) and one wave routes one chunk; the work is
+//   hist:    count each chunk's ids per expert (hist[E][NB]) and flag bad ids;
+//   scan:    exclusive per-(expert, chunk) bases, counts and M-tile counts
+//            scanned over experts, the status word, and the zeroed release
+//            counters of the pipelined forward that follows;
+//   scatter: each wave walks its chunk in order, 64 slots at a time; lanes
+//            holding the same expert find each other with ballots over the id
+//            bits, so the rank inside the round is a popcount and the order
+//            stays stable.
+// Launches: one 1024-thread block does all three when the slots fit 16
+// chunks (decode-sized batches); otherwise a hist launch, then 1024-thread
+// blocks of 16 chunks that each redo the (small) scan for themselves and
+// scatter.  With more than 910 experts the per-block table would not fit
+// 64 KB of LDS, and hist, scan and scatter run as three launches.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
+
+// Ids of up to 8 rounds of 64 slots from r0 < s1 on (lane's slots
+// r0 + 64 j + lane below s1; -1 past it).  The loads are unconditional (a
+// slot past s1 re-reads slot s1 - 1), so all 8 are in flight together and a
+// chunk costs one memory round trip per 512 slots instead of one per 64.
+template <typename Id>
+__device__ inline void load_ids8(const Id *__restrict__ ids, int64_t r0, int64_t s1, int64_t (&v)[8])
+{
+    const int lane = threadIdx.x & 63;
+    Id raw[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int64_t s = r0 + 64 * j + lane;
+        raw[j] = ids[s < s1 ? s : s1 - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        v[j] = r0 + 64 * j + lane < s1 ? (int64_t)raw[j] : -1;
+}
 
 template <typename Id>
 __global__ __launch_bounds__(64) void route_hist_kernel(const Id *__restrict__ ids, int64_t TK,
@@ -41,12 +64,19 @@ __global__ __launch_bounds__(64) void route_hist_kernel(const Id *__restrict__ i
     const int64_t s0 = (int64_t)b * RC;
     const int64_t s1 = s0 + RC < TK ? s0 + RC : TK;
     int anybad = 0;
-    for (int64_t s = s0 + threadIdx.x; s < s1; s += 64) {
-        const int64_t e = (int64_t)ids[s];
-        if (e >= 0 && e < E)
-            atomicAdd(&lh[e], 1);
-        else
-            anybad = 1;
+    for (int64_t r0 = s0; r0 < s1; r0 += 512) {
+        int64_t v[8];
+        load_ids8(ids, r0, s1, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t e = v[j];
+            if (r0 + 64 * j + threadIdx.x >= s1)
+                continue;
+            if (e >= 0 && e < E)
+                atomicAdd(&lh[e], 1);
+            else
+                anybad = 1;
+        }
     }
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += 64)
@@ -91,52 +121,31 @@ __device__ inline int32_t block_excl_scan(int32_t v, int32_t *s_w, int32_t *tota
     return s_w[16 + wave] + incl - v;
 }
 
-__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ hist,
-                                                          const int32_t *__restrict__ bad, int E,
-                                                          int NB, int BM,
-                                                          int32_t *__restrict__ counts,
-                                                          int32_t *__restrict__ offsets,
-                                                          int32_t *__restrict__ mtile_off,
-                                                          int32_t *__restrict__ mtile_expert,
-                                                          int32_t *__restrict__ status,
-                                                          int32_t *__restrict__ ctr, int nctr,
-                                                          SavedHeader *__restrict__ hdr,
-                                                          uint64_t problem_hash)
+// Start-of-forward bookkeeping done by the first routing block: the saved
+// context's header and the zeroed release counters of the pipelined forward.
+__device__ inline void write_header_and_counters(SavedHeader *hdr, uint64_t problem_hash,
+                                                 int32_t *ctr, int nctr)
 {
     if (hdr && threadIdx.x == 0) {
         hdr->magic = kSavedMagic;
         hdr->version = kSavedVersion;
         hdr->problem = problem_hash;
     }
-    for (int j = threadIdx.x; j < nctr; j += 1024)
+    for (int j = threadIdx.x; j < nctr; j += blockDim.x)
         ctr[j] = 0;
-    __shared__ int32_t s_cnt[1024];
-    __shared__ int32_t s_moff[1025];
-    __shared__ int32_t s_w[40];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int e = wave; e < E; e += 16) {
-        int32_t running = 0;
-        int32_t *row = hist + (int64_t)e * NB;
-        for (int j0 = 0; j0 < NB; j0 += 64) {
-            const int j = j0 + lane;
-            const int32_t v = j < NB ? row[j] : 0;
-            const int32_t incl = wave_incl_scan(v);
-            if (j < NB)
-                row[j] = running + incl - v;
-            running += __shfl(incl, 63, 64);
-        }
-        if (lane == 0)
-            s_cnt[e] = running;
-    }
-    int anybad = 0;
-    for (int j = threadIdx.x; j < NB; j += 1024)
-        anybad |= bad[j];
-    anybad = __syncthreads_or(anybad);
+}
 
+// counts, offsets, the M-tile tables and the status word, from expert e's
+// count c and exclusive offset off held by thread e (all 1024 threads of one
+// block call this; total = offsets[E]).
+__device__ inline void publish_plan(int32_t c, int32_t off, int32_t total, bool anybad, int E,
+                                    int BM, int32_t *__restrict__ counts,
+                                    int32_t *__restrict__ offsets,
+                                    int32_t *__restrict__ mtile_off,
+                                    int32_t *__restrict__ mtile_expert,
+                                    int32_t *__restrict__ status, int32_t *s_w, int32_t *s_moff)
+{
     const int e = threadIdx.x;
-    const int32_t c = e < E ? s_cnt[e] : 0;
-    int32_t total;
-    const int32_t off = block_excl_scan(c, s_w, &total);
     if (e < E) {
         counts[e] = c;
         offsets[e] = off;
@@ -169,6 +178,99 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ 
     }
 }
 
+__global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ hist,
+                                                          const int32_t *__restrict__ bad, int E,
+                                                          int NB, int BM,
+                                                          int32_t *__restrict__ counts,
+                                                          int32_t *__restrict__ offsets,
+                                                          int32_t *__restrict__ mtile_off,
+                                                          int32_t *__restrict__ mtile_expert,
+                                                          int32_t *__restrict__ status,
+                                                          int32_t *__restrict__ ctr, int nctr,
+                                                          SavedHeader *__restrict__ hdr,
+                                                          uint64_t problem_hash)
+{
+    write_header_and_counters(hdr, problem_hash, ctr, nctr);
+    __shared__ int32_t s_cnt[1024];
+    __shared__ int32_t s_moff[1025];
+    __shared__ int32_t s_w[40];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int e = wave; e < E; e += 16) {
+        int32_t running = 0;
+        int32_t *row = hist + (int64_t)e * NB;
+        for (int j0 = 0; j0 < NB; j0 += 64) {
+            const int j = j0 + lane;
+            const int32_t v = j < NB ? row[j] : 0;
+            const int32_t incl = wave_incl_scan(v);
+            if (j < NB)
+                row[j] = running + incl - v;
+            running += __shfl(incl, 63, 64);
+        }
+        if (lane == 0)
+            s_cnt[e] = running;
+    }
+    int anybad = 0;
+    for (int j = threadIdx.x; j < NB; j += 1024)
+        anybad |= bad[j];
+    anybad = __syncthreads_or(anybad);
+
+    const int e = threadIdx.x;
+    const int32_t c = e < E ? s_cnt[e] : 0;
+    int32_t total;
+    const int32_t off = block_excl_scan(c, s_w, &total);
+    publish_plan(c, off, total, anybad, E, BM, counts, offsets, mtile_off, mtile_expert, status,
+                 s_w, s_moff);
+}
+
+// One wave routes the slots [s0, s1) in order, 64 at a time: lanes holding
+// the same expert find each other with ballots over the id bits, so the rank
+// inside the round is a popcount and the order stays stable.  base[e * bs] is
+// expert e's next position for this chunk (LDS, advanced here).
+template <typename Id>
+__device__ inline void scatter_chunk(const Id *__restrict__ ids, int64_t s0, int64_t s1, int E,
+                                     int nbits, int32_t *base, int bs,
+                                     int32_t *__restrict__ sorted_slot,
+                                     int32_t *__restrict__ slot_pos)
+{
+    const int lane = threadIdx.x & 63;
+    const uint64_t lt = lanemask_lt();
+    for (int64_t r0 = s0; r0 < s1; r0 += 512) {
+        int64_t idv[8];
+        load_ids8(ids, r0, s1, idv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t r = r0 + 64 * j;
+            if (r >= s1)
+                break;
+            const int64_t s = r + lane;
+            const bool in = s < s1;
+            const int64_t eid = idv[j];
+            const bool valid = in && eid >= 0 && eid < E;
+            const int e = valid ? (int)eid : 0;
+            uint64_t m = __ballot(valid);
+            for (int bit = 0; bit < nbits; ++bit) {
+                const bool v = (e >> bit) & 1;
+                const uint64_t bb = __ballot(v);
+                m &= v ? bb : ~bb;
+            }
+            const int rank = __popcll(m & lt);
+            int pos = 0;
+            if (valid) {
+                pos = base[e * bs] + rank;
+                sorted_slot[pos] = (int32_t)s;
+                slot_pos[s] = pos;
+            } else if (in) {
+                slot_pos[s] = -1;
+            }
+            // the lowest lane of each expert group advances that expert's base
+            // after every lane of the round has read it (LDS operations of one
+            // wave complete in program order)
+            if (valid && rank == 0)
+                base[e * bs] = pos + __popcll(m);
+        }
+    }
+}
+
 template <typename Id>
 __global__ __launch_bounds__(64) void route_scatter_kernel(
     const Id *__restrict__ ids, int64_t TK, int E, int nbits, int RC, int NB,
@@ -180,36 +282,126 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(
     for (int e = threadIdx.x; e < E; e += 64)
         base[e] = offsets[e] + hist[(int64_t)e * NB + b];
     __syncthreads();
-    const int lane = threadIdx.x;
-    const uint64_t lt = lanemask_lt();
     const int64_t s0 = (int64_t)b * RC;
     const int64_t s1 = s0 + RC < TK ? s0 + RC : TK;
-    for (int64_t r = s0; r < s1; r += 64) {
-        const int64_t s = r + lane;
-        const bool in = s < s1;
-        const int64_t eid = in ? (int64_t)ids[s] : -1;
-        const bool valid = in && eid >= 0 && eid < E;
-        const int e = valid ? (int)eid : 0;
-        uint64_t m = __ballot(valid);
-        for (int bit = 0; bit < nbits; ++bit) {
-            const bool v = (e >> bit) & 1;
-            const uint64_t bb = __ballot(v);
-            m &= v ? bb : ~bb;
+    scatter_chunk(ids, s0, s1, E, nbits, base, 1, sorted_slot, slot_pos);
+}
+
+// Fused routing: a 1024-thread block owns the 16 consecutive chunks
+// 16 b .. 16 b + 15, wave w the chunk 16 b + w.
+//  ONE = true  (NB <= 16, one block): each wave first counts its chunk per
+//              expert into the block's table, so routing is one launch.
+//  ONE = false: the table comes from route_hist_kernel; every block reads
+//              each expert's row of it (all loads issued at once) for the
+//              total and the sum over chunks before its own, which replaces
+//              the separate scan launch.
+// Every block then scans the totals into offsets and turns its table into
+// per-(expert, chunk) bases; block 0 also publishes counts, offsets, the
+// M-tile tables and the status word.  LDS: tab[E][16], tot[E], bef[E].
+template <typename Id, bool ONE>
+__global__ __launch_bounds__(1024) void route_block_kernel(
+    const Id *__restrict__ ids, int64_t TK, int E, int nbits, int RC, int NB, int BM,
+    const int32_t *__restrict__ hist, const int32_t *__restrict__ bad,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ mtile_off,
+    int32_t *__restrict__ mtile_expert, int32_t *__restrict__ status, int32_t *__restrict__ ctr,
+    int nctr, SavedHeader *__restrict__ hdr, uint64_t problem_hash,
+    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_pos)
+{
+    extern __shared__ int32_t lds[];
+    int32_t *tab = lds;         // [E][16]: chunk counts, then chunk bases
+    int32_t *tot = tab + E * 16; // [E]: slots of expert e over all chunks
+    int32_t *bef = tot + E;      // [E]: slots of expert e in chunks before this block's
+    __shared__ int32_t s_w[40];
+    __shared__ int32_t s_moff[1025];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int b0 = blockIdx.x * 16;
+    const bool lead = blockIdx.x == 0;
+    if (lead)
+        write_header_and_counters(hdr, problem_hash, ctr, nctr);
+    int anybad = 0;
+    if constexpr (ONE) {
+        for (int i = threadIdx.x; i < E * 16; i += 1024)
+            tab[i] = 0;
+        __syncthreads();
+        const int64_t s0 = (int64_t)wave * RC;
+        const int64_t s1 = s0 + RC < TK ? s0 + RC : TK;
+        for (int64_t r0 = s0; r0 < s1; r0 += 512) {
+            int64_t v[8];
+            load_ids8(ids, r0, s1, v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t e = v[j];
+                if (r0 + 64 * j + lane >= s1)
+                    continue;
+                if (e >= 0 && e < E)
+                    atomicAdd(&tab[e * 16 + wave], 1);
+                else
+                    anybad = 1;
+            }
         }
-        const int rank = __popcll(m & lt);
-        int pos = 0;
-        if (valid) {
-            pos = base[e] + rank;
-            sorted_slot[pos] = (int32_t)s;
-            slot_pos[s] = pos;
-        } else if (in) {
-            slot_pos[s] = -1;
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += 1024) {
+            int32_t t = 0;
+#pragma unroll
+            for (int w = 0; w < 16; ++w)
+                t += tab[e * 16 + w];
+            tot[e] = t;
+            bef[e] = 0;
         }
-        // the lowest lane of each expert group advances that expert's base
-        // after every lane of the round has read it (LDS operations of one
-        // wave complete in program order)
-        if (valid && rank == 0)
-            base[e] = pos + __popcll(m);
+    } else {
+        // wave w reads the rows of experts w, w + 16, ...; the loads of one
+        // row segment are issued together, the sums are wave reductions
+        for (int e = wave; e < E; e += 16) {
+            const int32_t *row = hist + (int64_t)e * NB;
+            int32_t t = 0, bs = 0;
+            for (int j0 = 0; j0 < NB; j0 += 64) {
+                const int j = j0 + lane;
+                const int32_t v = j < NB ? row[j] : 0;
+                t += v;
+                bs += j < b0 ? v : 0;
+                if (j >= b0 && j < b0 + 16)
+                    tab[e * 16 + (j - b0)] = v;
+            }
+            if (lane < 16 && b0 + lane >= NB)
+                tab[e * 16 + lane] = 0;
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) {
+                t += __shfl_xor(t, d, 64);
+                bs += __shfl_xor(bs, d, 64);
+            }
+            if (lane == 0) {
+                tot[e] = t;
+                bef[e] = bs;
+            }
+        }
+        if (lead)
+            for (int j = threadIdx.x; j < NB; j += 1024)
+                anybad |= bad[j];
+    }
+    anybad = __syncthreads_or(anybad);
+
+    const int e = threadIdx.x; // E <= 1024
+    const int32_t c = e < E ? tot[e] : 0;
+    int32_t total;
+    const int32_t off = block_excl_scan(c, s_w, &total);
+    if (lead)
+        publish_plan(c, off, total, anybad, E, BM, counts, offsets, mtile_off, mtile_expert,
+                     status, s_w, s_moff);
+    if (e < E) {
+        int32_t run = off + bef[e];
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+            const int32_t v = tab[e * 16 + w];
+            tab[e * 16 + w] = run;
+            run += v;
+        }
+    }
+    __syncthreads();
+    const int b = b0 + wave;
+    if (b < NB) {
+        const int64_t s0 = (int64_t)b * RC;
+        const int64_t s1 = s0 + RC < TK ? s0 + RC : TK;
+        scatter_chunk(ids, s0, s1, E, nbits, tab + wave, 16, sorted_slot, slot_pos);
     }
 }
 
@@ -309,32 +501,54 @@ RoutePlan make_route_plan(int64_t TK, int E)
     return rp;
 }
 
-hipError_t launch_route(const void *ids, bool ids64, int64_t TK, int E, int BM,
-                        const RoutePlan &rp, const RouteBufs &rb, hipStream_t stream)
+template <typename Id>
+static void launch_route_t(const Id *ids, int64_t TK, int E, int BM, const RoutePlan &rp,
+                           const RouteBufs &rb, hipStream_t stream)
 {
     const size_t lds = sizeof(int32_t) * (size_t)E;
-    if (TK > 0) {
-        if (ids64)
-            hipLaunchKernelGGL(route_hist_kernel<int64_t>, dim3(rp.NB), dim3(64), lds, stream,
-                               (const int64_t *)ids, TK, E, rp.RC, rp.NB, rb.hist, rb.bad);
+    const size_t lds_block = sizeof(int32_t) * (size_t)E * 18; // tab[E][16], tot[E], bef[E]
+    const int nctr = rb.ctr ? rb.nctr : 0;
+    if (TK > 0 && lds_block <= 65536) {
+        if (rp.NB > 16)
+            hipLaunchKernelGGL(route_hist_kernel<Id>, dim3(rp.NB), dim3(64), lds, stream, ids, TK, E,
+                               rp.RC, rp.NB, rb.hist, rb.bad);
+        const int nblk = (rp.NB + 15) / 16;
+        if (nblk == 1)
+            hipLaunchKernelGGL((route_block_kernel<Id, true>), dim3(1), dim3(1024), lds_block, stream,
+                               ids, TK, E, rp.nbits, rp.RC, rp.NB, BM, rb.hist, rb.bad, rb.counts,
+                               rb.offsets, rb.mtile_off, rb.mtile_expert, rb.status, rb.ctr, nctr,
+                               rb.saved_hdr, rb.problem_hash, rb.sorted_slot, rb.slot_pos);
         else
-            hipLaunchKernelGGL(route_hist_kernel<int32_t>, dim3(rp.NB), dim3(64), lds, stream,
-                               (const int32_t *)ids, TK, E, rp.RC, rp.NB, rb.hist, rb.bad);
+            hipLaunchKernelGGL((route_block_kernel<Id, false>), dim3(nblk), dim3(1024), lds_block,
+                               stream, ids, TK, E, rp.nbits, rp.RC, rp.NB, BM, rb.hist, rb.bad,
+                               rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert, rb.status,
+                               rb.ctr, nctr, rb.saved_hdr, rb.problem_hash, rb.sorted_slot,
+                               rb.slot_pos);
+        return;
     }
+    // many experts (the block table would not fit), or no slots: hist, scan, scatter
+    if (TK > 0)
+        hipLaunchKernelGGL(route_hist_kernel<Id>, dim3(rp.NB), dim3(64), lds, stream, ids, TK, E,
+                           rp.RC, rp.NB, rb.hist, rb.bad);
     const int nb_scan = TK > 0 ? rp.NB : 0;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, rb.hist, rb.bad, E,
                        nb_scan, BM, rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert,
-                       rb.status, rb.ctr, rb.ctr ? rb.nctr : 0, rb.saved_hdr, rb.problem_hash);
-    if (TK > 0) {
-        if (ids64)
-            hipLaunchKernelGGL(route_scatter_kernel<int64_t>, dim3(rp.NB), dim3(64), lds, stream,
-                               (const int64_t *)ids, TK, E, rp.nbits, rp.RC, rp.NB, rb.hist,
-                               rb.offsets, rb.sorted_slot, rb.slot_pos);
-        else
-            hipLaunchKernelGGL(route_scatter_kernel<int32_t>, dim3(rp.NB), dim3(64), lds, stream,
-                               (const int32_t *)ids, TK, E, rp.nbits, rp.RC, rp.NB, rb.hist,
-                               rb.offsets, rb.sorted_slot, rb.slot_pos);
-    }
+                       rb.status, rb.ctr, nctr, rb.saved_hdr, rb.problem_hash);
+    if (TK > 0)
+        hipLaunchKernelGGL(route_scatter_kernel<Id>, dim3(rp.NB), dim3(64), lds, stream, ids, TK, E,
+                           rp.nbits, rp.RC, rp.NB, rb.hist, rb.offsets, rb.sorted_slot,
+                           rb.slot_pos);
+}
+
+// One launch when the slots fit 16 chunks, two (hist, block) otherwise, three
+// (hist, scan, scatter) when an expert table of 18 x E words would not fit 64 KB.
+hipError_t launch_route(const void *ids, bool ids64, int64_t TK, int E, int BM,
+                        const RoutePlan &rp, const RouteBufs &rb, hipStream_t stream)
+{
+    if (ids64)
+        launch_route_t((const int64_t *)ids, TK, E, BM, rp, rb, stream);
+    else
+        launch_route_t((const int32_t *)ids, TK, E, BM, rp, rb, stream);
     return hipGetLastError();
 }
 

@@ -44,11 +44,21 @@ def ids_case(name):
         return make_routing(w)[0], 32
     if name == "big_many_chunks":
         return rng.integers(0, 64, size=(40000, 6)).astype(np.int32), 64
+    # launch-shape boundaries: 16 chunks of 512 slots are one block, 17 are two
+    if name == "chunks16":
+        return rng.integers(0, 40, size=(1024, 8)).astype(np.int32), 40
+    if name == "chunks17_i64":
+        return rng.integers(0, 40, size=(1025, 8)).astype(np.int64), 40
+    if name == "e900_one_block":
+        return rng.integers(0, 900, size=(900, 8)).astype(np.int32), 900
+    if name == "e1024_many_chunks":
+        return rng.integers(0, 1024, size=(3000, 8)).astype(np.int32), 1024
     raise KeyError(name)
 
 
 CASES = ["uniform", "k1", "t1", "t63", "t65", "all_one", "empty_ends", "e1", "e1024",
-         "dups_i64", "zipf_t8191", "big_many_chunks"]
+         "dups_i64", "zipf_t8191", "big_many_chunks", "chunks16", "chunks17_i64",
+         "e900_one_block", "e1024_many_chunks"]
 
 
 @pytest.mark.parametrize("name", CASES)
@@ -91,6 +101,27 @@ def test_route_flags_out_of_range_ids_without_writing_out_of_bounds(gpu_lib):
     assert n_valid == ids.size - 2
     want_sorted = np.nonzero(good)[0][np.argsort(flat[good], kind="stable")]
     np.testing.assert_array_equal(ss.cpu().numpy()[:n_valid], want_sorted)
+
+
+@pytest.mark.parametrize("dtype", [np.int32, np.int64])
+def test_route_flags_bad_ids_in_multi_block_launch(gpu_lib, dtype):
+    # more than 16 chunks: the bad-id flags of every chunk reach the status word
+    rng = np.random.default_rng(7)
+    ids = rng.integers(0, 24, size=(3000, 4)).astype(dtype)
+    ids[2999, 3] = 24
+    ids[1500, 0] = -1
+    say(f"[route] bad ids, multi-block, {np.dtype(dtype).name}")
+    counts, offsets, ss, sp, ws = gpu_lib.moe_ffn_route(torch.from_numpy(ids).cuda(), 24)
+    assert gpu_lib.read_status(ws) == 1
+    flat = ids.ravel()
+    good = (flat >= 0) & (flat < 24)
+    sp = sp.cpu().numpy()
+    assert (sp[~good] == -1).all()
+    n_valid = int(offsets.cpu()[-1])
+    assert n_valid == int(good.sum())
+    want_sorted = np.nonzero(good)[0][np.argsort(flat[good], kind="stable")]
+    np.testing.assert_array_equal(ss.cpu().numpy()[:n_valid], want_sorted)
+    np.testing.assert_array_equal(sp[want_sorted], np.arange(n_valid))
 
 
 def test_route_is_deterministic(gpu_lib):
