@@ -107,6 +107,10 @@ template <int BM_, int NW_ = 8> struct Cfg {
 
 __device__ __forceinline__ int bswz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
 
+template <int N> struct IC {
+    static constexpr int value = N;
+};
+
 // swizzled 16-byte piece of A row r: rows of 8 pieces (128 B) XOR by
 // (r / 2) % 8, rows of 4 pieces (64 B) by (r / 4) % 4, so the 16 rows that one
 // 128-bit fragment read touches fall in 16 different bank groups
@@ -393,15 +397,23 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
     // pipe and the matrix cores are close to balanced, so the order is pinned:
     // the first MFMA group's operands, then one read per MFMA until all reads
     // are out, then the remaining MFMAs.
-    auto compute = [&](const unsigned char *sA) {
+    //
+    // FMA (a compile-time count, fma_c's value) is the number of this wave's
+    // 16-row blocks the step computes: a tile whose rows end early (the last
+    // M-tile of an expert) reads and multiplies only the blocks that hold
+    // rows, rounded up to an even count; the others keep their zeros and are
+    // never stored.
+    auto compute = [&](auto fma_c, const unsigned char *sA) {
+        constexpr int FMA = decltype(fma_c)::value;
+        static_assert(FMA >= 1 && FMA <= C::FM, "active row blocks");
         const unsigned char *sB = sA + C::A_BYTES;
-        bf16x8 af[C::KH][C::FM];
+        bf16x8 af[C::KH][FMA];
         bf16x8 bfr[C::KH][2][C::FN]; // [k half][panel][16-column block]
 #pragma unroll
         for (int h2 = 0; h2 < C::KH; ++h2) {
             const int kk = h2 * 32;
 #pragma unroll
-            for (int fm = 0; fm < C::FM; ++fm) {
+            for (int fm = 0; fm < FMA; ++fm) {
                 const int r = wm * C::WTM + fm * 16 + fr;
                 const int piece = aswz<C::PIECES>(r, (kk >> 3) + fk);
                 af[h2][fm] = *reinterpret_cast<const bf16x8 *>(sA + r * (BK * 2) + piece * 16);
@@ -432,11 +444,11 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
 #pragma unroll
                 for (int fn = 0; fn < C::FN; ++fn)
 #pragma unroll
-                    for (int fm = 0; fm < C::FM; ++fm)
+                    for (int fm = 0; fm < FMA; ++fm)
                         acc[p][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             bfr[h2][p][fn], af[h2][fm], acc[p][fm][fn], 0, 0, 0);
-        constexpr int NDS = C::KH * (C::FM + 4 * C::FN), NMF = C::KH * 2 * C::FN * C::FM;
-        constexpr int FIRST = C::FM + 2, PAIRS = NDS - FIRST;
+        constexpr int NDS = C::KH * (FMA + 4 * C::FN), NMF = C::KH * 2 * C::FN * FMA;
+        constexpr int FIRST = FMA + 2, PAIRS = NDS - FIRST;
         static_assert(PAIRS <= NMF, "read schedule");
         __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
 #pragma unroll
@@ -547,8 +559,10 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
         int owed = -1; // release of the previous tile, made once its stores are done
         while (true) {
             const int nk = (kind_of(cur.kind) == KIND_G1 ? H : I) / BK;
-            // a wave whose rows all lie past the expert's count skips the MFMAs
+            // a wave whose rows all lie past the expert's count skips the MFMAs;
+            // fmv = its 16-row blocks that hold rows
             const bool active = wm * C::WTM < cur.rows;
+            const int fmv = min(C::FM, (cur.rows - wm * C::WTM + 15) >> 4);
 #pragma unroll
             for (int p = 0; p < 2; ++p)
 #pragma unroll
@@ -556,6 +570,9 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
 #pragma unroll
                     for (int fn = 0; fn < C::FN; ++fn)
                         acc[p][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // the K loop of the tile, instantiated once per count of active row
+            // blocks (a wave-uniform choice made per tile, outside the loop)
+            auto kloop = [&](auto fma_c) {
             for (int kb = 0; kb < nk; ++kb) {
                 // wait for this wave's copies of the current step (copy groups
                 // issued after it may stay in flight), publish the stage, then
@@ -586,8 +603,26 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
                     issue(snext, step - nk, smem + s_next * C::STAGE_BYTES);
                 }
                 if (active)
-                    compute(smem + s_cur * C::STAGE_BYTES);
+                    compute(fma_c, smem + s_cur * C::STAGE_BYTES);
                 s_cur = s_cur == NSTAGE - 1 ? 0 : s_cur + 1;
+            }
+            };
+            if constexpr (C::FM == 8) {
+                if (fmv > 6)
+                    kloop(IC<8>{});
+                else if (fmv > 4)
+                    kloop(IC<6>{});
+                else if (fmv > 2)
+                    kloop(IC<4>{});
+                else
+                    kloop(IC<2>{});
+            } else if constexpr (C::FM == 4) {
+                if (fmv > 2)
+                    kloop(IC<4>{});
+                else
+                    kloop(IC<2>{});
+            } else {
+                kloop(IC<C::FM>{});
             }
             epilogue(cur);
             const int done = release_index(cur);
