@@ -108,6 +108,8 @@ typedef struct {
 #define MOE_FFN_DEV_BAD_ID 0x1    /* an expert id was outside [0, E); its slot was dropped */
 #define MOE_FFN_DEV_TIMEOUT 0x2   /* a pipelined wait hit the watchdog; outputs are unreliable */
 #define MOE_FFN_DEV_BAD_SAVED 0x4 /* bwd: the saved context did not belong to this problem */
+#define MOE_FFN_DEV_BAD_WS 0x8    /* bwd_w: the workspace did not hold moe_ffn_bwd_d's result for
+                                     this saved context; the weight gradients were zeroed */
 
 /* Stages of the forward, for the timing hook below. */
 enum {
@@ -205,12 +207,40 @@ int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, cons
                    void *ws, size_t ws_bytes, uint32_t flags, void *stream,
                    const moe_ffn_stage_events *ev);
 
+/* The backward split into its two halves (EP overlap page, section 2.3
+ * "W/D split + deferred W queue" and section 4.5's interface draft: a
+ * D-only entry that yields the input gradient, and a W-only entry that a
+ * scheduler can defer into an idle window).  Together they compute exactly
+ * what moe_ffn_bwd computes, bit for bit.
+ *
+ * moe_ffn_bwd_d: dx [T, H] and d_topk_weights [T, K] (fp32), from dy, the
+ * gates, both weight tensors and `saved`.  It leaves in `ws` (sized by
+ * moe_ffn_bwd_workspace_size) the intermediate gradients the weight half
+ * reads, stamped with the saved context's identity; the caller must keep
+ * `ws` untouched until the matching moe_ffn_bwd_w has been issued.
+ *
+ * moe_ffn_bwd_w: d_up_proj_weight [E, H, 2I] and d_down_proj_weight [E, I, H],
+ * from dy, x, the same `saved` and the `ws` of the moe_ffn_bwd_d call, issued
+ * after it on the same stream (or after an event recorded behind it).  If `ws`
+ * does not carry the stamp of that `saved` context, nothing is read from it:
+ * the weight gradients are written as zeros and the workspace status word
+ * gets MOE_FFN_DEV_BAD_WS (with MOE_FFN_CHECK_SAVED the call returns
+ * MOE_FFN_ERR_SAVED before launching instead).  Outputs are overwritten, not
+ * accumulated.  Pointer, size and error rules are those of moe_ffn_bwd. */
+int moe_ffn_bwd_d(const moe_ffn_problem *p, const void *dy, const float *topk_weights,
+                  const void *up_proj_weight, const void *down_proj_weight, const void *saved,
+                  void *dx, float *d_topk_weights, void *ws, size_t ws_bytes, uint32_t flags,
+                  void *stream);
+int moe_ffn_bwd_w(const moe_ffn_problem *p, const void *dy, const void *x, const void *saved,
+                  void *d_up_proj_weight, void *d_down_proj_weight, void *ws, size_t ws_bytes,
+                  uint32_t flags, void *stream);
+
 /* ---- status and measurement helpers ---------------------------------------- */
 
 /* Synchronises `stream`, then reads the device status word that the last
  * forward, route or backward call on this workspace left: 0, or an OR of
  * MOE_FFN_DEV_BAD_ID and MOE_FFN_DEV_TIMEOUT (forward, route) or
- * MOE_FFN_DEV_BAD_SAVED (backward). */
+ * MOE_FFN_DEV_BAD_SAVED, MOE_FFN_DEV_BAD_WS (backward). */
 int moe_ffn_read_status(const void *ws, void *stream, int32_t *device_status);
 
 /* Static text for a status code. */

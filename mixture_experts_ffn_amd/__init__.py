@@ -38,6 +38,8 @@ __all__ = [
     "STAGES",
     "BWD_STAGES",
     "bwd_workspace_size",
+    "moe_ffn_bwd_d",
+    "moe_ffn_bwd_w",
     "moe_ffn_bwd",
     "moe_ffn",
     "MoEFFNFunction",
@@ -54,7 +56,7 @@ CHECK_IDS = 0x1
 PIPELINE = 0x2
 TEST_DROP_RELEASE = 0x100
 CHECK_SAVED = 0x4
-DEV_BAD_ID, DEV_TIMEOUT, DEV_BAD_SAVED = 0x1, 0x2, 0x4
+DEV_BAD_ID, DEV_TIMEOUT, DEV_BAD_SAVED, DEV_BAD_WS = 0x1, 0x2, 0x4, 0x8
 STAGES = ("route", "gemm1", "gemm2", "combine", "pipeline")
 BWD_STAGES = ("act_grad", "input_grad", "dx_combine", "w2_grad", "w1_grad")
 
@@ -106,6 +108,8 @@ def load_library():
             "moe_ffn_bwd": [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
             "moe_ffn_bwd_ex": [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp,
                                ctypes.POINTER(StageEvents)],
+            "moe_ffn_bwd_d": [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
+            "moe_ffn_bwd_w": [pp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
             "moe_ffn_route": [pp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_ffn_read_status": [vp, vp, ctypes.POINTER(ctypes.c_int32)],
             "moe_ffn_event_create": [ctypes.POINTER(ctypes.c_void_p)],
@@ -283,6 +287,56 @@ def moe_ffn_bwd(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
     if return_ws:
         return dx, d_up, d_down, d_topk, ws
     return dx, d_up, d_down, d_topk
+
+
+def moe_ffn_bwd_d(dy, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved, *,
+                  ws=None, check_saved: bool = False):
+    """Data half of the backward: (dx, d_topk_weights, ws).
+
+    `ws` then holds the intermediate gradients that ``moe_ffn_bwd_w`` reads; keep it
+    untouched until that call has been issued on the same stream.
+    """
+    lib = load_library()
+    _require_gpu(dy, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved)
+    prob = make_problem(dy, topk_ids, up_proj_weight, down_proj_weight)
+    ws_bytes = bwd_workspace_size(prob)
+    dev = dy.device
+    dx = torch.empty_like(dy)
+    d_topk = torch.empty(topk_ids.shape, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    flags = CHECK_SAVED if check_saved else 0
+    with torch.cuda.device(dev):
+        rc = lib.moe_ffn_bwd_d(ctypes.byref(prob), _ptr(dy), _ptr(topk_weights),
+                               _ptr(up_proj_weight), _ptr(down_proj_weight), _ptr(saved), _ptr(dx),
+                               _ptr(d_topk), _ptr(ws), ws.numel(), flags, _stream(dev))
+    _check(rc)
+    return dx, d_topk, ws
+
+
+def moe_ffn_bwd_w(dy, x, topk_ids, up_proj_weight, down_proj_weight, saved, ws, *,
+                  check_saved: bool = False):
+    """Weight half of the backward: (d_up_proj_weight, d_down_proj_weight).
+
+    `ws` must be the workspace of the ``moe_ffn_bwd_d`` call for the same `saved`
+    context; otherwise the gradients are zeros and ``read_status(ws)`` has DEV_BAD_WS
+    (with ``check_saved`` the call raises instead).  topk_ids and the weights only
+    describe the problem's shape here.
+    """
+    lib = load_library()
+    _require_gpu(dy, x, topk_ids, saved, ws)
+    prob = make_problem(x, topk_ids, up_proj_weight, down_proj_weight)
+    if dy.shape != x.shape or dy.dtype != x.dtype:
+        raise MoEFFNError(2, "dy must have the shape and dtype of x")
+    dev = x.device
+    d_up = torch.empty_like(up_proj_weight)
+    d_down = torch.empty_like(down_proj_weight)
+    flags = CHECK_SAVED if check_saved else 0
+    with torch.cuda.device(dev):
+        rc = lib.moe_ffn_bwd_w(ctypes.byref(prob), _ptr(dy), _ptr(x), _ptr(saved), _ptr(d_up),
+                               _ptr(d_down), _ptr(ws), ws.numel(), flags, _stream(dev))
+    _check(rc)
+    return d_up, d_down
 
 
 class MoEFFNFunction(torch.autograd.Function):

@@ -10,6 +10,7 @@
 // shows why per-call context must not live in the operator).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -21,10 +22,13 @@
 static_assert(moe::MOE_DEV_BAD_ID == MOE_FFN_DEV_BAD_ID, "status bits");
 static_assert(moe::MOE_DEV_TIMEOUT == MOE_FFN_DEV_TIMEOUT, "status bits");
 static_assert(moe::MOE_DEV_BAD_SAVED == MOE_FFN_DEV_BAD_SAVED, "status bits");
+static_assert(moe::MOE_DEV_BAD_WS == MOE_FFN_DEV_BAD_WS, "status bits");
 
 namespace {
 
 thread_local char g_err[512];
+// epoch stamped into every saved context (distinct per forward that saves one)
+std::atomic<uint64_t> g_epoch{1};
 
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char *fmt, ...)
@@ -234,7 +238,7 @@ struct BwdLayout {
     int BM;
     int64_t max_mtiles;
     int dgp_width;
-    size_t status, counts, offsets, mtile_off, mtile_expert, dh, act_g, dgp, dxp, total;
+    size_t status, whdr, counts, offsets, mtile_off, mtile_expert, dh, act_g, dgp, dxp, total;
 };
 
 BwdLayout bwd_layout(const moe_ffn_problem &p)
@@ -252,6 +256,7 @@ BwdLayout bwd_layout(const moe_ffn_problem &p)
         return at;
     };
     B.status = take(sizeof(int32_t));
+    B.whdr = take(sizeof(moe::SavedHeader));
     B.counts = take(sizeof(int32_t) * (size_t)E);
     B.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
     B.mtile_off = take(sizeof(int32_t) * (size_t)(E + 1));
@@ -353,6 +358,7 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
     rb.nctr = (int)(2 * L.max_mtiles);
     rb.saved_hdr = saved ? at<moe::SavedHeader>(saved, L.s_hdr) : nullptr;
     rb.problem_hash = problem_hash(*p);
+    rb.epoch = saved ? g_epoch.fetch_add(1) : 0;
     if (saved) {
         rb.counts = at<int32_t>(saved, L.s_counts);
         rb.offsets = at<int32_t>(saved, L.s_offsets);
@@ -554,6 +560,7 @@ int moe_ffn_route(const moe_ffn_problem *p, const void *topk_ids, int32_t *count
     rb.nctr = 0;
     rb.saved_hdr = nullptr;
     rb.problem_hash = 0;
+    rb.epoch = 0;
     rb.hist = at<int32_t>(ws, R.hist);
     rb.bad = at<int32_t>(ws, R.bad);
     rb.mtile_off = at<int32_t>(ws, R.mtile_off);
@@ -583,7 +590,10 @@ int moe_ffn_bwd_workspace_size(const moe_ffn_problem *p, uint32_t flags, size_t 
     return MOE_FFN_OK;
 }
 
-int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, const void *topk_ids,
+// The backward, whole (BWD_STAGE_ALL) or one of its two stages: D computes
+// act_grad, input_grad and the dx / d_topk combine and leaves dh and act_g in
+// the workspace; W computes the weight gradients from them.
+static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const void *x,
                    const float *topk_weights, const void *up_proj_weight,
                    const void *down_proj_weight, const void *saved, void *dx,
                    void *d_up_proj_weight, void *d_down_proj_weight, float *d_topk_weights,
@@ -596,20 +606,21 @@ int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, cons
         return rc;
     if (p->dtype != MOE_FFN_BF16)
         return fail(MOE_FFN_ERR_DTYPE, "the backward supports bf16 problems only");
+    const bool do_d = stage != moe::BWD_STAGE_W, do_w = stage != moe::BWD_STAGE_D;
     const BwdLayout B = bwd_layout(*p);
     const FwdLayout L = fwd_layout(*p);
-    if ((rc = check_ptr(d_up_proj_weight, "d_up_proj_weight")) ||
-        (rc = check_ptr(d_down_proj_weight, "d_down_proj_weight")))
+    if (do_w && ((rc = check_ptr(d_up_proj_weight, "d_up_proj_weight")) ||
+                 (rc = check_ptr(d_down_proj_weight, "d_down_proj_weight"))))
         return rc;
-    const size_t id_align = p->ids_dtype == MOE_FFN_I64 ? 8 : 4;
     if (p->T > 0 &&
-        ((rc = check_ptr(dy, "dy")) || (rc = check_ptr(x, "x")) ||
-         (rc = check_ptr(topk_ids, "topk_ids", id_align)) ||
-         (rc = check_ptr(topk_weights, "topk_weights", 4)) ||
-         (rc = check_ptr(up_proj_weight, "up_proj_weight")) ||
-         (rc = check_ptr(down_proj_weight, "down_proj_weight")) ||
-         (rc = check_ptr(saved, "saved")) || (rc = check_ptr(dx, "dx")) ||
-         (rc = check_ptr(d_topk_weights, "d_topk_weights", 4)) || (rc = check_ptr(ws, "ws"))))
+        ((rc = check_ptr(dy, "dy")) || (rc = check_ptr(saved, "saved")) ||
+         (rc = check_ptr(ws, "ws")) ||
+         (do_d && ((rc = check_ptr(topk_weights, "topk_weights", 4)) ||
+                   (rc = check_ptr(up_proj_weight, "up_proj_weight")) ||
+                   (rc = check_ptr(down_proj_weight, "down_proj_weight")) ||
+                   (rc = check_ptr(dx, "dx")) ||
+                   (rc = check_ptr(d_topk_weights, "d_topk_weights", 4)))) ||
+         (do_w && (rc = check_ptr(x, "x")))))
         return rc;
     if (p->T > 0 && ws_bytes < B.total)
         return fail(MOE_FFN_ERR_WORKSPACE, "workspace too small: %zu < %zu", ws_bytes, B.total);
@@ -620,22 +631,33 @@ int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, cons
     const size_t dw_bytes = 2 * (size_t)p->E * (size_t)p->H * (size_t)p->I;
     if (p->T == 0) {
         // no slot reached any expert: the weight gradients are exactly zero
-        HIP_TRY(moe::launch_zero_fill(d_up_proj_weight, 2 * dw_bytes, s), "zero fill");
-        HIP_TRY(moe::launch_zero_fill(d_down_proj_weight, dw_bytes, s), "zero fill");
+        if (do_w) {
+            HIP_TRY(moe::launch_zero_fill(d_up_proj_weight, 2 * dw_bytes, s), "zero fill");
+            HIP_TRY(moe::launch_zero_fill(d_down_proj_weight, dw_bytes, s), "zero fill");
+        }
         return MOE_FFN_OK;
     }
     const int E = (int)p->E, I = (int)p->I, H = (int)p->H;
     void *sv = const_cast<void *>(saved);
     const moe::SavedHeader *hdr = at<moe::SavedHeader>(sv, L.s_hdr);
+    moe::SavedHeader *whdr = at<moe::SavedHeader>(ws, B.whdr);
     const uint64_t phash = problem_hash(*p);
     if (flags & MOE_FFN_CHECK_SAVED) {
-        moe::SavedHeader h_host{};
+        moe::SavedHeader h_host{}, w_host{};
         HIP_TRY(hipMemcpyAsync(&h_host, hdr, sizeof h_host, hipMemcpyDeviceToHost, s),
                 "saved header copy");
+        if (stage == moe::BWD_STAGE_W)
+            HIP_TRY(hipMemcpyAsync(&w_host, whdr, sizeof w_host, hipMemcpyDeviceToHost, s),
+                    "workspace header copy");
         HIP_TRY(hipStreamSynchronize(s), "stream sync");
         if (h_host.magic != moe::kSavedMagic || h_host.version != moe::kSavedVersion ||
             h_host.problem != phash)
             return fail(MOE_FFN_ERR_SAVED, "saved context was not written by a forward of this problem");
+        if (stage == moe::BWD_STAGE_W &&
+            (w_host.magic != h_host.magic || w_host.version != h_host.version ||
+             w_host.problem != h_host.problem || w_host.epoch != h_host.epoch))
+            return fail(MOE_FFN_ERR_SAVED,
+                        "workspace does not hold the data-gradient stage of this saved context");
     }
     const int32_t *saved_counts = at<int32_t>(sv, L.s_counts);
     const int32_t *saved_offsets = at<int32_t>(sv, L.s_offsets);
@@ -653,7 +675,8 @@ int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, cons
     moe::bf16_t *dxp = at<moe::bf16_t>(ws, B.dxp);
 
     HIP_TRY(moe::launch_bwd_setup(hdr, phash, saved_counts, saved_offsets, E, p->T * p->K, B.BM,
-                                  counts, offsets, mtile_off, mtile_expert, bstatus, s),
+                                  counts, offsets, mtile_off, mtile_expert, bstatus, whdr, stage,
+                                  s),
             "backward set-up launch");
     (void)counts;
 
@@ -665,73 +688,95 @@ int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, cons
     base.topk = (int)p->K;
     base.E = E;
 
-    // act_grad with the SwiGLU backward in its epilogue: dh, act_g, d_g partials
-    moe::EngineArgs a2 = base;
-    a2.A = static_cast<const moe::bf16_t *>(dy);
-    a2.B = static_cast<const moe::bf16_t *>(down_proj_weight);
-    a2.C = dh;
-    a2.C2 = act_g;
-    a2.Hs = h;
-    a2.gates = topk_weights;
-    a2.dgp = dgp;
-    a2.dgp_stride = B.dgp_width;
-    a2.N = I;
-    a2.Kd = H;
-    a2.lda = H;
-    a2.ldb = H;
-    a2.b_estride = (int64_t)I * H;
-    record(ev, MOE_FFN_STAGE_BWD_ACT_GRAD, true, s);
-    HIP_TRY(moe::launch_engine(moe::ENG_B2, B.BM, a2, num_cus, s), "act_grad launch");
-    record(ev, MOE_FFN_STAGE_BWD_ACT_GRAD, false, s);
+    if (do_d) {
+        // act_grad with the SwiGLU backward in its epilogue: dh, act_g, d_g partials
+        moe::EngineArgs a2 = base;
+        a2.A = static_cast<const moe::bf16_t *>(dy);
+        a2.B = static_cast<const moe::bf16_t *>(down_proj_weight);
+        a2.C = dh;
+        a2.C2 = act_g;
+        a2.Hs = h;
+        a2.gates = topk_weights;
+        a2.dgp = dgp;
+        a2.dgp_stride = B.dgp_width;
+        a2.N = I;
+        a2.Kd = H;
+        a2.lda = H;
+        a2.ldb = H;
+        a2.b_estride = (int64_t)I * H;
+        record(ev, MOE_FFN_STAGE_BWD_ACT_GRAD, true, s);
+        HIP_TRY(moe::launch_engine(moe::ENG_B2, B.BM, a2, num_cus, s), "act_grad launch");
+        record(ev, MOE_FFN_STAGE_BWD_ACT_GRAD, false, s);
 
-    // input_grad: dx_perm = dh W1[e]^T
-    moe::EngineArgs a4 = base;
-    a4.A = dh;
-    a4.B = static_cast<const moe::bf16_t *>(up_proj_weight);
-    a4.C = dxp;
-    a4.N = H;
-    a4.Kd = 2 * I;
-    a4.lda = 2 * I;
-    a4.ldb = 2 * I;
-    a4.ldc = H;
-    a4.b_estride = (int64_t)H * 2 * I;
-    record(ev, MOE_FFN_STAGE_BWD_INPUT_GRAD, true, s);
-    HIP_TRY(moe::launch_engine(moe::ENG_B4, B.BM, a4, num_cus, s), "input_grad launch");
-    record(ev, MOE_FFN_STAGE_BWD_INPUT_GRAD, false, s);
+        // input_grad: dx_perm = dh W1[e]^T
+        moe::EngineArgs a4 = base;
+        a4.A = dh;
+        a4.B = static_cast<const moe::bf16_t *>(up_proj_weight);
+        a4.C = dxp;
+        a4.N = H;
+        a4.Kd = 2 * I;
+        a4.lda = 2 * I;
+        a4.ldb = 2 * I;
+        a4.ldc = H;
+        a4.b_estride = (int64_t)H * 2 * I;
+        record(ev, MOE_FFN_STAGE_BWD_INPUT_GRAD, true, s);
+        HIP_TRY(moe::launch_engine(moe::ENG_B4, B.BM, a4, num_cus, s), "input_grad launch");
+        record(ev, MOE_FFN_STAGE_BWD_INPUT_GRAD, false, s);
 
-    record(ev, MOE_FFN_STAGE_BWD_COMBINE, true, s);
-    HIP_TRY(moe::launch_combine_bwd(dxp, dgp, B.dgp_width, slot_pos, bstatus, dx, d_topk_weights,
-                                    p->T, H, (int)p->K, s),
-            "dx combine launch");
-    record(ev, MOE_FFN_STAGE_BWD_COMBINE, false, s);
+        record(ev, MOE_FFN_STAGE_BWD_COMBINE, true, s);
+        HIP_TRY(moe::launch_combine_bwd(dxp, dgp, B.dgp_width, slot_pos, bstatus, dx,
+                                        d_topk_weights, p->T, H, (int)p->K, s),
+                "dx combine launch");
+        record(ev, MOE_FFN_STAGE_BWD_COMBINE, false, s);
+    }
+    if (do_w) {
+        // W2Grad: dW2[e] = act_g^T dY_perm
+        moe::EngineArgs a5 = base;
+        a5.A = act_g;
+        a5.B = static_cast<const moe::bf16_t *>(dy);
+        a5.C = static_cast<moe::bf16_t *>(d_down_proj_weight);
+        a5.M = I;
+        a5.N = H;
+        a5.lda = I;
+        a5.ldb = H;
+        record(ev, MOE_FFN_STAGE_BWD_W2_GRAD, true, s);
+        HIP_TRY(moe::launch_engine(moe::ENG_B5, B.BM, a5, num_cus, s), "W2Grad launch");
+        record(ev, MOE_FFN_STAGE_BWD_W2_GRAD, false, s);
 
-    // W2Grad: dW2[e] = act_g^T dY_perm
-    moe::EngineArgs a5 = base;
-    a5.A = act_g;
-    a5.B = static_cast<const moe::bf16_t *>(dy);
-    a5.C = static_cast<moe::bf16_t *>(d_down_proj_weight);
-    a5.M = I;
-    a5.N = H;
-    a5.lda = I;
-    a5.ldb = H;
-    record(ev, MOE_FFN_STAGE_BWD_W2_GRAD, true, s);
-    HIP_TRY(moe::launch_engine(moe::ENG_B5, B.BM, a5, num_cus, s), "W2Grad launch");
-    record(ev, MOE_FFN_STAGE_BWD_W2_GRAD, false, s);
-
-    // W1Grad: dW1[e] = x_perm^T dh
-    moe::EngineArgs a7 = base;
-    a7.A = static_cast<const moe::bf16_t *>(x);
-    a7.B = dh;
-    a7.C = static_cast<moe::bf16_t *>(d_up_proj_weight);
-    a7.M = H;
-    a7.N = 2 * I;
-    a7.lda = H;
-    a7.ldb = 2 * I;
-    record(ev, MOE_FFN_STAGE_BWD_W1_GRAD, true, s);
-    HIP_TRY(moe::launch_engine(moe::ENG_B7, B.BM, a7, num_cus, s), "W1Grad launch");
-    record(ev, MOE_FFN_STAGE_BWD_W1_GRAD, false, s);
-    (void)topk_ids;
+        // W1Grad: dW1[e] = x_perm^T dh
+        moe::EngineArgs a7 = base;
+        a7.A = static_cast<const moe::bf16_t *>(x);
+        a7.B = dh;
+        a7.C = static_cast<moe::bf16_t *>(d_up_proj_weight);
+        a7.M = H;
+        a7.N = 2 * I;
+        a7.lda = H;
+        a7.ldb = 2 * I;
+        record(ev, MOE_FFN_STAGE_BWD_W1_GRAD, true, s);
+        HIP_TRY(moe::launch_engine(moe::ENG_B7, B.BM, a7, num_cus, s), "W1Grad launch");
+        record(ev, MOE_FFN_STAGE_BWD_W1_GRAD, false, s);
+    }
     return MOE_FFN_OK;
+}
+
+int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, const void *topk_ids,
+                   const float *topk_weights, const void *up_proj_weight,
+                   const void *down_proj_weight, const void *saved, void *dx,
+                   void *d_up_proj_weight, void *d_down_proj_weight, float *d_topk_weights,
+                   void *ws, size_t ws_bytes, uint32_t flags, void *stream,
+                   const moe_ffn_stage_events *ev)
+{
+    // topk_ids is part of the signature the pages give the operator; the
+    // backward reads the routing the forward saved instead
+    const size_t id_align = p && p->ids_dtype == MOE_FFN_I64 ? 8 : 4;
+    if (p && p->T > 0) {
+        int rc = check_ptr(topk_ids, "topk_ids", id_align);
+        if (rc)
+            return rc;
+    }
+    return bwd_run(p, moe::BWD_STAGE_ALL, dy, x, topk_weights, up_proj_weight, down_proj_weight,
+                   saved, dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights, ws, ws_bytes,
+                   flags, stream, ev);
 }
 
 int moe_ffn_bwd(const moe_ffn_problem *p, const void *dy, const void *x, const void *topk_ids,
@@ -743,6 +788,25 @@ int moe_ffn_bwd(const moe_ffn_problem *p, const void *dy, const void *x, const v
     return moe_ffn_bwd_ex(p, dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
                           saved, dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights, ws,
                           ws_bytes, flags, stream, nullptr);
+}
+
+int moe_ffn_bwd_d(const moe_ffn_problem *p, const void *dy, const float *topk_weights,
+                  const void *up_proj_weight, const void *down_proj_weight, const void *saved,
+                  void *dx, float *d_topk_weights, void *ws, size_t ws_bytes, uint32_t flags,
+                  void *stream)
+{
+    return bwd_run(p, moe::BWD_STAGE_D, dy, nullptr, topk_weights, up_proj_weight,
+                   down_proj_weight, saved, dx, nullptr, nullptr, d_topk_weights, ws, ws_bytes,
+                   flags, stream, nullptr);
+}
+
+int moe_ffn_bwd_w(const moe_ffn_problem *p, const void *dy, const void *x, const void *saved,
+                  void *d_up_proj_weight, void *d_down_proj_weight, void *ws, size_t ws_bytes,
+                  uint32_t flags, void *stream)
+{
+    return bwd_run(p, moe::BWD_STAGE_W, dy, x, nullptr, nullptr, nullptr, saved, nullptr,
+                   d_up_proj_weight, d_down_proj_weight, nullptr, ws, ws_bytes, flags, stream,
+                   nullptr);
 }
 
 int moe_ffn_read_status(const void *ws, void *stream, int32_t *device_status)

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16 *__restrict
     const int64_t t = blockIdx.x;
     const int nch = H / 8;
     const int c = blockIdx.y * 256 + threadIdx.x;
-    const bool bad = status[0] & MOE_DEV_BAD_SAVED;
+    const bool bad = status[0] & (MOE_DEV_BAD_SAVED | MOE_DEV_BAD_WS);
     if (c < nch) {
         float acc[8];
 #pragma unroll

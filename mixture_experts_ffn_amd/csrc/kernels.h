@@ -11,13 +11,17 @@ typedef __bf16 bf16_t;
 // ---- routing -----------------------------------------------------------------
 // Header at the front of the saved context: the forward's routing step writes
 // it, the backward checks it before it trusts any of the saved arrays.
+// The backward's data-gradient stage copies it into its workspace, and the
+// weight-gradient stage, which reads that workspace, checks the copy against
+// the saved context it is given.
 struct SavedHeader {
     uint32_t magic;
     uint32_t version;
     uint64_t problem; // hash of (T, H, I, E, K, dtype, ids_dtype)
+    uint64_t epoch;   // distinct for every forward that saves a context
 };
 constexpr uint32_t kSavedMagic = 0x46454f4du; // "MOEF"
-constexpr uint32_t kSavedVersion = 1u;
+constexpr uint32_t kSavedVersion = 2u;
 
 struct RoutePlan {
     int RC;    // slots per chunk (one wave per chunk)
@@ -39,10 +43,11 @@ struct RouteBufs {
     int nctr;             // their number
     SavedHeader *saved_hdr; // optional: header of the saved context, written here
     uint64_t problem_hash;
+    uint64_t epoch;
 };
 
 // bits of the device status word
-enum { MOE_DEV_BAD_ID = 1, MOE_DEV_TIMEOUT = 2, MOE_DEV_BAD_SAVED = 4 };
+enum { MOE_DEV_BAD_ID = 1, MOE_DEV_TIMEOUT = 2, MOE_DEV_BAD_SAVED = 4, MOE_DEV_BAD_WS = 8 };
 
 
 RoutePlan make_route_plan(int64_t TK, int E);
@@ -144,7 +149,7 @@ hipError_t launch_combine(int dtype, const void *o, const int32_t *slot_pos, con
                           void *y, int64_t T, int H, int K, hipStream_t stream);
 // backward combine: dx[t] = Σ_k dxp[slot_pos[tK+k]] and
 // d_topk[t, k] = Σ_j dgp[slot_pos[tK+k], j] (0 for a dropped slot)
-// (all zeros when *status has MOE_DEV_BAD_SAVED)
+// (all zeros when *status has MOE_DEV_BAD_SAVED or MOE_DEV_BAD_WS)
 hipError_t launch_combine_bwd(const void *dxp, const float *dgp, int dgp_stride,
                               const int32_t *slot_pos, const int32_t *status, void *dx,
                               float *d_topk, int64_t T, int H, int K, hipStream_t stream);
@@ -153,10 +158,15 @@ hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t stream);
 // Backward set-up (one block): checks the saved context's header and the
 // consistency of its counts/offsets; copies them into the workspace (all zero,
 // and MOE_DEV_BAD_SAVED in *status, if the check fails) and builds the M-tile
-// tables from the copies.
+// tables from the copies.  The stages of a split backward also pass the
+// workspace's copy of the header, ws_hdr: the data-gradient stage
+// (BWD_STAGE_D) writes it (zeros if the saved context failed its check); the
+// weight-gradient stage (BWD_STAGE_W) requires it to equal the saved header,
+// else the copies are zero and *status gets MOE_DEV_BAD_WS.
+enum { BWD_STAGE_ALL = 0, BWD_STAGE_D = 1, BWD_STAGE_W = 2 };
 hipError_t launch_bwd_setup(const SavedHeader *hdr, uint64_t problem_hash, const int32_t *counts,
                             const int32_t *offsets, int E, int64_t TK, int BM, int32_t *counts_out,
                             int32_t *offsets_out, int32_t *mtile_off, int32_t *mtile_expert,
-                            int32_t *status, hipStream_t stream);
+                            int32_t *status, SavedHeader *ws_hdr, int stage, hipStream_t stream);
 
 } // namespace moe

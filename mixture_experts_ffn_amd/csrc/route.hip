@@ -124,12 +124,13 @@ __device__ inline int32_t block_excl_scan(int32_t v, int32_t *s_w, int32_t *tota
 // Start-of-forward bookkeeping done by the first routing block: the saved
 // context's header and the zeroed release counters of the pipelined forward.
 __device__ inline void write_header_and_counters(SavedHeader *hdr, uint64_t problem_hash,
-                                                 int32_t *ctr, int nctr)
+                                                 uint64_t epoch, int32_t *ctr, int nctr)
 {
     if (hdr && threadIdx.x == 0) {
         hdr->magic = kSavedMagic;
         hdr->version = kSavedVersion;
         hdr->problem = problem_hash;
+        hdr->epoch = epoch;
     }
     for (int j = threadIdx.x; j < nctr; j += blockDim.x)
         ctr[j] = 0;
@@ -188,9 +189,9 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ 
                                                           int32_t *__restrict__ status,
                                                           int32_t *__restrict__ ctr, int nctr,
                                                           SavedHeader *__restrict__ hdr,
-                                                          uint64_t problem_hash)
+                                                          uint64_t problem_hash, uint64_t epoch)
 {
-    write_header_and_counters(hdr, problem_hash, ctr, nctr);
+    write_header_and_counters(hdr, problem_hash, epoch, ctr, nctr);
     __shared__ int32_t s_cnt[1024];
     __shared__ int32_t s_moff[1025];
     __shared__ int32_t s_w[40];
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(1024) void route_block_kernel(
     const int32_t *__restrict__ hist, const int32_t *__restrict__ bad,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ mtile_off,
     int32_t *__restrict__ mtile_expert, int32_t *__restrict__ status, int32_t *__restrict__ ctr,
-    int nctr, SavedHeader *__restrict__ hdr, uint64_t problem_hash,
+    int nctr, SavedHeader *__restrict__ hdr, uint64_t problem_hash, uint64_t epoch,
     int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_pos)
 {
     extern __shared__ int32_t lds[];
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(1024) void route_block_kernel(
     const int b0 = blockIdx.x * 16;
     const bool lead = blockIdx.x == 0;
     if (lead)
-        write_header_and_counters(hdr, problem_hash, ctr, nctr);
+        write_header_and_counters(hdr, problem_hash, epoch, ctr, nctr);
     int anybad = 0;
     if constexpr (ONE) {
         for (int i = threadIdx.x; i < E * 16; i += 1024)
@@ -417,14 +418,21 @@ __global__ __launch_bounds__(1024) void bwd_setup_kernel(
     const int32_t *__restrict__ offsets, int E, int64_t TK, int BM,
     int32_t *__restrict__ counts_out, int32_t *__restrict__ offsets_out,
     int32_t *__restrict__ mtile_off, int32_t *__restrict__ mtile_expert,
-    int32_t *__restrict__ status)
+    int32_t *__restrict__ status, SavedHeader *__restrict__ ws_hdr, int stage)
 {
     __shared__ int32_t s_moff[1025];
     __shared__ int32_t s_w[40];
-    __shared__ int s_hdr_ok;
-    if (threadIdx.x == 0)
-        s_hdr_ok = hdr->magic == kSavedMagic && hdr->version == kSavedVersion &&
-                   hdr->problem == problem_hash;
+    __shared__ int s_hdr_ok, s_ws_ok;
+    if (threadIdx.x == 0) {
+        const SavedHeader h = *hdr;
+        s_hdr_ok = h.magic == kSavedMagic && h.version == kSavedVersion && h.problem == problem_hash;
+        s_ws_ok = 1;
+        if (stage == BWD_STAGE_W) {
+            const SavedHeader w = *ws_hdr;
+            s_ws_ok = w.magic == h.magic && w.version == h.version && w.problem == h.problem &&
+                      w.epoch == h.epoch;
+        }
+    }
     __syncthreads();
     const int e = threadIdx.x;
     int32_t c = 0, off = 0;
@@ -436,7 +444,7 @@ __global__ __launch_bounds__(1024) void bwd_setup_kernel(
         bad = c < 0 || off < 0 || next - off != c || (int64_t)next > TK || (e == 0 && off != 0);
     }
     bad = __syncthreads_or(bad);
-    const bool ok = s_hdr_ok && !bad;
+    const bool ok = s_hdr_ok && !bad && s_ws_ok;
     if (!ok) {
         c = 0;
         off = 0;
@@ -447,7 +455,14 @@ __global__ __launch_bounds__(1024) void bwd_setup_kernel(
     }
     if (e == 0) {
         offsets_out[E] = ok ? offsets[E] : 0;
-        status[0] = ok ? 0 : MOE_DEV_BAD_SAVED;
+        status[0] = ok ? 0 : !(s_hdr_ok && !bad) ? MOE_DEV_BAD_SAVED : MOE_DEV_BAD_WS;
+        if (stage == BWD_STAGE_D) {
+            // the stamp the weight-gradient stage will check (zeros: nothing to trust)
+            SavedHeader w{};
+            if (ok)
+                w = *hdr;
+            *ws_hdr = w;
+        }
     }
     const int32_t mt = e < E ? (c + BM - 1) / BM : 0;
     int32_t mtotal;
@@ -477,10 +492,11 @@ __global__ __launch_bounds__(1024) void bwd_setup_kernel(
 hipError_t launch_bwd_setup(const SavedHeader *hdr, uint64_t problem_hash, const int32_t *counts,
                             const int32_t *offsets, int E, int64_t TK, int BM, int32_t *counts_out,
                             int32_t *offsets_out, int32_t *mtile_off, int32_t *mtile_expert,
-                            int32_t *status, hipStream_t stream)
+                            int32_t *status, SavedHeader *ws_hdr, int stage, hipStream_t stream)
 {
     hipLaunchKernelGGL(bwd_setup_kernel, dim3(1), dim3(1024), 0, stream, hdr, problem_hash, counts,
-                       offsets, E, TK, BM, counts_out, offsets_out, mtile_off, mtile_expert, status);
+                       offsets, E, TK, BM, counts_out, offsets_out, mtile_off, mtile_expert, status,
+                       ws_hdr, stage);
     return hipGetLastError();
 }
 
@@ -517,13 +533,13 @@ static void launch_route_t(const Id *ids, int64_t TK, int E, int BM, const Route
             hipLaunchKernelGGL((route_block_kernel<Id, true>), dim3(1), dim3(1024), lds_block, stream,
                                ids, TK, E, rp.nbits, rp.RC, rp.NB, BM, rb.hist, rb.bad, rb.counts,
                                rb.offsets, rb.mtile_off, rb.mtile_expert, rb.status, rb.ctr, nctr,
-                               rb.saved_hdr, rb.problem_hash, rb.sorted_slot, rb.slot_pos);
+                               rb.saved_hdr, rb.problem_hash, rb.epoch, rb.sorted_slot, rb.slot_pos);
         else
             hipLaunchKernelGGL((route_block_kernel<Id, false>), dim3(nblk), dim3(1024), lds_block,
                                stream, ids, TK, E, rp.nbits, rp.RC, rp.NB, BM, rb.hist, rb.bad,
                                rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert, rb.status,
-                               rb.ctr, nctr, rb.saved_hdr, rb.problem_hash, rb.sorted_slot,
-                               rb.slot_pos);
+                               rb.ctr, nctr, rb.saved_hdr, rb.problem_hash, rb.epoch,
+                               rb.sorted_slot, rb.slot_pos);
         return;
     }
     // many experts (the block table would not fit), or no slots: hist, scan, scatter
@@ -533,7 +549,7 @@ static void launch_route_t(const Id *ids, int64_t TK, int E, int BM, const Route
     const int nb_scan = TK > 0 ? rp.NB : 0;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, rb.hist, rb.bad, E,
                        nb_scan, BM, rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert,
-                       rb.status, rb.ctr, nctr, rb.saved_hdr, rb.problem_hash);
+                       rb.status, rb.ctr, nctr, rb.saved_hdr, rb.problem_hash, rb.epoch);
     if (TK > 0)
         hipLaunchKernelGGL(route_scatter_kernel<Id>, dim3(rp.NB), dim3(64), lds, stream, ids, TK, E,
                            rp.nbits, rp.RC, rp.NB, rb.hist, rb.offsets, rb.sorted_slot,
