@@ -207,7 +207,7 @@ int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, cons
                    void *ws, size_t ws_bytes, uint32_t flags, void *stream,
                    const moe_ffn_stage_events *ev);
 
-/* The backward split into its two halves (EP overlap page, section 2.3
+/* The backward split into its two halves (EP overlap issue, section 2.3
  * "W/D split + deferred W queue" and section 4.5's interface draft: a
  * D-only entry that yields the input gradient, and a W-only entry that a
  * scheduler can defer into an idle window).  Together they compute exactly

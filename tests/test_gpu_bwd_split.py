@@ -1,6 +1,6 @@
 """The backward split into its data half and its weight half.
 
-EP overlap page, section 2.3 "W/D split + deferred W queue" and section 4.5's
+EP overlap issue, section 2.3 "W/D split + deferred W queue" and section 4.5's
 interface draft: a D-only call that yields the input gradient and a W-only
 call that a scheduler may run later.  moe_ffn_bwd_d followed by moe_ffn_bwd_w
 must reproduce moe_ffn_bwd bit for bit; a weight half given a workspace that
