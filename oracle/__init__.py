@@ -235,3 +235,34 @@ def backward_sampled(dy, x, topk_ids, topk_weights, up_proj, down_proj, toks, w1
                                           _p(dx), _p(dg), _p(w1c), n1, _p(d1), _p(w2r), n2,
                                           _p(d2)))
     return dx[:n], dg[:n], d1[:n1], d2[:n2]
+
+
+# ----------------------------------------------------------------- shared expert
+# Issue page, section 6.1 ("shared-expert fused MoE") and the EP overlap issue,
+# section 4.3: the shared expert is a SwiGLU feed-forward every token passes
+# through, its output added to the combined routed output.  It is the routed
+# definition at one expert, K = 1 and gate 1 (the reduction pinned as a dense
+# SwiGLU FFN), applied to shared_up [H, 2Is] and shared_down [Is, H].
+def _single_expert_route(T):
+    return np.zeros((T, 1), np.int32), np.ones((T, 1), np.float32)
+
+
+def shared_expert(x, shared_up, shared_down):
+    """FFN_s(x) [T,H] float64."""
+    ids, g = _single_expert_route(np.asarray(x).shape[0])
+    return forward(x, ids, g, np.asarray(shared_up)[None], np.asarray(shared_down)[None])
+
+
+def forward_shared(x, topk_ids, topk_weights, up_proj, down_proj, shared_up, shared_down):
+    """y = Σ_k g·FFN_e(x) + FFN_s(x), [T,H] float64."""
+    return (forward(x, topk_ids, topk_weights, up_proj, down_proj)
+            + shared_expert(x, shared_up, shared_down))
+
+
+def backward_shared(dy, x, topk_ids, topk_weights, up_proj, down_proj, shared_up, shared_down):
+    """(dx, d_up, d_down, d_topk, d_shared_up [H,2Is], d_shared_down [Is,H]) float64."""
+    dx, d_up, d_down, d_topk = backward(dy, x, topk_ids, topk_weights, up_proj, down_proj)
+    ids, g = _single_expert_route(np.asarray(x).shape[0])
+    sdx, s_up, s_down, _ = backward(dy, x, ids, g, np.asarray(shared_up)[None],
+                                    np.asarray(shared_down)[None])
+    return dx + sdx, d_up, d_down, d_topk, s_up[0], s_down[0]

@@ -11,6 +11,8 @@ slice, PCG64 bit generator):
 * ``up_proj``      ~ N(0, 1/sqrt(H)), shape [E, H, 2I]   (fan_in = H)
 * ``down_proj``    ~ N(0, 1/sqrt(I)), shape [E, I, H]    (fan_in = I)
 * ``dy``           ~ N(0, 1), shape [T, H]
+* ``shared_up``    ~ N(0, 1/sqrt(H)), shape [H, 2·Is]  (workloads with a shared expert)
+* ``shared_down``  ~ N(0, 1/sqrt(Is)), shape [Is, H]
 * routing "uniform": router logits ~ N(0, 1) [T, E]; ``topk_ids`` are the K
   largest logits of each token in descending order (ties: lower expert id
   first), ``topk_weights`` the softmax over those K logits.
@@ -46,7 +48,7 @@ __all__ = [
 ]
 
 # tensor ids inside one workload's seed space
-_TID_X, _TID_W1, _TID_W2, _TID_LOGITS, _TID_DY, _TID_PERM, _TID_GUMBEL = range(7)
+_TID_X, _TID_W1, _TID_W2, _TID_LOGITS, _TID_DY, _TID_PERM, _TID_GUMBEL, _TID_SW1, _TID_SW2 = range(9)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -65,6 +67,7 @@ class Workload:
     zipf_s: float = 1.2
     n_empty: int = 0
     backward: bool = False
+    Is: int = 0  # intermediate width of the shared expert (0: none)
 
     @property
     def TK(self) -> int:
@@ -209,6 +212,11 @@ def make_inputs(w: Workload, seed: int = 0, with_dy: bool | None = None, threads
     ids, gates, _ = make_routing(w, seed)
     out["topk_ids"] = ids
     out["topk_weights"] = gates
+    if w.Is:
+        out["shared_up"] = _normal_slices((H, 2 * w.Is), 1.0 / np.sqrt(H), w.dtype,
+                                          (w.cfg_id, _TID_SW1, seed), threads)
+        out["shared_down"] = _normal_slices((w.Is, H), 1.0 / np.sqrt(w.Is), w.dtype,
+                                            (w.cfg_id, _TID_SW2, seed), threads)
     if with_dy is None:
         with_dy = w.backward
     if with_dy:

@@ -431,3 +431,89 @@ def test_backward_sampled_agrees_with_full():
     assert rel_err(sg, dg[toks]) < 1e-12
     assert rel_err(s1, np.stack([d_up[e][:, j] for e, j in w1c])) < 1e-12
     assert rel_err(s2, np.stack([d_down[e][i, :] for e, i in w2r])) < 1e-12
+
+
+# --------------------------------------------------------------------------- shared expert
+# Issue page, section 6.1, and the EP overlap issue, section 4.3: the shared
+# expert's SwiGLU FFN output is added to the combined routed output.
+def dense_ffn(x, W1, W2):
+    Is = W2.shape[0]
+    h = x @ W1
+    return (F.silu(h[:, :Is]) * h[:, Is:]) @ W2
+
+
+def shared_inputs(T=9, H=16, I=8, E=3, K=2, Is=24, dtype="f32", cfg_id=140):
+    w = small(T, H, I, E, K, dtype=dtype, cfg_id=cfg_id, Is=Is)
+    return make_inputs(w, with_dy=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_shared_expert_is_dense_swiglu_ffn(dtype):
+    """The shared term against torch.nn.functional.silu and plain matmuls."""
+    inp = shared_inputs(dtype=dtype)
+    got = oracle.shared_expert(inp["x"], inp["shared_up"], inp["shared_down"])
+    want = dense_ffn(as64(inp["x"]), as64(inp["shared_up"]), as64(inp["shared_down"]))
+    assert rel_err(got, want.numpy()) < 1e-12
+
+
+def test_forward_shared_with_zero_shared_weights_is_the_routed_layer():
+    inp = shared_inputs()
+    zup, zdown = np.zeros_like(inp["shared_up"]), np.zeros_like(inp["shared_down"])
+    got = oracle.forward_shared(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["up_proj"],
+                                inp["down_proj"], zup, zdown)
+    want = oracle.forward(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["up_proj"],
+                          inp["down_proj"])
+    assert np.array_equal(got, want)
+
+
+def test_shared_term_does_not_depend_on_the_routing():
+    inp = shared_inputs()
+    rng = np.random.default_rng(3)
+    diffs = []
+    for _ in range(2):
+        ids = random_ids(rng, 9, 2, 3)
+        g = rng.uniform(0.1, 1.0, size=(9, 2)).astype(np.float32)
+        a = oracle.forward_shared(inp["x"], ids, g, inp["up_proj"], inp["down_proj"],
+                                  inp["shared_up"], inp["shared_down"])
+        b = oracle.forward(inp["x"], ids, g, inp["up_proj"], inp["down_proj"])
+        diffs.append(a - b)
+    assert rel_err(diffs[0], diffs[1]) < 1e-12
+
+
+def test_shared_expert_splits_into_chunks_of_the_routed_width():
+    """Is = 3I: the shared FFN equals the sum of three width-I SwiGLU FFNs whose gate
+    columns are gate chunk c, up columns up chunk c and down rows chunk c (the
+    decomposition the GPU schedules as three extra experts)."""
+    I, Is = 8, 24
+    inp = shared_inputs(I=I, Is=Is)
+    W1, W2 = inp["shared_up"], inp["shared_down"]
+    whole = oracle.shared_expert(inp["x"], W1, W2)
+    parts = 0.0
+    for c in range(Is // I):
+        w1c = np.concatenate([W1[:, c * I:(c + 1) * I], W1[:, Is + c * I:Is + (c + 1) * I]], axis=1)
+        parts = parts + oracle.shared_expert(inp["x"], np.ascontiguousarray(w1c),
+                                             np.ascontiguousarray(W2[c * I:(c + 1) * I]))
+    assert rel_err(parts, whole) < 1e-12
+
+
+def test_backward_shared_matches_autograd():
+    inp = shared_inputs()
+    got = oracle.backward_shared(inp["dy"], inp["x"], inp["topk_ids"], inp["topk_weights"],
+                                 inp["up_proj"], inp["down_proj"], inp["shared_up"],
+                                 inp["shared_down"])
+    x, g, W1, W2, S1, S2 = [as64(a).requires_grad_(True) for a in
+                            (inp["x"], inp["topk_weights"], inp["up_proj"], inp["down_proj"],
+                             inp["shared_up"], inp["shared_down"])]
+    y = brute_forward(x, inp["topk_ids"], g, W1, W2) + dense_ffn(x, S1, S2)
+    (y * as64(inp["dy"])).sum().backward()
+    want = (x.grad, W1.grad, W2.grad, g.grad, S1.grad, S2.grad)
+    for name, a, b in zip(("dx", "d_up", "d_down", "d_topk", "d_shared_up", "d_shared_down"),
+                          got, want):
+        assert rel_err(a, b.numpy()) < 1e-12, name
+
+
+def test_forward_shared_t0():
+    inp = shared_inputs(T=0)
+    y = oracle.forward_shared(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["up_proj"],
+                              inp["down_proj"], inp["shared_up"], inp["shared_down"])
+    assert y.shape == (0, 16)
