@@ -71,6 +71,8 @@ typedef struct {
     int64_t T, H, I, E, K;
     int32_t dtype;     /* MOE_FFN_F32 or MOE_FFN_BF16 */
     int32_t ids_dtype; /* MOE_FFN_I32 or MOE_FFN_I64 */
+    int64_t Is;        /* intermediate width of the shared expert, a multiple of I with
+                          E + Is / I <= 1024; 0: no shared expert (the *_shared calls) */
 } moe_ffn_problem;
 
 /* Flags. */
@@ -166,6 +168,51 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
                    const float *topk_weights, const void *up_proj_weight,
                    const void *down_proj_weight, void *y, void *saved, void *ws, size_t ws_bytes,
                    uint32_t flags, void *stream, const moe_ffn_stage_events *ev);
+/* moe_ffn_fwd, moe_ffn_fwd_ex, moe_ffn_bwd, moe_ffn_bwd_ex, moe_ffn_bwd_d and
+ * moe_ffn_bwd_w take problems without a shared expert (Is == 0;
+ * MOE_FFN_ERR_SHAPE otherwise). */
+
+/* ---- shared expert -------------------------------------------------------- */
+
+/* The optional shared expert (issue page, section 6.1 "shared-expert fused
+ * MoE"; the EP overlap issue, section 4.3: its output is added to the combined
+ * routed output): a SwiGLU feed-forward that every token passes through,
+ *   y[t] = Σ_k g[t,k] · FFN_{e[t,k]}(x[t]) + FFN_s(x[t]),
+ *   FFN_s(x) = (silu(x · Ws1[:, :Is]) ⊙ (x · Ws1[:, Is:])) · Ws2,
+ * with Ws1 = up_proj_weight [H, 2·Is] and Ws2 = down_proj_weight [Is, H] in
+ * the problem dtype, row-major, 16-byte aligned, owned by the caller.  The
+ * problem's Is must be a multiple of I: the kernels run the shared expert as
+ * Is / I extra experts (column chunk c of the gate and of the up half, row
+ * chunk c of Ws2) whose tiles are scheduled with the routed experts' and whose
+ * outputs the combine adds after the routed terms (gate 1, chunk order).
+ * Workspace and saved sizes (moe_ffn_fwd_workspace_size,
+ * moe_ffn_bwd_workspace_size) depend on Is.  MOE_FFN_PIPELINE is ignored here
+ * (the bulk launches run). */
+typedef struct {
+    const void *up_proj_weight;   /* [H, 2·Is] */
+    const void *down_proj_weight; /* [Is, H] */
+} moe_ffn_shared_weights;
+typedef struct {
+    void *d_up_proj_weight;   /* [H, 2·Is], overwritten */
+    void *d_down_proj_weight; /* [Is, H], overwritten */
+} moe_ffn_shared_grads;
+
+/* moe_ffn_fwd with a shared expert (p->Is > 0; with Is == 0 it is moe_ffn_fwd). */
+int moe_ffn_fwd_shared(const moe_ffn_problem *p, const void *x, const void *topk_ids,
+                       const float *topk_weights, const void *up_proj_weight,
+                       const void *down_proj_weight, const moe_ffn_shared_weights *shared,
+                       void *y, void *saved, void *ws, size_t ws_bytes, uint32_t flags,
+                       void *stream);
+/* moe_ffn_bwd with a shared expert: also the shared weights' gradients; dx
+ * includes the shared expert's contribution, d_topk_weights does not involve
+ * it.  `saved` must come from moe_ffn_fwd_shared for the same problem. */
+int moe_ffn_bwd_shared(const moe_ffn_problem *p, const void *dy, const void *x,
+                       const void *topk_ids, const float *topk_weights,
+                       const void *up_proj_weight, const void *down_proj_weight,
+                       const moe_ffn_shared_weights *shared, const void *saved, void *dx,
+                       void *d_up_proj_weight, void *d_down_proj_weight, float *d_topk_weights,
+                       const moe_ffn_shared_grads *d_shared, void *ws, size_t ws_bytes,
+                       uint32_t flags, void *stream);
 
 /* ---- routing alone -------------------------------------------------------- */
 

@@ -74,7 +74,15 @@ class MoEFFNError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64), ("I", ctypes.c_int64),
                 ("E", ctypes.c_int64), ("K", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("ids_dtype", ctypes.c_int32)]
+                ("ids_dtype", ctypes.c_int32), ("Is", ctypes.c_int64)]
+
+
+class SharedWeights(ctypes.Structure):
+    _fields_ = [("up_proj_weight", ctypes.c_void_p), ("down_proj_weight", ctypes.c_void_p)]
+
+
+class SharedGrads(ctypes.Structure):
+    _fields_ = [("d_up_proj_weight", ctypes.c_void_p), ("d_down_proj_weight", ctypes.c_void_p)]
 
 
 class StageEvents(ctypes.Structure):
@@ -109,6 +117,10 @@ def load_library():
             "moe_ffn_bwd_ex": [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp,
                                ctypes.POINTER(StageEvents)],
             "moe_ffn_bwd_d": [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
+            "moe_ffn_fwd_shared": [pp, vp, vp, vp, vp, vp, ctypes.POINTER(SharedWeights), vp, vp,
+                                   vp, sz, u32, vp],
+            "moe_ffn_bwd_shared": [pp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(SharedWeights), vp,
+                                   vp, vp, vp, vp, ctypes.POINTER(SharedGrads), vp, sz, u32, vp],
             "moe_ffn_bwd_w": [pp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
             "moe_ffn_route": [pp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_ffn_read_status": [vp, vp, ctypes.POINTER(ctypes.c_int32)],
@@ -204,10 +216,27 @@ def route_workspace_size(problem: Problem) -> int:
     return ws.value
 
 
+def _shared_problem(prob, x, shared_up_proj_weight, shared_down_proj_weight):
+    """Set prob.Is from the shared-expert weights (both or neither)."""
+    if shared_up_proj_weight is None and shared_down_proj_weight is None:
+        return None
+    if shared_up_proj_weight is None or shared_down_proj_weight is None:
+        raise MoEFFNError(2, "pass both shared_up_proj_weight and shared_down_proj_weight")
+    _require_gpu(shared_up_proj_weight, shared_down_proj_weight)
+    Is, H = shared_down_proj_weight.shape
+    if shared_up_proj_weight.shape != (H, 2 * Is) or H != x.shape[1]:
+        raise MoEFFNError(2, "expected shared_up [H, 2Is] and shared_down [Is, H]")
+    if shared_up_proj_weight.dtype != x.dtype or shared_down_proj_weight.dtype != x.dtype:
+        raise MoEFFNError(3, "the shared weights must have the dtype of x")
+    prob.Is = Is
+    return SharedWeights(shared_up_proj_weight.data_ptr(), shared_down_proj_weight.data_ptr())
+
+
 def moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *,
                 save_for_backward: bool = False, check_ids: bool = False, ws=None,
                 stage_events: StageEvents | None = None, return_ws: bool = False,
-                pipelined: bool = False, flags: int = 0):
+                pipelined: bool = False, flags: int = 0, shared_up_proj_weight=None,
+                shared_down_proj_weight=None):
     """y [T, H] of the MoE expert-FFN layer (see include/moe_ffn.h).
 
     With ``save_for_backward`` also returns the saved context (a uint8 device
@@ -215,13 +244,18 @@ def moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *,
     workspace (uint8 tensor of at least ``fwd_workspace_size`` bytes).
     ``pipelined`` selects the one-launch forward with tile-granular release
     (bf16, H % 256 == 0, I % 128 == 0; other shapes ignore it);
-    ``flags`` passes further MOE_FFN_* bits through.
+    ``flags`` passes further MOE_FFN_* bits through.  ``shared_up_proj_weight``
+    [H, 2Is] and ``shared_down_proj_weight`` [Is, H] (Is a multiple of I) add the
+    shared expert's SwiGLU FFN to y; the saved context then covers it too.
     """
     lib = load_library()
     _require_gpu(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight)
     if topk_weights.dtype != torch.float32 or topk_weights.shape != topk_ids.shape:
         raise MoEFFNError(3, "topk_weights must be float32 with the shape of topk_ids")
     prob = make_problem(x, topk_ids, up_proj_weight, down_proj_weight)
+    sw = _shared_problem(prob, x, shared_up_proj_weight, shared_down_proj_weight)
+    if sw is not None and stage_events is not None:
+        raise MoEFFNError(2, "stage_events is not available with a shared expert")
     ws_bytes, saved_bytes = fwd_workspace_size(prob)
     dev = x.device
     y = torch.empty_like(x)
@@ -233,9 +267,16 @@ def moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *,
     flags |= (CHECK_IDS if check_ids else 0) | (PIPELINE if pipelined else 0)
     ev = ctypes.byref(stage_events) if stage_events is not None else None
     with torch.cuda.device(dev):
-        rc = lib.moe_ffn_fwd_ex(ctypes.byref(prob), _ptr(x), _ptr(topk_ids), _ptr(topk_weights),
-                                _ptr(up_proj_weight), _ptr(down_proj_weight), _ptr(y),
-                                _ptr(saved), _ptr(ws), ws.numel(), flags, _stream(dev), ev)
+        if sw is not None:
+            rc = lib.moe_ffn_fwd_shared(ctypes.byref(prob), _ptr(x), _ptr(topk_ids),
+                                        _ptr(topk_weights), _ptr(up_proj_weight),
+                                        _ptr(down_proj_weight), ctypes.byref(sw), _ptr(y),
+                                        _ptr(saved), _ptr(ws), ws.numel(), flags, _stream(dev))
+        else:
+            rc = lib.moe_ffn_fwd_ex(ctypes.byref(prob), _ptr(x), _ptr(topk_ids),
+                                    _ptr(topk_weights), _ptr(up_proj_weight),
+                                    _ptr(down_proj_weight), _ptr(y), _ptr(saved), _ptr(ws),
+                                    ws.numel(), flags, _stream(dev), ev)
     _check(rc)
     out = (y,)
     if save_for_backward:
@@ -254,8 +295,12 @@ def bwd_workspace_size(problem: Problem, flags: int = 0) -> int:
 
 def moe_ffn_bwd(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, saved, *,
                 ws=None, stage_events: StageEvents | None = None, check_saved: bool = False,
-                return_ws: bool = False):
+                return_ws: bool = False, shared_up_proj_weight=None,
+                shared_down_proj_weight=None):
     """Gradients (dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights) of the layer.
+
+    With the shared expert's weights (as given to the forward) it also returns
+    (d_shared_up_proj_weight, d_shared_down_proj_weight).
 
     `saved` is the context returned by ``moe_ffn_fwd(..., save_for_backward=True)`` for the
     same inputs.  Outputs are freshly allocated and overwritten (never accumulated).
@@ -268,6 +313,9 @@ def moe_ffn_bwd(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
     prob = make_problem(x, topk_ids, up_proj_weight, down_proj_weight)
     if dy.shape != x.shape or dy.dtype != x.dtype:
         raise MoEFFNError(2, "dy must have the shape and dtype of x")
+    sw = _shared_problem(prob, x, shared_up_proj_weight, shared_down_proj_weight)
+    if sw is not None and stage_events is not None:
+        raise MoEFFNError(2, "stage_events is not available with a shared expert")
     ws_bytes = bwd_workspace_size(prob)
     dev = x.device
     dx = torch.empty_like(x)
@@ -279,11 +327,25 @@ def moe_ffn_bwd(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
     ev = ctypes.byref(stage_events) if stage_events is not None else None
     flags = CHECK_SAVED if check_saved else 0
     with torch.cuda.device(dev):
-        rc = lib.moe_ffn_bwd_ex(ctypes.byref(prob), _ptr(dy), _ptr(x), _ptr(topk_ids),
-                                _ptr(topk_weights), _ptr(up_proj_weight), _ptr(down_proj_weight),
-                                _ptr(saved), _ptr(dx), _ptr(d_up), _ptr(d_down), _ptr(d_topk),
-                                _ptr(ws), ws.numel(), flags, _stream(dev), ev)
+        if sw is not None:
+            d_sup = torch.empty_like(shared_up_proj_weight)
+            d_sdown = torch.empty_like(shared_down_proj_weight)
+            sg = SharedGrads(d_sup.data_ptr(), d_sdown.data_ptr())
+            rc = lib.moe_ffn_bwd_shared(ctypes.byref(prob), _ptr(dy), _ptr(x), _ptr(topk_ids),
+                                        _ptr(topk_weights), _ptr(up_proj_weight),
+                                        _ptr(down_proj_weight), ctypes.byref(sw), _ptr(saved),
+                                        _ptr(dx), _ptr(d_up), _ptr(d_down), _ptr(d_topk),
+                                        ctypes.byref(sg), _ptr(ws), ws.numel(), flags,
+                                        _stream(dev))
+        else:
+            rc = lib.moe_ffn_bwd_ex(ctypes.byref(prob), _ptr(dy), _ptr(x), _ptr(topk_ids),
+                                    _ptr(topk_weights), _ptr(up_proj_weight),
+                                    _ptr(down_proj_weight), _ptr(saved), _ptr(dx), _ptr(d_up),
+                                    _ptr(d_down), _ptr(d_topk), _ptr(ws), ws.numel(), flags,
+                                    _stream(dev), ev)
     _check(rc)
+    if sw is not None:
+        return (dx, d_up, d_down, d_topk, d_sup, d_sdown) + ((ws,) if return_ws else ())
     if return_ws:
         return dx, d_up, d_down, d_topk, ws
     return dx, d_up, d_down, d_topk

@@ -81,8 +81,19 @@ int validate_problem(const moe_ffn_problem *p)
         return fail(MOE_FFN_ERR_SHAPE, "T*K must be < 2^31");
     if (p->H * 2 * p->I >= (int64_t(1) << 31))
         return fail(MOE_FFN_ERR_SHAPE, "H*2I must be < 2^31");
+    if (p->Is < 0 || p->Is % p->I)
+        return fail(MOE_FFN_ERR_SHAPE, "Is must be a non-negative multiple of I (got %lld)",
+                    (long long)p->Is);
+    if (p->E + p->Is / p->I > 1024)
+        return fail(MOE_FFN_ERR_SHAPE, "E + Is / I must be <= 1024");
+    if (p->T * (p->K + p->Is / p->I) >= (int64_t(1) << 31) || p->H * 2 * p->Is >= (int64_t(1) << 31))
+        return fail(MOE_FFN_ERR_SHAPE, "T*(K + Is/I) and H*2Is must be < 2^31");
     return MOE_FFN_OK;
 }
+
+// Shared-expert chunks S = Is / I; the plan covers E + S experts and
+// T*K + S*T permuted rows (the shared rows after the routed ones).
+int nshared(const moe_ffn_problem &p) { return (int)(p.Is / p.I); }
 
 bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
@@ -170,10 +181,12 @@ FwdLayout fwd_layout(const moe_ffn_problem &p)
     FwdLayout L;
     const int64_t TK = p.T * p.K;
     const int E = (int)p.E;
+    const int Ep = E + nshared(p);                  // experts of the plan
+    const int64_t TKp = TK + (int64_t)nshared(p) * p.T; // permuted rows
     const size_t es = elem_size(p.dtype);
     L.tiles = pick_tiles(p);
     L.rp = moe::make_route_plan(TK, E);
-    L.max_mtiles = moe::max_mtiles_bound(TK, E, L.tiles.BM);
+    L.max_mtiles = moe::max_mtiles_bound(TKp, Ep, L.tiles.BM);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -183,23 +196,23 @@ FwdLayout fwd_layout(const moe_ffn_problem &p)
     L.status = take(sizeof(int32_t));
     L.hist = take(sizeof(int32_t) * (size_t)E * (size_t)L.rp.NB);
     L.bad = take(sizeof(int32_t) * (size_t)L.rp.NB);
-    L.counts = take(sizeof(int32_t) * (size_t)E);
-    L.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
-    L.mtile_off = take(sizeof(int32_t) * (size_t)(E + 1));
+    L.counts = take(sizeof(int32_t) * (size_t)Ep);
+    L.offsets = take(sizeof(int32_t) * (size_t)(Ep + 1));
+    L.mtile_off = take(sizeof(int32_t) * (size_t)(Ep + 1));
     L.mtile_expert = take(sizeof(int32_t) * (size_t)L.max_mtiles);
-    L.sorted_slot = take(sizeof(int32_t) * (size_t)TK);
+    L.sorted_slot = take(sizeof(int32_t) * (size_t)TKp);
     L.slot_pos = take(sizeof(int32_t) * (size_t)TK);
     L.ctr = take(sizeof(int32_t) * 2 * (size_t)L.max_mtiles);
-    L.act = take(es * (size_t)TK * (size_t)p.I);
-    L.o = take(es * (size_t)TK * (size_t)p.H);
+    L.act = take(es * (size_t)TKp * (size_t)p.I);
+    L.o = take(es * (size_t)TKp * (size_t)p.H);
     L.ws_total = off;
     off = 0;
     L.s_hdr = take(sizeof(moe::SavedHeader));
-    L.s_counts = take(sizeof(int32_t) * (size_t)E);
-    L.s_offsets = take(sizeof(int32_t) * (size_t)(E + 1));
-    L.s_sorted = take(sizeof(int32_t) * (size_t)TK);
+    L.s_counts = take(sizeof(int32_t) * (size_t)Ep);
+    L.s_offsets = take(sizeof(int32_t) * (size_t)(Ep + 1));
+    L.s_sorted = take(sizeof(int32_t) * (size_t)TKp);
     L.s_slotpos = take(sizeof(int32_t) * (size_t)TK);
-    L.s_h = take(es * (size_t)TK * (size_t)(2 * p.I));
+    L.s_h = take(es * (size_t)TKp * (size_t)(2 * p.I));
     L.saved_total = off;
     return L;
 }
@@ -244,8 +257,8 @@ struct BwdLayout {
 BwdLayout bwd_layout(const moe_ffn_problem &p)
 {
     BwdLayout B;
-    const int64_t TK = p.T * p.K;
-    const int E = (int)p.E;
+    const int64_t TK = p.T * p.K + (int64_t)nshared(p) * p.T; // permuted rows
+    const int E = (int)p.E + nshared(p);                     // experts of the plan
     B.BM = 128;
     B.max_mtiles = moe::max_mtiles_bound(TK, E, B.BM);
     B.dgp_width = moe::engine_dgp_width((int)p.I);
@@ -318,18 +331,26 @@ int moe_ffn_fwd_workspace_size(const moe_ffn_problem *p, uint32_t flags, size_t 
     return MOE_FFN_OK;
 }
 
-int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids,
+// The forward, with or without a shared expert (sh: its weights; p->Is > 0).
+static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids,
                    const float *topk_weights, const void *up_proj_weight,
-                   const void *down_proj_weight, void *y, void *saved, void *ws, size_t ws_bytes,
-                   uint32_t flags, void *stream, const moe_ffn_stage_events *ev)
+                   const void *down_proj_weight, const moe_ffn_shared_weights *sh, void *y,
+                   void *saved, void *ws, size_t ws_bytes, uint32_t flags, void *stream,
+                   const moe_ffn_stage_events *ev)
 {
     g_err[0] = 0;
     int rc = validate_problem(p);
     if (rc)
         return rc;
+    const int S = nshared(*p);
+    if (S > 0 && !sh)
+        return fail(MOE_FFN_ERR_NULL, "a problem with Is > 0 needs the shared-expert weights");
     const FwdLayout L = fwd_layout(*p);
     if (p->T == 0)
         return MOE_FFN_OK;
+    if (S > 0 && ((rc = check_ptr(sh->up_proj_weight, "shared up_proj_weight")) ||
+                  (rc = check_ptr(sh->down_proj_weight, "shared down_proj_weight"))))
+        return rc;
     const size_t id_align = p->ids_dtype == MOE_FFN_I64 ? 8 : 4;
     if ((rc = check_ptr(x, "x")) || (rc = check_ptr(topk_ids, "topk_ids", id_align)) ||
         (rc = check_ptr(topk_weights, "topk_weights", 4)) ||
@@ -359,6 +380,10 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
     rb.saved_hdr = saved ? at<moe::SavedHeader>(saved, L.s_hdr) : nullptr;
     rb.problem_hash = problem_hash(*p);
     rb.epoch = saved ? g_epoch.fetch_add(1) : 0;
+    rb.nshared = S;
+    rb.T = p->T;
+    const int Ep = E + S; // experts of the plan: routed, then the shared chunks
+    const int64_t Is = p->Is;
     if (saved) {
         rb.counts = at<int32_t>(saved, L.s_counts);
         rb.offsets = at<int32_t>(saved, L.s_offsets);
@@ -399,13 +424,20 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
         g1.mtile_off = rb.mtile_off;
         g1.mtile_expert = rb.mtile_expert;
         g1.topk = (int)p->K;
-        g1.E = E;
+        g1.E = Ep;
         g1.N = (int)p->I;
         g1.Kd = (int)p->H;
         g1.lda = (int)p->H;
         g1.ldb = (int)(2 * p->I);
         g1.ldc = (int)p->I;
         g1.b_estride = p->H * 2 * p->I;
+        g1.Er = E;
+        if (S > 0) {
+            g1.Bs = static_cast<const moe::bf16_t *>(sh->up_proj_weight);
+            g1.bs_cstride = p->I;
+            g1.bs_ldb = (int)(2 * Is);
+            g1.bs_panel = (int)Is;
+        }
         record(ev, MOE_FFN_STAGE_GEMM1, true, s);
         HIP_TRY(moe::launch_engine(moe::ENG_F1, L.tiles.BM, g1, num_cus, s), "gemm1 launch");
         record(ev, MOE_FFN_STAGE_GEMM1, false, s);
@@ -421,6 +453,12 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
         g2.ldb = (int)p->H;
         g2.ldc = (int)p->H;
         g2.b_estride = p->I * p->H;
+        if (S > 0) {
+            g2.Bs = static_cast<const moe::bf16_t *>(sh->down_proj_weight);
+            g2.bs_cstride = p->I * p->H;
+            g2.bs_ldb = (int)p->H;
+            g2.bs_panel = 0;
+        }
         record(ev, MOE_FFN_STAGE_GEMM2, true, s);
         HIP_TRY(moe::launch_engine(moe::ENG_F2, L.tiles.BM, g2, num_cus, s), "gemm2 launch");
         record(ev, MOE_FFN_STAGE_GEMM2, false, s);
@@ -450,12 +488,19 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
         a.T = (int)p->T;
         a.H = (int)p->H;
         a.I = (int)p->I;
-        a.E = E;
+        a.E = Ep;
         a.K = (int)p->K;
+        a.sh.Er = E;
+        a.sh.S = S;
+        a.sh.Is = (int)Is;
+        a.sh.w1 = S > 0 ? sh->up_proj_weight : nullptr;
+        a.sh.w2 = S > 0 ? sh->down_proj_weight : nullptr;
         a.max_mtiles = (int)L.max_mtiles;
         a.drop_mt = (flags & MOE_FFN_TEST_DROP_RELEASE) ? 0 : -1;
         const int BM = L.tiles.BM;
-        if (flags & MOE_FFN_PIPELINE) {
+        // the pipelined launch serves routed experts only; with a shared expert
+        // the bulk launches run
+        if ((flags & MOE_FFN_PIPELINE) && S == 0) {
             record(ev, MOE_FFN_STAGE_PIPELINE, true, s);
             HIP_TRY(moe::launch_fast_fwd(moe::FAST_PIPE, BM, a, num_cus, s), "pipeline launch");
             record(ev, MOE_FFN_STAGE_PIPELINE, false, s);
@@ -482,8 +527,15 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
         g1.Nout = (int)p->I;
         g1.ldb = (int)(2 * p->I);
         g1.topk = (int)p->K;
-        g1.E = E;
+        g1.E = Ep;
         g1.max_mtiles = (int)L.max_mtiles;
+        g1.Er = E;
+        if (S > 0) {
+            g1.Bs = sh->up_proj_weight;
+            g1.bs_cstride = p->I;
+            g1.bs_ldb = (int)(2 * Is);
+            g1.bs_panel = (int)Is;
+        }
         record(ev, MOE_FFN_STAGE_GEMM1, true, s);
         HIP_TRY(moe::launch_gemm1_swiglu(p->dtype, L.tiles, g1, s), "gemm1 launch");
         record(ev, MOE_FFN_STAGE_GEMM1, false, s);
@@ -497,6 +549,12 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
         g2.Kdim = (int)p->I;
         g2.Nout = (int)p->H;
         g2.ldb = (int)p->H;
+        if (S > 0) {
+            g2.Bs = sh->down_proj_weight;
+            g2.bs_cstride = p->I * p->H;
+            g2.bs_ldb = (int)p->H;
+            g2.bs_panel = 0;
+        }
         record(ev, MOE_FFN_STAGE_GEMM2, true, s);
         HIP_TRY(moe::launch_gemm2(p->dtype, L.tiles, g2, s), "gemm2 launch");
         record(ev, MOE_FFN_STAGE_GEMM2, false, s);
@@ -504,10 +562,31 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
 
     record(ev, MOE_FFN_STAGE_COMBINE, true, s);
     HIP_TRY(moe::launch_combine(p->dtype, at<void>(ws, L.o), rb.slot_pos, topk_weights, y, p->T,
-                                (int)p->H, (int)p->K, s),
+                                (int)p->H, (int)p->K, rb.offsets, E, S, s),
             "combine launch");
     record(ev, MOE_FFN_STAGE_COMBINE, false, s);
     return MOE_FFN_OK;
+}
+
+int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids,
+                   const float *topk_weights, const void *up_proj_weight,
+                   const void *down_proj_weight, void *y, void *saved, void *ws, size_t ws_bytes,
+                   uint32_t flags, void *stream, const moe_ffn_stage_events *ev)
+{
+    if (p && p->Is != 0)
+        return fail(MOE_FFN_ERR_SHAPE, "Is != 0: use moe_ffn_fwd_shared");
+    return fwd_run(p, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, nullptr, y,
+                   saved, ws, ws_bytes, flags, stream, ev);
+}
+
+int moe_ffn_fwd_shared(const moe_ffn_problem *p, const void *x, const void *topk_ids,
+                       const float *topk_weights, const void *up_proj_weight,
+                       const void *down_proj_weight, const moe_ffn_shared_weights *shared,
+                       void *y, void *saved, void *ws, size_t ws_bytes, uint32_t flags,
+                       void *stream)
+{
+    return fwd_run(p, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, shared, y,
+                   saved, ws, ws_bytes, flags, stream, nullptr);
 }
 
 int moe_ffn_fwd(const moe_ffn_problem *p, const void *x, const void *topk_ids,
@@ -561,6 +640,8 @@ int moe_ffn_route(const moe_ffn_problem *p, const void *topk_ids, int32_t *count
     rb.saved_hdr = nullptr;
     rb.problem_hash = 0;
     rb.epoch = 0;
+    rb.nshared = 0;
+    rb.T = p->T;
     rb.hist = at<int32_t>(ws, R.hist);
     rb.bad = at<int32_t>(ws, R.bad);
     rb.mtile_off = at<int32_t>(ws, R.mtile_off);
@@ -595,10 +676,11 @@ int moe_ffn_bwd_workspace_size(const moe_ffn_problem *p, uint32_t flags, size_t 
 // the workspace; W computes the weight gradients from them.
 static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const void *x,
                    const float *topk_weights, const void *up_proj_weight,
-                   const void *down_proj_weight, const void *saved, void *dx,
-                   void *d_up_proj_weight, void *d_down_proj_weight, float *d_topk_weights,
-                   void *ws, size_t ws_bytes, uint32_t flags, void *stream,
-                   const moe_ffn_stage_events *ev)
+                   const void *down_proj_weight, const moe_ffn_shared_weights *sh,
+                   const void *saved, void *dx, void *d_up_proj_weight,
+                   void *d_down_proj_weight, float *d_topk_weights,
+                   const moe_ffn_shared_grads *sg, void *ws, size_t ws_bytes, uint32_t flags,
+                   void *stream, const moe_ffn_stage_events *ev)
 {
     g_err[0] = 0;
     int rc = validate_problem(p);
@@ -606,6 +688,18 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
         return rc;
     if (p->dtype != MOE_FFN_BF16)
         return fail(MOE_FFN_ERR_DTYPE, "the backward supports bf16 problems only");
+    const int S = nshared(*p);
+    if (S > 0 && stage != moe::BWD_STAGE_ALL)
+        return fail(MOE_FFN_ERR_SHAPE, "the split backward serves problems without a shared expert");
+    if (S > 0 && (!sh || !sg))
+        return fail(MOE_FFN_ERR_NULL, "a problem with Is > 0 needs the shared weights and gradients");
+    if (S > 0 && ((rc = check_ptr(sg->d_up_proj_weight, "d_shared_up_proj_weight")) ||
+                  (rc = check_ptr(sg->d_down_proj_weight, "d_shared_down_proj_weight"))))
+        return rc;
+    if (S > 0 && p->T > 0 &&
+        ((rc = check_ptr(sh->up_proj_weight, "shared up_proj_weight")) ||
+         (rc = check_ptr(sh->down_proj_weight, "shared down_proj_weight"))))
+        return rc;
     const bool do_d = stage != moe::BWD_STAGE_W, do_w = stage != moe::BWD_STAGE_D;
     const BwdLayout B = bwd_layout(*p);
     const FwdLayout L = fwd_layout(*p);
@@ -634,6 +728,11 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
         if (do_w) {
             HIP_TRY(moe::launch_zero_fill(d_up_proj_weight, 2 * dw_bytes, s), "zero fill");
             HIP_TRY(moe::launch_zero_fill(d_down_proj_weight, dw_bytes, s), "zero fill");
+        }
+        if (S > 0) {
+            const size_t sw_bytes = 2 * (size_t)p->Is * (size_t)p->H;
+            HIP_TRY(moe::launch_zero_fill(sg->d_up_proj_weight, 2 * sw_bytes, s), "zero fill");
+            HIP_TRY(moe::launch_zero_fill(sg->d_down_proj_weight, sw_bytes, s), "zero fill");
         }
         return MOE_FFN_OK;
     }
@@ -674,9 +773,11 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
     float *dgp = at<float>(ws, B.dgp);
     moe::bf16_t *dxp = at<moe::bf16_t>(ws, B.dxp);
 
-    HIP_TRY(moe::launch_bwd_setup(hdr, phash, saved_counts, saved_offsets, E, p->T * p->K, B.BM,
-                                  counts, offsets, mtile_off, mtile_expert, bstatus, whdr, stage,
-                                  s),
+    const int Ep = E + S; // experts of the plan: routed, then the shared chunks
+    const int64_t Is = p->Is;
+    HIP_TRY(moe::launch_bwd_setup(hdr, phash, saved_counts, saved_offsets, Ep,
+                                  p->T * p->K + (int64_t)S * p->T, B.BM, counts, offsets,
+                                  mtile_off, mtile_expert, bstatus, whdr, stage, s),
             "backward set-up launch");
     (void)counts;
 
@@ -686,7 +787,8 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
     base.mtile_off = mtile_off;
     base.mtile_expert = mtile_expert;
     base.topk = (int)p->K;
-    base.E = E;
+    base.E = Ep;
+    base.Er = E;
 
     if (do_d) {
         // act_grad with the SwiGLU backward in its epilogue: dh, act_g, d_g partials
@@ -704,6 +806,11 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
         a2.lda = H;
         a2.ldb = H;
         a2.b_estride = (int64_t)I * H;
+        if (S > 0) { // shared chunk c: rows [cI, cI + I) of the shared down_proj
+            a2.Bs = static_cast<const moe::bf16_t *>(sh->down_proj_weight);
+            a2.bs_cstride = (int64_t)I * H;
+            a2.bs_ldb = H;
+        }
         record(ev, MOE_FFN_STAGE_BWD_ACT_GRAD, true, s);
         HIP_TRY(moe::launch_engine(moe::ENG_B2, B.BM, a2, num_cus, s), "act_grad launch");
         record(ev, MOE_FFN_STAGE_BWD_ACT_GRAD, false, s);
@@ -719,13 +826,19 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
         a4.ldb = 2 * I;
         a4.ldc = H;
         a4.b_estride = (int64_t)H * 2 * I;
+        if (S > 0) { // shared chunk c: gate columns cI.., up columns Is + cI.. of its rows
+            a4.Bs = static_cast<const moe::bf16_t *>(sh->up_proj_weight);
+            a4.bs_cstride = I;
+            a4.bs_ldb = (int)(2 * Is);
+            a4.bs_kjump = (int)(Is - I);
+        }
         record(ev, MOE_FFN_STAGE_BWD_INPUT_GRAD, true, s);
         HIP_TRY(moe::launch_engine(moe::ENG_B4, B.BM, a4, num_cus, s), "input_grad launch");
         record(ev, MOE_FFN_STAGE_BWD_INPUT_GRAD, false, s);
 
         record(ev, MOE_FFN_STAGE_BWD_COMBINE, true, s);
         HIP_TRY(moe::launch_combine_bwd(dxp, dgp, B.dgp_width, slot_pos, bstatus, dx,
-                                        d_topk_weights, p->T, H, (int)p->K, s),
+                                        d_topk_weights, p->T, H, (int)p->K, offsets, E, S, s),
                 "dx combine launch");
         record(ev, MOE_FFN_STAGE_BWD_COMBINE, false, s);
     }
@@ -739,6 +852,11 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
         a5.N = H;
         a5.lda = I;
         a5.ldb = H;
+        if (S > 0) { // shared chunk c: rows [cI, cI + I) of the shared down_proj gradient
+            a5.Cs = static_cast<moe::bf16_t *>(sg->d_down_proj_weight);
+            a5.cs_cstride = (int64_t)I * H;
+            a5.cs_ldc = H;
+        }
         record(ev, MOE_FFN_STAGE_BWD_W2_GRAD, true, s);
         HIP_TRY(moe::launch_engine(moe::ENG_B5, B.BM, a5, num_cus, s), "W2Grad launch");
         record(ev, MOE_FFN_STAGE_BWD_W2_GRAD, false, s);
@@ -752,6 +870,12 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
         a7.N = 2 * I;
         a7.lda = H;
         a7.ldb = 2 * I;
+        if (S > 0) { // shared chunk c: its gate and up column chunks of the shared gradient
+            a7.Cs = static_cast<moe::bf16_t *>(sg->d_up_proj_weight);
+            a7.cs_cstride = I;
+            a7.cs_ldc = (int)(2 * Is);
+            a7.cs_cjump = (int)(Is - I);
+        }
         record(ev, MOE_FFN_STAGE_BWD_W1_GRAD, true, s);
         HIP_TRY(moe::launch_engine(moe::ENG_B7, B.BM, a7, num_cus, s), "W1Grad launch");
         record(ev, MOE_FFN_STAGE_BWD_W1_GRAD, false, s);
@@ -774,9 +898,11 @@ int moe_ffn_bwd_ex(const moe_ffn_problem *p, const void *dy, const void *x, cons
         if (rc)
             return rc;
     }
+    if (p && p->Is != 0)
+        return fail(MOE_FFN_ERR_SHAPE, "Is != 0: use moe_ffn_bwd_shared");
     return bwd_run(p, moe::BWD_STAGE_ALL, dy, x, topk_weights, up_proj_weight, down_proj_weight,
-                   saved, dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights, ws, ws_bytes,
-                   flags, stream, ev);
+                   nullptr, saved, dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights,
+                   nullptr, ws, ws_bytes, flags, stream, ev);
 }
 
 int moe_ffn_bwd(const moe_ffn_problem *p, const void *dy, const void *x, const void *topk_ids,
@@ -796,17 +922,36 @@ int moe_ffn_bwd_d(const moe_ffn_problem *p, const void *dy, const float *topk_we
                   void *stream)
 {
     return bwd_run(p, moe::BWD_STAGE_D, dy, nullptr, topk_weights, up_proj_weight,
-                   down_proj_weight, saved, dx, nullptr, nullptr, d_topk_weights, ws, ws_bytes,
-                   flags, stream, nullptr);
+                   down_proj_weight, nullptr, saved, dx, nullptr, nullptr, d_topk_weights,
+                   nullptr, ws, ws_bytes, flags, stream, nullptr);
 }
 
 int moe_ffn_bwd_w(const moe_ffn_problem *p, const void *dy, const void *x, const void *saved,
                   void *d_up_proj_weight, void *d_down_proj_weight, void *ws, size_t ws_bytes,
                   uint32_t flags, void *stream)
 {
-    return bwd_run(p, moe::BWD_STAGE_W, dy, x, nullptr, nullptr, nullptr, saved, nullptr,
-                   d_up_proj_weight, d_down_proj_weight, nullptr, ws, ws_bytes, flags, stream,
-                   nullptr);
+    return bwd_run(p, moe::BWD_STAGE_W, dy, x, nullptr, nullptr, nullptr, nullptr, saved,
+                   nullptr, d_up_proj_weight, d_down_proj_weight, nullptr, nullptr, ws, ws_bytes,
+                   flags, stream, nullptr);
+}
+
+int moe_ffn_bwd_shared(const moe_ffn_problem *p, const void *dy, const void *x,
+                       const void *topk_ids, const float *topk_weights,
+                       const void *up_proj_weight, const void *down_proj_weight,
+                       const moe_ffn_shared_weights *shared, const void *saved, void *dx,
+                       void *d_up_proj_weight, void *d_down_proj_weight, float *d_topk_weights,
+                       const moe_ffn_shared_grads *d_shared, void *ws, size_t ws_bytes,
+                       uint32_t flags, void *stream)
+{
+    const size_t id_align = p && p->ids_dtype == MOE_FFN_I64 ? 8 : 4;
+    if (p && p->T > 0) {
+        int rc = check_ptr(topk_ids, "topk_ids", id_align);
+        if (rc)
+            return rc;
+    }
+    return bwd_run(p, moe::BWD_STAGE_ALL, dy, x, topk_weights, up_proj_weight, down_proj_weight,
+                   shared, saved, dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights,
+                   d_shared, ws, ws_bytes, flags, stream, nullptr);
 }
 
 int moe_ffn_read_status(const void *ws, void *stream, int32_t *device_status)

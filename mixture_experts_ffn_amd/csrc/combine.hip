@@ -1,6 +1,7 @@
 // combine.hip — unpermute and top-k gate-weighted combine.
 //
 // y[t, :] = Σ_{k = 0..K-1} g[t, k] · o[slot_pos[t·K + k], :]
+//           + Σ_{c = 0..S-1} o[offsets[Er] + c·T + t, :]   (shared expert, if any)
 //
 // (HyperMegaMoE issue page, section 2.1 "Combine" and section 4.1: expert
 // outputs go back to their token and are summed with the routing weights.)
@@ -23,7 +24,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ o,
                                                       const int32_t *__restrict__ slot_pos,
                                                       const float *__restrict__ gates,
-                                                      T *__restrict__ y, int H, int K)
+                                                      T *__restrict__ y, int H, int K,
+                                                      const int32_t *__restrict__ offsets,
+                                                      int Er, int S, int64_t ntok)
 {
     constexpr int VEC = 16 / (int)sizeof(T);
     const int64_t t = blockIdx.x;
@@ -55,6 +58,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ o,
                 acc[j] += g * to_f32<T>(vv[j]);
         }
     }
+    // the shared expert's chunks (issue page, section 6.1: merged at combine),
+    // gate 1, after the routed terms
+    if (S > 0) {
+        const int64_t base = offsets[Er] + t;
+        for (int sc = 0; sc < S; ++sc) {
+            const u32x4 v =
+                *reinterpret_cast<const u32x4 *>(o + (base + sc * ntok) * H + (int64_t)c * VEC);
+            const T *vv = reinterpret_cast<const T *>(&v);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+                acc[j] += to_f32<T>(vv[j]);
+        }
+    }
     u32x4 out;
     T *oo = reinterpret_cast<T *>(&out);
 #pragma unroll
@@ -75,7 +91,9 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16 *__restrict
                                                           const int32_t *__restrict__ slot_pos,
                                                           const int32_t *__restrict__ status,
                                                           bf16 *__restrict__ dx,
-                                                          float *__restrict__ d_topk, int H, int K)
+                                                          float *__restrict__ d_topk, int H, int K,
+                                                          const int32_t *__restrict__ offsets,
+                                                          int Er, int S, int64_t ntok)
 {
     // grid: (token, block of 256 16-byte chunks); the first chunk block of a
     // token also finishes its d_topk_weights
@@ -108,6 +126,18 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16 *__restrict
                         acc[j] += static_cast<float>(vv[j]);
                 }
             }
+            // the shared expert's chunks, after the routed terms
+            if (S > 0) {
+                const int64_t base = offsets[Er] + t;
+                for (int sc = 0; sc < S; ++sc) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(
+                        dxp + (base + sc * ntok) * H + (int64_t)c * 8);
+                    const bf16 *vv = reinterpret_cast<const bf16 *>(&v);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        acc[j] += static_cast<float>(vv[j]);
+                }
+            }
         }
         u32x4 out;
         bf16 *oo = reinterpret_cast<bf16 *>(&out);
@@ -132,14 +162,15 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const bf16 *__restrict
 
 hipError_t launch_combine_bwd(const void *dxp, const float *dgp, int dgp_stride,
                               const int32_t *slot_pos, const int32_t *status, void *dx,
-                              float *d_topk, int64_t T, int H, int K, hipStream_t stream)
+                              float *d_topk, int64_t T, int H, int K, const int32_t *offsets,
+                              int Er, int S, hipStream_t stream)
 {
     if (T <= 0)
         return hipSuccess;
     const unsigned cblocks = (unsigned)((H / 8 + 255) / 256);
     hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)T, cblocks), dim3(256), 0, stream,
                        static_cast<const bf16 *>(dxp), dgp, dgp_stride, slot_pos, status,
-                       static_cast<bf16 *>(dx), d_topk, H, K);
+                       static_cast<bf16 *>(dx), d_topk, H, K, offsets, Er, S, T);
     return hipGetLastError();
 }
 
@@ -162,7 +193,8 @@ hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t stream)
 }
 
 hipError_t launch_combine(int dtype, const void *o, const int32_t *slot_pos, const float *gates,
-                          void *y, int64_t T, int H, int K, hipStream_t stream)
+                          void *y, int64_t T, int H, int K, const int32_t *offsets, int Er, int S,
+                          hipStream_t stream)
 {
     if (T <= 0)
         return hipSuccess;
@@ -171,11 +203,11 @@ hipError_t launch_combine(int dtype, const void *o, const int32_t *slot_pos, con
     if (dtype == 1)
         hipLaunchKernelGGL(combine_kernel<bf16>, dim3((unsigned)T, cblocks), dim3(256), 0, stream,
                            static_cast<const bf16 *>(o), slot_pos, gates, static_cast<bf16 *>(y), H,
-                           K);
+                           K, offsets, Er, S, T);
     else
         hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)T, cblocks), dim3(256), 0, stream,
                            static_cast<const float *>(o), slot_pos, gates, static_cast<float *>(y),
-                           H, K);
+                           H, K, offsets, Er, S, T);
     return hipGetLastError();
 }
 

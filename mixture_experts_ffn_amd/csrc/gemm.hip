@@ -119,13 +119,17 @@ __global__ __launch_bounds__(kWave *WM *WN, 2) void grouped_gemm_kernel(GroupedG
     const int row0 = args.offsets[e] + m_t * BM;
     const int rows = min(BM, seg1 - row0);
     const int n0 = n_t * BN;
-    const int Kdim = args.Kdim, Nout = args.Nout, ldb = args.ldb;
+    // a shared-expert chunk (e >= Er) reads its chunk of the shared weights
+    const bool shd = args.Bs && e >= args.Er;
+    const int Kdim = args.Kdim, Nout = args.Nout, ldb = shd ? args.bs_ldb : args.ldb;
+    const int upanel = shd ? args.bs_panel : Nout; // GEMM1: column offset of the up panel
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
 
     const T *__restrict__ A = static_cast<const T *>(args.A);
-    const T *__restrict__ Bw = static_cast<const T *>(args.B) + (int64_t)e * Kdim * ldb;
+    const T *__restrict__ Bw = shd ? static_cast<const T *>(args.Bs) + (int64_t)(e - args.Er) * args.bs_cstride
+                                   : static_cast<const T *>(args.B) + (int64_t)e * Kdim * ldb;
 
     // ---- per-thread load assignments (fixed for the whole K loop)
     const T *a_src[Cfg::A_CPT];
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(kWave *WM *WN, 2) void grouped_gemm_kernel(GroupedG
         const int nn = (nc % (BN / VEC)) * VEC;
         const int col = n0 + nn;
         b_ok[i] = col < Nout;
-        b_src[i] = Bw + (int64_t)(kg * KR) * ldb + panel * Nout + (b_ok[i] ? col : 0);
+        b_src[i] = Bw + (int64_t)(kg * KR) * ldb + panel * upanel + (b_ok[i] ? col : 0);
         b_k[i] = kg * KR;
         b_lds[i] = (panel * BN + nn) * LDK + kg * KR;
     }

@@ -273,6 +273,8 @@ template <int KIND, int BM, int WM> struct Src {
     int b_k[C::B_LOADS];
     bool a_col_ok[C::A_LOADS]; // KCOL: column inside the problem
     bool b_col_ok[C::B_LOADS];
+    int64_t ldb; // row stride of the tile's weight operand
+    int kjump;   // KROW weights: extra offset of k >= Kd / 2 (shared up_proj chunk in B4)
 };
 
 // Row indices of the gathered token-row KCOL operand of a weight gradient
@@ -379,6 +381,14 @@ __device__ __forceinline__ void make_src(const EngineArgs &a, const TileInfo &t,
         }
     }
     // ---- B
+    // weight operand of the tile's expert: a shared-expert chunk (e >= Er) reads
+    // its chunk of the shared weights with their own strides
+    const bool shd = KT::TOKEN_M && a.Bs && t.e >= a.Er;
+    const bf16_t *wbase = shd ? a.Bs + (int64_t)(t.e - a.Er) * a.bs_cstride
+                              : a.B + (int64_t)t.e * a.b_estride;
+    s.ldb = shd ? a.bs_ldb : a.ldb;
+    s.kjump = shd ? a.bs_kjump : 0;
+    const int upanel = shd ? a.bs_panel : a.N; // F1: column offset of the up panel
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i) {
         const int c = wave * C::B_LOADS + i;
@@ -388,7 +398,7 @@ __device__ __forceinline__ void make_src(const EngineArgs &a, const TileInfo &t,
             const int piece = krow_piece<C::KPIECES>(r, lane % C::KPIECES);
             const int n = t.n0 + r;
             const int nc = n < a.N ? n : 0; // tail columns repeat column 0; never stored
-            s.b[i] = a.B + (int64_t)t.e * a.b_estride + (int64_t)nc * a.ldb + piece * 8;
+            s.b[i] = wbase + (int64_t)nc * s.ldb + piece * 8;
             s.b_k[i] = piece * 8;
             s.b_col_ok[i] = true;
         } else {
@@ -406,11 +416,10 @@ __device__ __forceinline__ void make_src(const EngineArgs &a, const TileInfo &t,
             const int colp = t.n0 + (2 * u + (pp & 1)) * 8; // column within the panel
             s.b_col_ok[i] = colp < a.N;
             s.b_k[i] = 0;
-            const int col = (s.b_col_ok[i] ? colp : 0) + panel * a.N;
             if constexpr (KT::TOKEN_M) // weight operand: memory rows are k
-                s.b[i] = a.B + (int64_t)t.e * a.b_estride + (int64_t)kr * a.ldb + col;
+                s.b[i] = wbase + (int64_t)kr * s.ldb + (s.b_col_ok[i] ? colp : 0) + panel * upanel;
             else // token operand: memory row looked up per step
-                s.b[i] = a.B + col;
+                s.b[i] = a.B + (s.b_col_ok[i] ? colp : 0) + panel * a.N;
         }
     }
 }
@@ -457,12 +466,16 @@ __device__ __forceinline__ void issue(const EngineArgs &a, const TileInfo &t,
         lds_void *dst = (lds_void *)(sbase + C::A_BYTES + (wave * C::B_LOADS + i) * 1024);
         const void *src;
         if constexpr (KT::BLAY == KROW) {
-            src = (k0 + s.b_k[i] < t.klen) ? (const void *)(s.b[i] + k0) : (const void *)kZeroPage;
+            const int kk = k0 + s.b_k[i];
+            const bf16_t *p = s.b[i] + k0;
+            if constexpr (KIND == B4) // a shared up_proj chunk: the up half starts Is - I further on
+                p += kk >= (a.Kd >> 1) ? s.kjump : 0;
+            src = kk < t.klen ? (const void *)p : (const void *)kZeroPage;
         } else if constexpr (KT::TOKEN_M) {
             constexpr int RB = C::PW * 2;
             const int c = wave * C::B_LOADS + i;
             const int kr = KT::PAIRED ? (c % C::KCPP) * 4 + (lane >> 4) : kcol_krow<RB>(c, lane);
-            src = (s.b_col_ok[i] && k0 + kr < t.klen) ? (const void *)(s.b[i] + (int64_t)k0 * a.ldb)
+            src = (s.b_col_ok[i] && k0 + kr < t.klen) ? (const void *)(s.b[i] + (int64_t)k0 * s.ldb)
                                                        : (const void *)kZeroPage;
         } else {
             constexpr int RB = C::PW * 2;
@@ -550,10 +563,14 @@ __device__ __forceinline__ void epilogue(const EngineArgs &a, const TileInfo &t,
                 hbv[fm][fn] = *reinterpret_cast<const u32x2 *>(a.Hs + p * 2 * I + I + cc);
             }
         }
+        // rows of the shared expert's chunks (from offsets[Er] on) have gate 1
+        const int64_t shared_row0 = a.Bs && a.Er < a.E ? (int64_t)ldc(a.offsets, a.Er) : INT64_MAX;
         float gv[C::FM];
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-            gv[fm] = a.gates[slot[fm]];
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int r = wm * C::WTM + fm * 16 + (lane & 15);
+            gv[fm] = t.m0 + r >= shared_row0 ? 1.0f : a.gates[slot[fm]];
+        }
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
             const int r = wm * C::WTM + fm * 16 + (lane & 15);
@@ -595,7 +612,12 @@ __device__ __forceinline__ void epilogue(const EngineArgs &a, const TileInfo &t,
         }
     } else if constexpr (KIND == B5 || KIND == B7) {
         // weight gradient tile of expert e: rows m, columns n of dW[e] [M, N]
-        bf16 *dW = a.C + (int64_t)t.e * a.M * a.N;
+        // a shared-expert chunk writes its rows (B5) or its gate and up column
+        // chunks (B7) of the shared gradient
+        const bool shd = a.Cs && t.e >= a.Er;
+        bf16 *dW = shd ? a.Cs + (int64_t)(t.e - a.Er) * a.cs_cstride : a.C + (int64_t)t.e * a.M * a.N;
+        const int64_t ldw = shd ? a.cs_ldc : a.N;
+        const int cjump = shd ? a.cs_cjump : 0;
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
             const int r = wm * C::WTM + fm * 16 + (lane & 15);
@@ -606,7 +628,7 @@ __device__ __forceinline__ void epilogue(const EngineArgs &a, const TileInfo &t,
             for (int fn = 0; fn < C::FN; ++fn) {
                 const int c = t.n0 + wn * C::WTN + fn * 16 + cl;
                 if (c < a.N)
-                    *reinterpret_cast<u32x2 *>(dW + m * a.N + c) =
+                    *reinterpret_cast<u32x2 *>(dW + m * ldw + c + (c >= (a.N >> 1) ? cjump : 0)) =
                         pack4(acc[0][fm][fn][0], acc[0][fm][fn][1], acc[0][fm][fn][2],
                               acc[0][fm][fn][3]);
             }

@@ -353,11 +353,19 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
                 sr.a[i] = static_cast<const bf16 *>(args.act) + grow * I + piece * 8;
             }
         }
-        const bf16 *W = g1 ? static_cast<const bf16 *>(args.w1) + (int64_t)t.e * H * (2 * I)
-                           : static_cast<const bf16 *>(args.w2) + (int64_t)t.e * I * H;
-        sr.ldb = g1 ? 2 * I : H;
+        // a shared-expert chunk c = e - Er reads its column chunk of the shared
+        // up_proj (rows of 2Is, up panel Is columns in) or its row chunk of the
+        // shared down_proj
+        const bool shd = args.sh.S > 0 && t.e >= args.sh.Er;
+        const int64_t sc = t.e - args.sh.Er;
+        const bf16 *W =
+            g1 ? (shd ? static_cast<const bf16 *>(args.sh.w1) + sc * I
+                      : static_cast<const bf16 *>(args.w1) + (int64_t)t.e * H * (2 * I))
+               : (shd ? static_cast<const bf16 *>(args.sh.w2) + sc * I * H
+                      : static_cast<const bf16 *>(args.w2) + (int64_t)t.e * I * H);
+        sr.ldb = g1 ? 2 * (shd ? args.sh.Is : I) : H;
         sr.coherent_a = PIPE && !g1;
-        const int pstride = g1 ? I : PW; // column offset of the second panel
+        const int pstride = g1 ? (shd ? args.sh.Is : I) : PW; // column offset of the second panel
 #pragma unroll
         for (int i = 0; i < C::B_LOADS; ++i) {
             // chunk c covers 1024 bytes = 4 k-rows of one 128-column panel

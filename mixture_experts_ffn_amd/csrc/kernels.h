@@ -23,6 +23,22 @@ struct SavedHeader {
 constexpr uint32_t kSavedMagic = 0x46454f4du; // "MOEF"
 constexpr uint32_t kSavedVersion = 2u;
 
+// The optional shared expert (issue page, section 6.1) of intermediate width
+// Is = S * I, run as S extra experts Er .. Er + S - 1 that every token reaches
+// with gate 1: expert Er + c uses gate columns [cI, cI + I) and up columns
+// [Is + cI, Is + cI + I) of w1 [H, 2Is] and rows [cI, cI + I) of w2 [Is, H].
+// Its rows follow the routed ones in permuted order: row offsets[Er] + cT + t
+// is token t of chunk c.
+struct SharedExperts {
+    int Er = 0;              // routed experts; expert e >= Er is shared chunk e - Er
+    int S = 0;               // chunks (0: no shared expert)
+    int Is = 0;              // S * I
+    const void *w1 = nullptr; // [H, 2Is]
+    const void *w2 = nullptr; // [Is, H]
+    void *dw1 = nullptr;      // backward: [H, 2Is]
+    void *dw2 = nullptr;      // backward: [Is, H]
+};
+
 struct RoutePlan {
     int RC;    // slots per chunk (one wave per chunk)
     int NB;    // number of chunks
@@ -44,6 +60,8 @@ struct RouteBufs {
     SavedHeader *saved_hdr; // optional: header of the saved context, written here
     uint64_t problem_hash;
     uint64_t epoch;
+    int nshared = 0;        // shared-expert chunks S: experts E .. E+S-1 of T rows each
+    int64_t T = 0;          // tokens (rows of every shared chunk)
 };
 
 // bits of the device status word
@@ -79,6 +97,13 @@ struct GroupedGemmArgs {
     int topk;                    // K
     int E;
     int max_mtiles;              // upper bound of sum_e ceil(counts[e] / BM)
+    // shared-expert chunks (experts e >= Er; E counts them too): weights
+    // Bs + (e - Er) * bs_cstride, row stride bs_ldb, GEMM1's up panel bs_panel
+    // columns in
+    int Er;
+    const void *Bs;
+    int64_t bs_cstride;
+    int bs_ldb, bs_panel;
 };
 
 // plan-level tile choice for the forward
@@ -116,6 +141,7 @@ struct FastFwdArgs {
     int ids64;
     int max_mtiles;
     int drop_mt;                 // test hook: M-tile whose first GEMM1 release is dropped (-1)
+    SharedExperts sh;            // E counts the shared chunks too (sh.Er routed)
 };
 enum { FAST_G1 = 0, FAST_G2 = 1, FAST_PIPE = 2 };
 hipError_t launch_fast_fwd(int mode, int BM, const FastFwdArgs &a, int num_cus,
@@ -139,20 +165,36 @@ struct EngineArgs {
     int lda, ldb, ldc;
     int64_t b_estride;           // expert stride of a weight operand (elements)
     int dgp_stride;
+    // shared-expert chunks (experts e >= Er; E counts them too): their weight
+    // operand is Bs + (e - Er) * bs_cstride with row stride bs_ldb; F1: its up
+    // panel starts bs_panel columns in; B4: k >= Kd / 2 reads bs_kjump further
+    // on; B5/B7: the gradient goes to Cs + (e - Er) * cs_cstride with row
+    // stride cs_ldc, B7 columns >= N / 2 cs_cjump further on
+    int Er;
+    const bf16_t *Bs;
+    int64_t bs_cstride;
+    int bs_ldb, bs_panel, bs_kjump;
+    bf16_t *Cs;
+    int64_t cs_cstride;
+    int cs_ldc, cs_cjump;
 };
 enum { ENG_F1 = 0, ENG_F2 = 1, ENG_B2 = 2, ENG_B4 = 3, ENG_B5 = 4, ENG_B7 = 5 };
 hipError_t launch_engine(int kind, int BM, const EngineArgs &a, int num_cus, hipStream_t stream);
 int engine_dgp_width(int I); // columns of the B2 partial-dot buffer
 
 // ---- combine ---------------------------------------------------------------------
+// y[t] = Σ_k g[t, k] o[slot_pos[tK+k]] + Σ_c o[offsets[Er] + cT + t] (the S
+// shared-expert chunks, gate 1, after the routed terms; S = 0: none)
 hipError_t launch_combine(int dtype, const void *o, const int32_t *slot_pos, const float *gates,
-                          void *y, int64_t T, int H, int K, hipStream_t stream);
-// backward combine: dx[t] = Σ_k dxp[slot_pos[tK+k]] and
+                          void *y, int64_t T, int H, int K, const int32_t *offsets, int Er, int S,
+                          hipStream_t stream);
+// backward combine: dx[t] = Σ_k dxp[slot_pos[tK+k]] + Σ_c dxp[offsets[Er] + cT + t] and
 // d_topk[t, k] = Σ_j dgp[slot_pos[tK+k], j] (0 for a dropped slot)
 // (all zeros when *status has MOE_DEV_BAD_SAVED or MOE_DEV_BAD_WS)
 hipError_t launch_combine_bwd(const void *dxp, const float *dgp, int dgp_stride,
                               const int32_t *slot_pos, const int32_t *status, void *dx,
-                              float *d_topk, int64_t T, int H, int K, hipStream_t stream);
+                              float *d_topk, int64_t T, int H, int K, const int32_t *offsets,
+                              int Er, int S, hipStream_t stream);
 // zero `bytes` (a multiple of 16) at a 16-byte aligned pointer
 hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t stream);
 // Backward set-up (one block): checks the saved context's header and the

@@ -138,13 +138,17 @@ __device__ inline void write_header_and_counters(SavedHeader *hdr, uint64_t prob
 
 // counts, offsets, the M-tile tables and the status word, from expert e's
 // count c and exclusive offset off held by thread e (all 1024 threads of one
-// block call this; total = offsets[E]).
+// block call this; E counts the nsh shared-expert chunks, whose counts are T,
+// and total = offsets[E]).  The rows of the shared chunks follow the routed
+// ones: row offsets[E - nsh] + cT + t gets sorted_slot t·K, so the gather of a
+// GEMM (slot / K) reads token t.
 __device__ inline void publish_plan(int32_t c, int32_t off, int32_t total, bool anybad, int E,
                                     int BM, int32_t *__restrict__ counts,
                                     int32_t *__restrict__ offsets,
                                     int32_t *__restrict__ mtile_off,
                                     int32_t *__restrict__ mtile_expert,
-                                    int32_t *__restrict__ status, int32_t *s_w, int32_t *s_moff)
+                                    int32_t *__restrict__ status, int32_t *s_w, int32_t *s_moff,
+                                    int nsh, int64_t T, int K, int32_t *__restrict__ sorted_slot)
 {
     const int e = threadIdx.x;
     if (e < E) {
@@ -177,6 +181,9 @@ __device__ inline void publish_plan(int32_t c, int32_t off, int32_t total, bool 
         }
         mtile_expert[j] = lo;
     }
+    const int64_t routed = total - (int64_t)nsh * T;
+    for (int64_t i = threadIdx.x; i < (int64_t)nsh * T; i += 1024)
+        sorted_slot[routed + i] = (int32_t)((i % T) * K);
 }
 
 __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ hist,
@@ -189,7 +196,9 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ 
                                                           int32_t *__restrict__ status,
                                                           int32_t *__restrict__ ctr, int nctr,
                                                           SavedHeader *__restrict__ hdr,
-                                                          uint64_t problem_hash, uint64_t epoch)
+                                                          uint64_t problem_hash, uint64_t epoch,
+                                                          int nsh, int64_t T, int K,
+                                                          int32_t *__restrict__ sorted_slot)
 {
     write_header_and_counters(hdr, problem_hash, epoch, ctr, nctr);
     __shared__ int32_t s_cnt[1024];
@@ -216,11 +225,11 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ 
     anybad = __syncthreads_or(anybad);
 
     const int e = threadIdx.x;
-    const int32_t c = e < E ? s_cnt[e] : 0;
+    const int32_t c = e < E ? s_cnt[e] : e < E + nsh ? (int32_t)T : 0;
     int32_t total;
     const int32_t off = block_excl_scan(c, s_w, &total);
-    publish_plan(c, off, total, anybad, E, BM, counts, offsets, mtile_off, mtile_expert, status,
-                 s_w, s_moff);
+    publish_plan(c, off, total, anybad, E + nsh, BM, counts, offsets, mtile_off, mtile_expert,
+                 status, s_w, s_moff, nsh, T, K, sorted_slot);
 }
 
 // One wave routes the slots [s0, s1) in order, 64 at a time: lanes holding
@@ -305,8 +314,8 @@ __global__ __launch_bounds__(1024) void route_block_kernel(
     const int32_t *__restrict__ hist, const int32_t *__restrict__ bad,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ mtile_off,
     int32_t *__restrict__ mtile_expert, int32_t *__restrict__ status, int32_t *__restrict__ ctr,
-    int nctr, SavedHeader *__restrict__ hdr, uint64_t problem_hash, uint64_t epoch,
-    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_pos)
+    int nctr, SavedHeader *__restrict__ hdr, uint64_t problem_hash, uint64_t epoch, int nsh,
+    int64_t T, int K, int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_pos)
 {
     extern __shared__ int32_t lds[];
     int32_t *tab = lds;         // [E][16]: chunk counts, then chunk bases
@@ -381,13 +390,13 @@ __global__ __launch_bounds__(1024) void route_block_kernel(
     }
     anybad = __syncthreads_or(anybad);
 
-    const int e = threadIdx.x; // E <= 1024
-    const int32_t c = e < E ? tot[e] : 0;
+    const int e = threadIdx.x; // E + nsh <= 1024
+    const int32_t c = e < E ? tot[e] : e < E + nsh ? (int32_t)T : 0;
     int32_t total;
     const int32_t off = block_excl_scan(c, s_w, &total);
     if (lead)
-        publish_plan(c, off, total, anybad, E, BM, counts, offsets, mtile_off, mtile_expert,
-                     status, s_w, s_moff);
+        publish_plan(c, off, total, anybad, E + nsh, BM, counts, offsets, mtile_off,
+                     mtile_expert, status, s_w, s_moff, nsh, T, K, sorted_slot);
     if (e < E) {
         int32_t run = off + bef[e];
 #pragma unroll
@@ -523,6 +532,7 @@ static void launch_route_t(const Id *ids, int64_t TK, int E, int BM, const Route
 {
     const size_t lds = sizeof(int32_t) * (size_t)E;
     const size_t lds_block = sizeof(int32_t) * (size_t)E * 18; // tab[E][16], tot[E], bef[E]
+    const int K = rb.T > 0 ? (int)(TK / rb.T) : 1;
     const int nctr = rb.ctr ? rb.nctr : 0;
     if (TK > 0 && lds_block <= 65536) {
         if (rp.NB > 16)
@@ -533,13 +543,14 @@ static void launch_route_t(const Id *ids, int64_t TK, int E, int BM, const Route
             hipLaunchKernelGGL((route_block_kernel<Id, true>), dim3(1), dim3(1024), lds_block, stream,
                                ids, TK, E, rp.nbits, rp.RC, rp.NB, BM, rb.hist, rb.bad, rb.counts,
                                rb.offsets, rb.mtile_off, rb.mtile_expert, rb.status, rb.ctr, nctr,
-                               rb.saved_hdr, rb.problem_hash, rb.epoch, rb.sorted_slot, rb.slot_pos);
+                               rb.saved_hdr, rb.problem_hash, rb.epoch, rb.nshared, rb.T, K,
+                               rb.sorted_slot, rb.slot_pos);
         else
             hipLaunchKernelGGL((route_block_kernel<Id, false>), dim3(nblk), dim3(1024), lds_block,
                                stream, ids, TK, E, rp.nbits, rp.RC, rp.NB, BM, rb.hist, rb.bad,
                                rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert, rb.status,
                                rb.ctr, nctr, rb.saved_hdr, rb.problem_hash, rb.epoch,
-                               rb.sorted_slot, rb.slot_pos);
+                               rb.nshared, rb.T, K, rb.sorted_slot, rb.slot_pos);
         return;
     }
     // many experts (the block table would not fit), or no slots: hist, scan, scatter
@@ -549,7 +560,8 @@ static void launch_route_t(const Id *ids, int64_t TK, int E, int BM, const Route
     const int nb_scan = TK > 0 ? rp.NB : 0;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, rb.hist, rb.bad, E,
                        nb_scan, BM, rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert,
-                       rb.status, rb.ctr, nctr, rb.saved_hdr, rb.problem_hash, rb.epoch);
+                       rb.status, rb.ctr, nctr, rb.saved_hdr, rb.problem_hash, rb.epoch,
+                       rb.nshared, rb.T, K, rb.sorted_slot);
     if (TK > 0)
         hipLaunchKernelGGL(route_scatter_kernel<Id>, dim3(rp.NB), dim3(64), lds, stream, ids, TK, E,
                            rp.nbits, rp.RC, rp.NB, rb.hist, rb.offsets, rb.sorted_slot,
