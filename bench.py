@@ -88,6 +88,7 @@ def main():
 
     d = {k: to_dev(v) for k, v in inp.items()}
     prob = m.make_problem(d["x"], d["topk_ids"], d["up_proj"], d["down_proj"])
+    prob.Is = w.Is
     ws_bytes, _ = m.fwd_workspace_size(prob)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
@@ -95,15 +96,19 @@ def main():
     if w.backward:
         bws = torch.empty(max(m.bwd_workspace_size(prob), 1), dtype=torch.uint8, device=dev)
 
+    sh = ({"shared_up_proj_weight": d["shared_up"], "shared_down_proj_weight": d["shared_down"]}
+          if w.Is else {})
+
     def step(ev=None, bev=None, pipelined=False):
         if not w.backward:
             return m.moe_ffn_fwd(d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
-                                 d["down_proj"], ws=ws, stage_events=ev, pipelined=pipelined)
+                                 d["down_proj"], ws=ws, stage_events=ev, pipelined=pipelined,
+                                 **sh)
         y, saved = m.moe_ffn_fwd(d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
                                  d["down_proj"], ws=ws, stage_events=ev, save_for_backward=True,
-                                 pipelined=pipelined)
+                                 pipelined=pipelined, **sh)
         m.moe_ffn_bwd(d["dy"], d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
-                      d["down_proj"], saved, ws=bws, stage_events=bev)
+                      d["down_proj"], saved, ws=bws, stage_events=bev, **sh)
         return y
 
     def stats(ms):
@@ -210,7 +215,8 @@ def main():
     live = counts > 0
     es = 2 if w.dtype == "bf16" else 4
     layer_flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
-    layer_bytes = live.sum() * 3 * w.H * w.I * es + 2 * w.T * w.H * es + w.T * w.K * 8
+    layer_bytes = ((live.sum() * w.I + w.Is) * 3 * w.H * es + 2 * w.T * w.H * es
+                   + w.T * w.K * 8)
     if pipelined:
         # dominant kernel: the pipelined forward's one launch (both grouped GEMMs
         # and the combine); algorithmic work = the forward's flops, or for the
@@ -221,8 +227,10 @@ def main():
         kernel = "moe::fast::moe_fwd_bf16<BM, FAST_PIPE> (GEMM1+SwiGLU, GEMM2, combine)"
     else:
         # dominant kernel: the gathered up_proj GEMM with the SwiGLU epilogue
-        k_flops = 4.0 * w.T * w.K * w.H * w.I
-        k_bytes = live.sum() * w.H * 2 * w.I * es + w.T * w.H * es + w.T * w.K * w.I * es
+        # (one launch covers the routed experts and the shared expert's chunks)
+        k_flops = 4.0 * w.T * w.H * (w.K * w.I + w.Is)
+        k_bytes = ((live.sum() * w.I + w.Is) * w.H * 2 * es + w.T * w.H * es
+                   + w.T * (w.K * w.I + w.Is) * es)
         k_ms = stage_ms["gemm1"]
         kernel = ("moe::fast::moe_fwd_bf16<BM, FAST_G1> (gathered up_proj GEMM + SwiGLU)"
                   if w.dtype == "bf16" and w.H % 256 == 0 and w.I % 128 == 0 else
@@ -294,13 +302,15 @@ def main():
 
 def dense_reference(w, dev, reps=20):
     """Context only: torch.matmul (the vendor BLAS) on the dense bf16 GEMMs of the
-    same total size, [T*K, H] x [H, 2I] and [T*K, I] x [I, H], as an achievable
+    same total size, [R, H] x [H, 2I] and [R, I] x [I, H] with R = T*K (+ T*Is/I
+    with a shared expert), as an achievable
     rate for comparison with the grouped kernels."""
     import torch
 
     out = {}
-    for name, (M, Kd, N) in {"gemm1": (w.T * w.K, w.H, 2 * w.I),
-                             "gemm2": (w.T * w.K, w.I, w.H)}.items():
+    rows = w.T * w.K + w.T * (w.Is // w.I)  # the shared expert's chunks add T rows each
+    for name, (M, Kd, N) in {"gemm1": (rows, w.H, 2 * w.I),
+                             "gemm2": (rows, w.I, w.H)}.items():
         a = torch.randn(M, Kd, device=dev, dtype=torch.bfloat16)
         b = torch.randn(Kd, N, device=dev, dtype=torch.bfloat16)
         for _ in range(3):
@@ -363,8 +373,13 @@ def cpu_baseline(w, inp, y_gpu, target_s):
 
     def run(n):
         t0 = time.perf_counter()
-        yo = oracle.forward(inp["x"][:n], inp["topk_ids"][:n], inp["topk_weights"][:n],
-                            inp["up_proj"], inp["down_proj"])
+        if w.Is:
+            yo = oracle.forward_shared(inp["x"][:n], inp["topk_ids"][:n],
+                                       inp["topk_weights"][:n], inp["up_proj"], inp["down_proj"],
+                                       inp["shared_up"], inp["shared_down"])
+        else:
+            yo = oracle.forward(inp["x"][:n], inp["topk_ids"][:n], inp["topk_weights"][:n],
+                                inp["up_proj"], inp["down_proj"])
         return yo, time.perf_counter() - t0
 
     n = min(w.T, 8)

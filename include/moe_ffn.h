@@ -197,13 +197,14 @@ typedef struct {
     void *d_down_proj_weight; /* [Is, H], overwritten */
 } moe_ffn_shared_grads;
 
-/* moe_ffn_fwd with a shared expert (p->Is > 0; with Is == 0 it is moe_ffn_fwd). */
+/* moe_ffn_fwd_ex with a shared expert (p->Is > 0; with Is == 0 it is
+ * moe_ffn_fwd_ex); ev may be NULL. */
 int moe_ffn_fwd_shared(const moe_ffn_problem *p, const void *x, const void *topk_ids,
                        const float *topk_weights, const void *up_proj_weight,
                        const void *down_proj_weight, const moe_ffn_shared_weights *shared,
                        void *y, void *saved, void *ws, size_t ws_bytes, uint32_t flags,
-                       void *stream);
-/* moe_ffn_bwd with a shared expert: also the shared weights' gradients; dx
+                       void *stream, const moe_ffn_stage_events *ev);
+/* moe_ffn_bwd_ex with a shared expert (ev may be NULL): also the shared weights' gradients; dx
  * includes the shared expert's contribution, d_topk_weights does not involve
  * it.  `saved` must come from moe_ffn_fwd_shared for the same problem. */
 int moe_ffn_bwd_shared(const moe_ffn_problem *p, const void *dy, const void *x,
@@ -212,7 +213,7 @@ int moe_ffn_bwd_shared(const moe_ffn_problem *p, const void *dy, const void *x,
                        const moe_ffn_shared_weights *shared, const void *saved, void *dx,
                        void *d_up_proj_weight, void *d_down_proj_weight, float *d_topk_weights,
                        const moe_ffn_shared_grads *d_shared, void *ws, size_t ws_bytes,
-                       uint32_t flags, void *stream);
+                       uint32_t flags, void *stream, const moe_ffn_stage_events *ev);
 
 /* ---- routing alone -------------------------------------------------------- */
 

@@ -118,9 +118,10 @@ def load_library():
                                ctypes.POINTER(StageEvents)],
             "moe_ffn_bwd_d": [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
             "moe_ffn_fwd_shared": [pp, vp, vp, vp, vp, vp, ctypes.POINTER(SharedWeights), vp, vp,
-                                   vp, sz, u32, vp],
+                                   vp, sz, u32, vp, ctypes.POINTER(StageEvents)],
             "moe_ffn_bwd_shared": [pp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(SharedWeights), vp,
-                                   vp, vp, vp, vp, ctypes.POINTER(SharedGrads), vp, sz, u32, vp],
+                                   vp, vp, vp, vp, ctypes.POINTER(SharedGrads), vp, sz, u32, vp,
+                                   ctypes.POINTER(StageEvents)],
             "moe_ffn_bwd_w": [pp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
             "moe_ffn_route": [pp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_ffn_read_status": [vp, vp, ctypes.POINTER(ctypes.c_int32)],
@@ -254,8 +255,6 @@ def moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *,
         raise MoEFFNError(3, "topk_weights must be float32 with the shape of topk_ids")
     prob = make_problem(x, topk_ids, up_proj_weight, down_proj_weight)
     sw = _shared_problem(prob, x, shared_up_proj_weight, shared_down_proj_weight)
-    if sw is not None and stage_events is not None:
-        raise MoEFFNError(2, "stage_events is not available with a shared expert")
     ws_bytes, saved_bytes = fwd_workspace_size(prob)
     dev = x.device
     y = torch.empty_like(x)
@@ -271,7 +270,8 @@ def moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *,
             rc = lib.moe_ffn_fwd_shared(ctypes.byref(prob), _ptr(x), _ptr(topk_ids),
                                         _ptr(topk_weights), _ptr(up_proj_weight),
                                         _ptr(down_proj_weight), ctypes.byref(sw), _ptr(y),
-                                        _ptr(saved), _ptr(ws), ws.numel(), flags, _stream(dev))
+                                        _ptr(saved), _ptr(ws), ws.numel(), flags, _stream(dev),
+                                        ev)
         else:
             rc = lib.moe_ffn_fwd_ex(ctypes.byref(prob), _ptr(x), _ptr(topk_ids),
                                     _ptr(topk_weights), _ptr(up_proj_weight),
@@ -314,8 +314,6 @@ def moe_ffn_bwd(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
     if dy.shape != x.shape or dy.dtype != x.dtype:
         raise MoEFFNError(2, "dy must have the shape and dtype of x")
     sw = _shared_problem(prob, x, shared_up_proj_weight, shared_down_proj_weight)
-    if sw is not None and stage_events is not None:
-        raise MoEFFNError(2, "stage_events is not available with a shared expert")
     ws_bytes = bwd_workspace_size(prob)
     dev = x.device
     dx = torch.empty_like(x)
@@ -336,7 +334,7 @@ def moe_ffn_bwd(dy, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight,
                                         _ptr(down_proj_weight), ctypes.byref(sw), _ptr(saved),
                                         _ptr(dx), _ptr(d_up), _ptr(d_down), _ptr(d_topk),
                                         ctypes.byref(sg), _ptr(ws), ws.numel(), flags,
-                                        _stream(dev))
+                                        _stream(dev), ev)
         else:
             rc = lib.moe_ffn_bwd_ex(ctypes.byref(prob), _ptr(dy), _ptr(x), _ptr(topk_ids),
                                     _ptr(topk_weights), _ptr(up_proj_weight),

@@ -583,10 +583,10 @@ int moe_ffn_fwd_shared(const moe_ffn_problem *p, const void *x, const void *topk
                        const float *topk_weights, const void *up_proj_weight,
                        const void *down_proj_weight, const moe_ffn_shared_weights *shared,
                        void *y, void *saved, void *ws, size_t ws_bytes, uint32_t flags,
-                       void *stream)
+                       void *stream, const moe_ffn_stage_events *ev)
 {
     return fwd_run(p, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, shared, y,
-                   saved, ws, ws_bytes, flags, stream, nullptr);
+                   saved, ws, ws_bytes, flags, stream, ev);
 }
 
 int moe_ffn_fwd(const moe_ffn_problem *p, const void *x, const void *topk_ids,
@@ -941,7 +941,7 @@ int moe_ffn_bwd_shared(const moe_ffn_problem *p, const void *dy, const void *x,
                        const moe_ffn_shared_weights *shared, const void *saved, void *dx,
                        void *d_up_proj_weight, void *d_down_proj_weight, float *d_topk_weights,
                        const moe_ffn_shared_grads *d_shared, void *ws, size_t ws_bytes,
-                       uint32_t flags, void *stream)
+                       uint32_t flags, void *stream, const moe_ffn_stage_events *ev)
 {
     const size_t id_align = p && p->ids_dtype == MOE_FFN_I64 ? 8 : 4;
     if (p && p->T > 0) {
@@ -951,7 +951,7 @@ int moe_ffn_bwd_shared(const moe_ffn_problem *p, const void *dy, const void *x,
     }
     return bwd_run(p, moe::BWD_STAGE_ALL, dy, x, topk_weights, up_proj_weight, down_proj_weight,
                    shared, saved, dx, d_up_proj_weight, d_down_proj_weight, d_topk_weights,
-                   d_shared, ws, ws_bytes, flags, stream, nullptr);
+                   d_shared, ws, ws_bytes, flags, stream, ev);
 }
 
 int moe_ffn_read_status(const void *ws, void *stream, int32_t *device_status)

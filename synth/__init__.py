@@ -77,11 +77,12 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
     def fwd_flops(self) -> float:
-        """Algorithmic forward flops: 2*TK*H*2I (up) + 2*TK*I*H (down)."""
-        return 6.0 * self.T * self.K * self.H * self.I
+        """Algorithmic forward flops: 2*TK*H*2I (up) + 2*TK*I*H (down), plus
+        6*T*H*Is for a shared expert."""
+        return 6.0 * self.T * self.H * (self.K * self.I + self.Is)
 
     def bwd_flops(self) -> float:
-        return 12.0 * self.T * self.K * self.H * self.I
+        return 12.0 * self.T * self.H * (self.K * self.I + self.Is)
 
 
 # The five workloads of the study: a tiny fp32 case, a prefill shape, a
@@ -96,6 +97,11 @@ WORKLOADS = {
                  zipf_s=1.2, n_empty=3),
         Workload("decode_bf16", 3, T=128, H=7168, I=2048, E=32, K=8),
         Workload("fwdbwd_bf16", 4, T=4096, H=4096, I=1536, E=16, K=4, backward=True),
+        # the prefill and forward+backward shapes with a shared expert of width
+        # 2I and I (the pages give no size; these are common choices)
+        Workload("prefill_shared_bf16", 5, T=4096, H=2048, I=1408, E=64, K=6, Is=2816),
+        Workload("fwdbwd_shared_bf16", 6, T=4096, H=4096, I=1536, E=16, K=4, backward=True,
+                 Is=1536),
     ]
 }
 

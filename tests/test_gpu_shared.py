@@ -120,8 +120,8 @@ def test_shared_with_zero_tokens(gpu_lib):
 
 
 def test_shared_forward_prefill_size_sampled(gpu_lib):
-    w = WORKLOADS["prefill_bf16"].with_(Is=2 * WORKLOADS["prefill_bf16"].I)
-    say("[shared-full] generating prefill_bf16 with Is = 2I")
+    w = WORKLOADS["prefill_shared_bf16"]
+    say("[shared-full] generating prefill_shared_bf16 (Is = 2I)")
     inp = make_inputs(w)
     d = to_device(inp)
     say("[shared-full] running")
@@ -134,3 +134,43 @@ def test_shared_forward_prefill_size_sampled(gpu_lib):
     err = max_rel_err(host_f64(y[torch.from_numpy(toks).cuda()]), ref)
     say(f"[shared-full] sampled 16 tokens max_rel_err={err:.3e}")
     assert err <= TOL["bf16"]
+
+
+def test_shared_backward_full_size_sampled(gpu_lib):
+    # the forward+backward shape with Is = I; every gradient on sampled rows or
+    # columns (the shared part is the routed definition at one expert, gate 1)
+    w = WORKLOADS["fwdbwd_shared_bf16"]
+    say("[shared-bwd-full] generating fwdbwd_shared_bf16")
+    inp = make_inputs(w, with_dy=True)
+    d = to_device(inp)
+    say(f"[shared-bwd-full] running T={w.T} H={w.H} I={w.I} E={w.E} K={w.K} Is={w.Is}")
+    _, saved = fwd(gpu_lib, d, save_for_backward=True)
+    dx, d_up, d_down, d_topk, ds_up, ds_down = gpu_lib.moe_ffn_bwd(
+        d["dy"], d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"], d["down_proj"], saved,
+        shared_up_proj_weight=d["shared_up"], shared_down_proj_weight=d["shared_down"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    toks = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, 10, replace=False)]))
+    w1c = [(int(rng.integers(w.E)), int(j)) for j in [0, w.I, 2 * w.I - 1]]
+    w2r = [(int(rng.integers(w.E)), int(i)) for i in [0, w.I - 1]]
+    rx, rg, r1, r2 = oracle.backward_sampled(inp["dy"], inp["x"], inp["topk_ids"],
+                                             inp["topk_weights"], inp["up_proj"],
+                                             inp["down_proj"], toks, w1c, w2r)
+    sc = [0, w.Is - 1, w.Is, 2 * w.Is - 1] + [int(j) for j in rng.choice(2 * w.Is, 4)]
+    sr = [0, w.Is - 1] + [int(i) for i in rng.choice(w.Is, 4)]
+    ids1 = np.zeros((w.T, 1), np.int32)
+    g1 = np.ones((w.T, 1), np.float32)
+    sx, _, s1, s2 = oracle.backward_sampled(inp["dy"], inp["x"], ids1, g1,
+                                            inp["shared_up"][None], inp["shared_down"][None],
+                                            toks, [(0, j) for j in sc], [(0, i) for i in sr])
+    tk = torch.from_numpy(toks).cuda()
+    errs = dict(
+        dx=max_rel_err(host_f64(dx[tk]), rx + sx),
+        d_topk=max_rel_err(d_topk[tk].double().cpu().numpy(), rg),
+        d_up=max_rel_err(np.stack([host_f64(d_up[e, :, j]) for e, j in w1c]), r1),
+        d_down=max_rel_err(np.stack([host_f64(d_down[e, i, :]) for e, i in w2r]), r2),
+        d_shared_up=max_rel_err(np.stack([host_f64(ds_up[:, j]) for j in sc]), s1),
+        d_shared_down=max_rel_err(np.stack([host_f64(ds_down[i, :]) for i in sr]), s2))
+    say("[shared-bwd-full] " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()))
+    for n, e in errs.items():
+        assert e <= TOL["bf16"], (n, e)
