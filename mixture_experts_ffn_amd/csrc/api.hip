@@ -251,7 +251,8 @@ struct BwdLayout {
     int BM;
     int64_t max_mtiles;
     int dgp_width;
-    size_t status, whdr, counts, offsets, mtile_off, mtile_expert, dh, act_g, dgp, dxp, total;
+    size_t status, whdr, counts, offsets, mtile_off, mtile_expert, xcd_bounds, dh, act_g, dgp, dxp,
+        total;
 };
 
 BwdLayout bwd_layout(const moe_ffn_problem &p)
@@ -274,6 +275,7 @@ BwdLayout bwd_layout(const moe_ffn_problem &p)
     B.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
     B.mtile_off = take(sizeof(int32_t) * (size_t)(E + 1));
     B.mtile_expert = take(sizeof(int32_t) * (size_t)B.max_mtiles);
+    B.xcd_bounds = take(sizeof(int32_t) * 2 * 9);
     B.dh = take(2 * (size_t)TK * (size_t)(2 * p.I));
     B.act_g = take(2 * (size_t)TK * (size_t)p.I);
     B.dgp = take(sizeof(float) * (size_t)TK * (size_t)B.dgp_width);
@@ -775,9 +777,15 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
 
     const int Ep = E + S; // experts of the plan: routed, then the shared chunks
     const int64_t Is = p->Is;
+    // XCD bounds of the two weight-gradient launches (W2Grad, W1Grad)
+    moe::XcdSplits splits{};
+    splits.n = 2;
+    splits.bounds = at<int32_t>(ws, B.xcd_bounds);
+    moe::engine_feature_tiling(moe::ENG_B5, I, H, num_cus, &splits.F[0], &splits.wgx[0]);
+    moe::engine_feature_tiling(moe::ENG_B7, H, 2 * I, num_cus, &splits.F[1], &splits.wgx[1]);
     HIP_TRY(moe::launch_bwd_setup(hdr, phash, saved_counts, saved_offsets, Ep,
                                   p->T * p->K + (int64_t)S * p->T, B.BM, counts, offsets,
-                                  mtile_off, mtile_expert, bstatus, whdr, stage, s),
+                                  mtile_off, mtile_expert, bstatus, whdr, stage, splits, s),
             "backward set-up launch");
     (void)counts;
 
@@ -852,6 +860,7 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
         a5.N = H;
         a5.lda = I;
         a5.ldb = H;
+        a5.xcd_bounds = splits.bounds;
         if (S > 0) { // shared chunk c: rows [cI, cI + I) of the shared down_proj gradient
             a5.Cs = static_cast<moe::bf16_t *>(sg->d_down_proj_weight);
             a5.cs_cstride = (int64_t)I * H;
@@ -870,6 +879,7 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
         a7.N = 2 * I;
         a7.lda = H;
         a7.ldb = 2 * I;
+        a7.xcd_bounds = splits.bounds + 9;
         if (S > 0) { // shared chunk c: its gate and up column chunks of the shared gradient
             a7.Cs = static_cast<moe::bf16_t *>(sg->d_up_proj_weight);
             a7.cs_cstride = I;

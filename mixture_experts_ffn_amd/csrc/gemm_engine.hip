@@ -262,6 +262,27 @@ __device__ __forceinline__ int total_tiles(const EngineArgs &a)
         return a.E * ((a.M + BM - 1) / BM) * ntn;
 }
 
+// The contiguous tile range [lo, hi) of XCD x: an eighth of the tile count, or,
+// for the feature-tiled kinds when the backward set-up has computed them, the
+// cost-balanced bounds in a.xcd_bounds (a weight-gradient tile's K loop runs
+// over its expert's rows, so its cost follows the routing).
+template <int KIND, int BM, int WM>
+__device__ __forceinline__ void xcd_range(const EngineArgs &a, int x, int &lo, int &hi)
+{
+    using C = Cfg<KIND, BM, WM>;
+    if constexpr (!C::KT::TOKEN_M) {
+        if (a.xcd_bounds) {
+            lo = ldc(a.xcd_bounds, x);
+            hi = ldc(a.xcd_bounds, x + 1);
+            return;
+        }
+    }
+    const int total = uni(total_tiles<KIND, BM, WM>(a));
+    const int range = (total + 7) >> 3;
+    lo = min(x * range, total);
+    hi = min((x + 1) * range, total);
+}
+
 // Per-lane copy state of one tile.  KROW operands and weight operands are
 // affine in k, so one pointer per chunk suffices; token-row KCOL operands
 // (the weight gradients) look their rows up per K step.
@@ -677,12 +698,13 @@ __global__ __launch_bounds__(64 * Shape<KIND>::NW, Shape<KIND>::WGPC) void engin
     constexpr int BK = C::BK;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * C::STAGE_BYTES];
 
-    const int total = uni(total_tiles<KIND, BM, WM>(a));
     const int per_xcd_wg = gridDim.x >> 3;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int range = (total + 7) >> 3;
-    const int hi = min((xcd + 1) * range, total);
-    const int L0 = xcd * range + slot;
+    int lo, hi;
+    xcd_range<KIND, BM, WM>(a, xcd, lo, hi);
+    lo = uni(lo);
+    hi = uni(hi);
+    const int L0 = lo + slot;
     if (L0 >= hi)
         return;
 
@@ -838,6 +860,17 @@ static hipError_t launch(const EngineArgs &a, int num_cus, hipStream_t stream)
 }
 
 } // namespace eng
+
+void engine_feature_tiling(int kind, int M, int N, int num_cus, int *tiles_per_expert,
+                           int *wg_per_xcd)
+{
+    using namespace eng;
+    // the weight-gradient kinds launch with 128-row feature tiles (launch_engine)
+    const int out_n = kind == ENG_B5 ? Cfg<B5, 128, 2>::OUT_N : Cfg<B7, 128, 2>::OUT_N;
+    const int wgpc = kind == ENG_B5 ? Shape<B5>::WGPC : Shape<B7>::WGPC;
+    *tiles_per_expert = ((M + 127) / 128) * ((N + out_n - 1) / out_n);
+    *wg_per_xcd = (num_cus + 7) / 8 * wgpc;
+}
 
 int engine_dgp_width(int I) { return ((I + 255) / 256) * eng::Cfg<eng::B2, 128, 2>::WAVES_N; }
 

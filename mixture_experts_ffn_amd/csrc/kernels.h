@@ -177,10 +177,17 @@ struct EngineArgs {
     bf16_t *Cs;
     int64_t cs_cstride;
     int cs_ldc, cs_cjump;
+    // feature-tiled kinds, optional: [9] tile bounds of the eight XCDs (from
+    // the backward set-up); null: an eighth of the tiles each
+    const int32_t *xcd_bounds;
 };
 enum { ENG_F1 = 0, ENG_F2 = 1, ENG_B2 = 2, ENG_B4 = 3, ENG_B5 = 4, ENG_B7 = 5 };
 hipError_t launch_engine(int kind, int BM, const EngineArgs &a, int num_cus, hipStream_t stream);
 int engine_dgp_width(int I); // columns of the B2 partial-dot buffer
+// a weight-gradient kind's (ENG_B5 / ENG_B7) feature tiles per expert for an
+// M x N gradient, and its workgroups per XCD
+void engine_feature_tiling(int kind, int M, int N, int num_cus, int *tiles_per_expert,
+                           int *wg_per_xcd);
 
 // ---- combine ---------------------------------------------------------------------
 // y[t] = Σ_k g[t, k] o[slot_pos[tK+k]] + Σ_c o[offsets[Er] + cT + t] (the S
@@ -205,10 +212,21 @@ hipError_t launch_zero_fill(void *p, size_t bytes, hipStream_t stream);
 // (BWD_STAGE_D) writes it (zeros if the saved context failed its check); the
 // weight-gradient stage (BWD_STAGE_W) requires it to equal the saved header,
 // else the copies are zero and *status gets MOE_DEV_BAD_WS.
+// It also writes, for each of `nsplit` (<= 2) weight-gradient launches with
+// split_F[i] feature tiles per expert and split_wgx[i] workgroups per XCD, the
+// nine tile bounds of a cost-balanced split over the eight XCDs into
+// xcd_bounds[9 i .. 9 i + 8].
 enum { BWD_STAGE_ALL = 0, BWD_STAGE_D = 1, BWD_STAGE_W = 2 };
+struct XcdSplits {
+    int n;          // launches (0..2)
+    int F[2];       // feature tiles per expert
+    int wgx[2];     // workgroups per XCD
+    int32_t *bounds; // [n][9]
+};
 hipError_t launch_bwd_setup(const SavedHeader *hdr, uint64_t problem_hash, const int32_t *counts,
                             const int32_t *offsets, int E, int64_t TK, int BM, int32_t *counts_out,
                             int32_t *offsets_out, int32_t *mtile_off, int32_t *mtile_expert,
-                            int32_t *status, SavedHeader *ws_hdr, int stage, hipStream_t stream);
+                            int32_t *status, SavedHeader *ws_hdr, int stage,
+                            const XcdSplits &splits, hipStream_t stream);
 
 } // namespace moe

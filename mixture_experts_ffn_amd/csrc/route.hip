@@ -427,9 +427,11 @@ __global__ __launch_bounds__(1024) void bwd_setup_kernel(
     const int32_t *__restrict__ offsets, int E, int64_t TK, int BM,
     int32_t *__restrict__ counts_out, int32_t *__restrict__ offsets_out,
     int32_t *__restrict__ mtile_off, int32_t *__restrict__ mtile_expert,
-    int32_t *__restrict__ status, SavedHeader *__restrict__ ws_hdr, int stage)
+    int32_t *__restrict__ status, SavedHeader *__restrict__ ws_hdr, int stage, XcdSplits splits)
 {
     __shared__ int32_t s_moff[1025];
+    __shared__ int32_t s_off[1025];
+    __shared__ int32_t s_raw[2][8];
     __shared__ int32_t s_w[40];
     __shared__ int s_hdr_ok, s_ws_ok;
     if (threadIdx.x == 0) {
@@ -461,9 +463,11 @@ __global__ __launch_bounds__(1024) void bwd_setup_kernel(
     if (e < E) {
         counts_out[e] = c;
         offsets_out[e] = off;
+        s_off[e] = off;
     }
     if (e == 0) {
         offsets_out[E] = ok ? offsets[E] : 0;
+        s_off[E] = ok ? offsets[E] : 0;
         status[0] = ok ? 0 : !(s_hdr_ok && !bad) ? MOE_DEV_BAD_SAVED : MOE_DEV_BAD_WS;
         if (stage == BWD_STAGE_D) {
             // the stamp the weight-gradient stage will check (zeros: nothing to trust)
@@ -496,16 +500,68 @@ __global__ __launch_bounds__(1024) void bwd_setup_kernel(
         }
         mtile_expert[j] = lo;
     }
+
+    // Cost-balanced XCD bounds of the weight-gradient launches.  A tile of
+    // expert e contracts over its count[e] rows; its cost is modelled as
+    // count[e] + TILE_EPS rows (TILE_EPS for the epilogue and tile switch), so
+    // with F tiles per expert the cost before tile e F + j is
+    // F (off[e] + e TILE_EPS) + j (count[e] + TILE_EPS).  XCD x starts at the
+    // first tile whose cost prefix reaches x/8 of the total; that start is then
+    // moved to a whole number of rounds of the XCD's workgroups (a multiple of
+    // wgx tiles from the previous bound, when there are two rounds or more), so
+    // that tiles of equal cost split evenly over the workgroups.
+    constexpr int TILE_EPS = 64;
+    if (splits.n > 0) {
+        const int k = threadIdx.x >> 3, x = threadIdx.x & 7;
+        if (k < splits.n && x > 0) {
+            const int64_t F = k == 0 ? splits.F[0] : splits.F[1];
+            auto prefix = [&](int ex) { return F * ((int64_t)s_off[ex] + (int64_t)ex * TILE_EPS); };
+            const int64_t target = prefix(E) * x / 8;
+            int lo = 0, hi = E; // largest ex in [0, E] with prefix(ex) <= target
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (prefix(mid) <= target)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            int64_t L = (int64_t)E * F;
+            if (lo < E) {
+                const int64_t w = (int64_t)(s_off[lo + 1] - s_off[lo]) + TILE_EPS;
+                const int64_t j = (target - prefix(lo) + w - 1) / w;
+                L = lo * F + (j < F ? j : F);
+            }
+            s_raw[k][x] = (int32_t)L;
+        }
+        __syncthreads();
+        if (threadIdx.x < splits.n) {
+            const int kk = threadIdx.x;
+            const int F = kk == 0 ? splits.F[0] : splits.F[1];
+            const int wgx = kk == 0 ? splits.wgx[0] : splits.wgx[1];
+            const int32_t total = E * F;
+            int32_t b = 0;
+            splits.bounds[9 * kk] = 0;
+            for (int xx = 1; xx < 8; ++xx) {
+                int32_t n = max(s_raw[kk][xx], b) - b;
+                if (n >= 2 * wgx)
+                    n = (n + wgx / 2) / wgx * wgx;
+                b = min(b + n, total);
+                splits.bounds[9 * kk + xx] = b;
+            }
+            splits.bounds[9 * kk + 8] = total;
+        }
+    }
 }
 
 hipError_t launch_bwd_setup(const SavedHeader *hdr, uint64_t problem_hash, const int32_t *counts,
                             const int32_t *offsets, int E, int64_t TK, int BM, int32_t *counts_out,
                             int32_t *offsets_out, int32_t *mtile_off, int32_t *mtile_expert,
-                            int32_t *status, SavedHeader *ws_hdr, int stage, hipStream_t stream)
+                            int32_t *status, SavedHeader *ws_hdr, int stage,
+                            const XcdSplits &splits, hipStream_t stream)
 {
     hipLaunchKernelGGL(bwd_setup_kernel, dim3(1), dim3(1024), 0, stream, hdr, problem_hash, counts,
                        offsets, E, TK, BM, counts_out, offsets_out, mtile_off, mtile_expert, status,
-                       ws_hdr, stage);
+                       ws_hdr, stage, splits);
     return hipGetLastError();
 }
 
