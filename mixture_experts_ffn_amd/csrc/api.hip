@@ -288,7 +288,7 @@ BwdLayout bwd_layout(const moe_ffn_problem &p)
 // carries from the forward to the backward
 uint64_t problem_hash(const moe_ffn_problem &p)
 {
-    const int64_t v[7] = {p.T, p.H, p.I, p.E, p.K, p.dtype, p.ids_dtype};
+    const int64_t v[8] = {p.T, p.H, p.I, p.E, p.K, p.dtype, p.ids_dtype, p.Is};
     uint64_t h = 1469598103934665603ull;
     for (int64_t x : v)
         for (int b = 0; b < 8; ++b) {

@@ -17,7 +17,7 @@ typedef __bf16 bf16_t;
 struct SavedHeader {
     uint32_t magic;
     uint32_t version;
-    uint64_t problem; // hash of (T, H, I, E, K, dtype, ids_dtype)
+    uint64_t problem; // hash of (T, H, I, E, K, dtype, ids_dtype, Is)
     uint64_t epoch;   // distinct for every forward that saves a context
 };
 constexpr uint32_t kSavedMagic = 0x46454f4du; // "MOEF"

@@ -174,3 +174,28 @@ def test_shared_backward_full_size_sampled(gpu_lib):
     say("[shared-bwd-full] " + " ".join(f"{k}={v:.3e}" for k, v in errs.items()))
     for n, e in errs.items():
         assert e <= TOL["bf16"], (n, e)
+
+
+def test_shared_backward_rejects_a_routed_only_saved_context(gpu_lib):
+    # the saved context of the same batch's forward without the shared expert
+    # (its problem hash differs in Is), padded to the shared layout's size
+    inp = make_inputs(workload("sh_foreign", 643, 300, 256, 128, 8, 2, 256), with_dy=True)
+    d = to_device(inp)
+    say("[shared] routed-only saved context")
+    _, saved_s = fwd(gpu_lib, d, save_for_backward=True)
+    _, saved_r = gpu_lib.moe_ffn_fwd(d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
+                                     d["down_proj"], save_for_backward=True)
+    foreign = torch.zeros_like(saved_s)
+    foreign[:saved_r.numel()] = saved_r
+    torch.cuda.synchronize()
+    args = (d["dy"], d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"], d["down_proj"])
+    sh = dict(shared_up_proj_weight=d["shared_up"], shared_down_proj_weight=d["shared_down"])
+    with pytest.raises(gpu_lib.MoEFFNError) as ei:
+        gpu_lib.moe_ffn_bwd(*args, foreign, check_saved=True, **sh)
+    assert ei.value.status == 7
+    *grads, ws = gpu_lib.moe_ffn_bwd(*args, foreign, return_ws=True, **sh)
+    torch.cuda.synchronize()
+    assert gpu_lib.read_status(ws) == gpu_lib.DEV_BAD_SAVED
+    assert len(grads) == 6
+    for g in grads:
+        assert not g.float().abs().sum().item()
