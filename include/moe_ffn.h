@@ -99,6 +99,10 @@ typedef struct {
  * of one GEMM1 tile and uses a 20 ms watchdog, so that the waits behind it
  * time out (status MOE_FFN_DEV_TIMEOUT) while every kernel still ends. */
 #define MOE_FFN_TEST_DROP_RELEASE 0x100u
+/* Test hook: the fast-path forward kernels run as 16 workgroups (2 per XCD),
+ * so that each workgroup walks many tiles (and, in the pipelined launch, waits
+ * on many releases) at sizes a CPU reference checks in full. */
+#define MOE_FFN_TEST_SMALL_GRID 0x200u
 /* bwd: read the saved context's header on the host first (synchronising the
  * stream) and return MOE_FFN_ERR_SAVED, before anything is launched, if it was
  * not written by a forward of this problem.  Without the flag the same check

@@ -55,6 +55,7 @@ F32, BF16, I32, I64 = 0, 1, 2, 3
 CHECK_IDS = 0x1
 PIPELINE = 0x2
 TEST_DROP_RELEASE = 0x100
+TEST_SMALL_GRID = 0x200
 CHECK_SAVED = 0x4
 DEV_BAD_ID, DEV_TIMEOUT, DEV_BAD_SAVED, DEV_BAD_WS = 0x1, 0x2, 0x4, 0x8
 STAGES = ("route", "gemm1", "gemm2", "combine", "pipeline")

@@ -498,6 +498,7 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
         a.sh.w1 = S > 0 ? sh->up_proj_weight : nullptr;
         a.sh.w2 = S > 0 ? sh->down_proj_weight : nullptr;
         a.max_mtiles = (int)L.max_mtiles;
+        a.grid = (flags & MOE_FFN_TEST_SMALL_GRID) ? 16 : 0;
         a.drop_mt = (flags & MOE_FFN_TEST_DROP_RELEASE) ? 0 : -1;
         const int BM = L.tiles.BM;
         // the pipelined launch serves routed experts only; with a shared expert

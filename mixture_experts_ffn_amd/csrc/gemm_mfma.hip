@@ -747,7 +747,7 @@ template <int BM, int MODE, int NWAVES = waves_for(BM)>
 static hipError_t launch(const FastFwdArgs &a, int num_cus, hipStream_t stream)
 {
     // 8 / NWAVES workgroups per CU (8 waves per CU), whole XCDs
-    const int grid = (num_cus + 7) / 8 * 8 * (8 / NWAVES);
+    const int grid = a.grid > 0 ? a.grid : (num_cus + 7) / 8 * 8 * (8 / NWAVES);
     hipLaunchKernelGGL((moe_fwd_bf16<BM, MODE, NWAVES>), dim3((unsigned)grid), dim3(64 * NWAVES),
                        0, stream, a);
     return hipGetLastError();
