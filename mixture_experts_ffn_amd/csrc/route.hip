@@ -565,12 +565,24 @@ hipError_t launch_bwd_setup(const SavedHeader *hdr, uint64_t problem_hash, const
     return hipGetLastError();
 }
 
+// Chunk size: a chunk is one wave's serial work (rounds of 64 slots, each a
+// load, a few ballots and a dependent LDS update), so chunks are kept short
+// enough that many waves share it: up to 8192 slots spread over the 16 waves
+// of one block (at least 64 slots each), beyond that 128-slot chunks over
+// several blocks, doubled while there would be more than 4096 chunks.
 RoutePlan make_route_plan(int64_t TK, int E)
 {
     RoutePlan rp;
-    int64_t rc = 512;
-    while ((TK + rc - 1) / rc > 4096)
-        rc *= 2;
+    int64_t rc;
+    if (TK <= 8192) {
+        rc = ((TK + 15) / 16 + 63) / 64 * 64;
+        if (rc < 64)
+            rc = 64;
+    } else {
+        rc = 128;
+        while ((TK + rc - 1) / rc > 4096)
+            rc *= 2;
+    }
     rp.RC = (int)rc;
     rp.NB = (int)((TK + rc - 1) / rc);
     if (rp.NB < 1)
