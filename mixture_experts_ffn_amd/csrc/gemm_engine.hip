@@ -336,11 +336,15 @@ __device__ __forceinline__ void fetch_gather(const EngineArgs &a, const TileInfo
 // Memory row of the lane's k-row for a token-row KCOL operand (weight
 // gradients): k-rows kbase .. kbase + KPC - 1 of the chunk are permuted rows
 // seg0 + k; a gathered operand maps them through the prefetched indices.
-template <int RB>
-__device__ __forceinline__ int64_t kcol_token_row(const TileInfo &t, int kbase, int lane)
+// slot / topk for 0 <= slot < 2^31 by multiply and shift: with l = ceil(log2 d)
+// and m = floor(2^(31+l) / d) + 1 (set by launch_engine), floor(v m / 2^(31+l))
+// equals floor(v / d) for every v below 2^31 (Granlund and Montgomery,
+// "Division by invariant integers using multiplication", section 4).
+__device__ __forceinline__ int div_topk(int v, const EngineArgs &a)
 {
-    return (int64_t)t.seg0 + kbase + lane / (RB / 16);
+    return a.topk_l == 0 ? v : (int)(__umulhi((uint32_t)v, a.topk_m) >> (a.topk_l - 1));
 }
+
 template <int RB, typename G>
 __device__ __forceinline__ int64_t kcol_gather_row(const EngineArgs &a, int lane, const G &g, int i)
 {
@@ -351,7 +355,13 @@ __device__ __forceinline__ int64_t kcol_gather_row(const EngineArgs &a, int lane
 #pragma unroll
     for (int q = 1; q < KPC; ++q)
         v = j == q ? g.v[i * KPC + q] : v;
-    return (int64_t)(v / a.topk);
+    return (int64_t)div_topk(v, a);
+}
+
+// k-row of lane within chunk c for a KCOL operand with `RB`-byte k-rows
+template <int RB> __device__ __forceinline__ int kcol_krow(int c, int lane)
+{
+    return c * (1024 / RB) + lane / (RB / 16);
 }
 
 template <int KIND, int BM, int WM>
@@ -382,7 +392,7 @@ __device__ __forceinline__ void make_src(const EngineArgs &a, const TileInfo &t,
 #pragma unroll
                 for (int j = 1; j < KRPC; ++j)
                     v = lane / KPIECES == j ? idx[j] : v;
-                mrow = v / a.topk;
+                mrow = div_topk(v, a);
             } else {
                 mrow = t.m0 + (r < t.rows ? r : 0);
             }
@@ -397,7 +407,9 @@ __device__ __forceinline__ void make_src(const EngineArgs &a, const TileInfo &t,
             const int u = (pp >> 1) ^ bswz(c * KPC + lane / (RB / 16));
             const int col = t.m0 + (2 * u + (pp & 1)) * 8;
             s.a_col_ok[i] = col < a.M;
-            s.a[i] = a.A + (s.a_col_ok[i] ? col : 0); // row part added per step
+            s.a[i] = a.A + (s.a_col_ok[i] ? col : 0); // gathered: row part added per step
+            if constexpr (!GatherIdx<KIND, BM, WM>::ON_A) // token rows seg0 + k: k0 rows added per step
+                s.a[i] += ((int64_t)t.seg0 + kcol_krow<RB>(c, lane)) * a.lda;
             s.a_k[i] = 0;
         }
     }
@@ -439,16 +451,13 @@ __device__ __forceinline__ void make_src(const EngineArgs &a, const TileInfo &t,
             s.b_k[i] = 0;
             if constexpr (KT::TOKEN_M) // weight operand: memory rows are k
                 s.b[i] = wbase + (int64_t)kr * s.ldb + (s.b_col_ok[i] ? colp : 0) + panel * upanel;
-            else // token operand: memory row looked up per step
+            else if constexpr (GatherIdx<KIND, BM, WM>::ON_B) // gathered token operand: row per step
                 s.b[i] = a.B + (s.b_col_ok[i] ? colp : 0) + panel * a.N;
+            else // token rows seg0 + k: k0 rows added per step
+                s.b[i] = a.B + (s.b_col_ok[i] ? colp : 0) + panel * a.N +
+                         ((int64_t)t.seg0 + kcol_krow<C::PW * 2>(c, lane)) * a.ldb;
         }
     }
-}
-
-// k-row of lane within chunk c for a KCOL operand with `RB`-byte k-rows
-template <int RB> __device__ __forceinline__ int kcol_krow(int c, int lane)
-{
-    return c * (1024 / RB) + lane / (RB / 16);
 }
 
 template <int KIND, int BM, int WM>
@@ -471,13 +480,12 @@ __device__ __forceinline__ void issue(const EngineArgs &a, const TileInfo &t,
             constexpr int RB = BM * 2;
             const int kr = kcol_krow<RB>(wave * C::A_LOADS + i, lane);
             const int kk = k0 + kr;
-            int64_t mrow;
+            const bf16_t *p;
             if constexpr (G::ON_A)
-                mrow = kcol_gather_row<RB>(a, lane, g, i);
+                p = s.a[i] + kcol_gather_row<RB>(a, lane, g, i) * a.lda;
             else
-                mrow = kcol_token_row<RB>(t, k0 + (wave * C::A_LOADS + i) * (1024 / RB), lane);
-            src = (s.a_col_ok[i] && kk < t.klen) ? (const void *)(s.a[i] + mrow * a.lda)
-                                                  : (const void *)kZeroPage;
+                p = s.a[i] + (int64_t)k0 * a.lda;
+            src = (s.a_col_ok[i] && kk < t.klen) ? (const void *)p : (const void *)kZeroPage;
         }
         g2l16(src, dst);
     }
@@ -502,13 +510,12 @@ __device__ __forceinline__ void issue(const EngineArgs &a, const TileInfo &t,
             constexpr int RB = C::PW * 2;
             const int kr = kcol_krow<RB>(wave * C::B_LOADS + i, lane);
             const int kk = k0 + kr;
-            int64_t mrow;
+            const bf16_t *p;
             if constexpr (G::ON_B)
-                mrow = kcol_gather_row<RB>(a, lane, g, i);
+                p = s.b[i] + kcol_gather_row<RB>(a, lane, g, i) * a.ldb;
             else
-                mrow = kcol_token_row<RB>(t, k0 + (wave * C::B_LOADS + i) * (1024 / RB), lane);
-            src = (s.b_col_ok[i] && kk < t.klen) ? (const void *)(s.b[i] + mrow * a.ldb)
-                                                  : (const void *)kZeroPage;
+                p = s.b[i] + (int64_t)k0 * a.ldb;
+            src = (s.b_col_ok[i] && kk < t.klen) ? (const void *)p : (const void *)kZeroPage;
         }
         g2l16(src, dst);
     }
@@ -874,9 +881,15 @@ void engine_feature_tiling(int kind, int M, int N, int num_cus, int *tiles_per_e
 
 int engine_dgp_width(int I) { return ((I + 255) / 256) * eng::Cfg<eng::B2, 128, 2>::WAVES_N; }
 
-hipError_t launch_engine(int kind, int BM, const EngineArgs &a, int num_cus, hipStream_t stream)
+hipError_t launch_engine(int kind, int BM, const EngineArgs &args, int num_cus, hipStream_t stream)
 {
     using namespace eng;
+    // multiplier of the slot / topk divisions (div_topk)
+    EngineArgs a = args;
+    a.topk_l = 0;
+    while ((1 << a.topk_l) < a.topk)
+        ++a.topk_l;
+    a.topk_m = a.topk_l == 0 ? 0u : (uint32_t)((1ull << (31 + a.topk_l)) / (uint64_t)a.topk + 1);
     switch (kind) {
     case F1: return BM == 64 ? launch<F1, 64, 1>(a, num_cus, stream) : launch<F1, 128, 1>(a, num_cus, stream);
     case F2: return BM == 64 ? launch<F2, 64, 1>(a, num_cus, stream) : launch<F2, 128, 1>(a, num_cus, stream);

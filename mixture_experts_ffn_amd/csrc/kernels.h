@@ -162,6 +162,8 @@ struct EngineArgs {
     const int32_t *mtile_off;    // [E + 1] (token-tiled kinds)
     const int32_t *mtile_expert; // [max M-tiles]
     int topk, E;
+    uint32_t topk_m;             // set by launch_engine: slot / topk by multiply and shift
+    int topk_l;
     int M, N, Kd;                // feature-tiled: M, N; token-tiled: N and Kd
     int lda, ldb, ldc;
     int64_t b_estride;           // expert stride of a weight operand (elements)
