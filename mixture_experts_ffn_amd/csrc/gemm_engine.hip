@@ -322,14 +322,16 @@ __device__ __forceinline__ void fetch_gather(const EngineArgs &a, const TileInfo
 {
     using G = GatherIdx<KIND, BM, WM>;
     if constexpr (G::ON_A || G::ON_B) {
-        const int k0 = kb * Cfg<KIND, BM, WM>::BK;
+        // the wave's NCH x KPC k-rows are consecutive, so their indices are one
+        // block of sorted_slot, read as one wide scalar load; the block may run
+        // past the expert's rows (and up to 64 entries past the array, which
+        // is padded for this): those rows copy zeros whatever their index
+        const int base = uni(t.seg0 + kb * Cfg<KIND, BM, WM>::BK + wave * G::NCH * G::KPC);
+        const __attribute__((address_space(4))) int32_t *src =
+            (const __attribute__((address_space(4))) int32_t *)a.sorted_slot + base;
 #pragma unroll
-        for (int i = 0; i < G::NCH; ++i) {
-            const int kbase = k0 + (wave * G::NCH + i) * G::KPC;
-#pragma unroll
-            for (int q = 0; q < G::KPC; ++q) // rows past the expert's count: 0 (their pieces copy zeros)
-                g.v[i * G::KPC + q] = kbase + q < t.klen ? ldc(a.sorted_slot, t.seg0 + kbase + q) : 0;
-        }
+        for (int j = 0; j < G::NCH * G::KPC; ++j)
+            g.v[j] = src[j];
     }
 }
 
