@@ -200,9 +200,10 @@ FwdLayout fwd_layout(const moe_ffn_problem &p)
     L.offsets = take(sizeof(int32_t) * (size_t)(Ep + 1));
     L.mtile_off = take(sizeof(int32_t) * (size_t)(Ep + 1));
     L.mtile_expert = take(sizeof(int32_t) * (size_t)L.max_mtiles);
-    // sorted_slot (here and in the saved context) has 64 entries of padding: the
-    // weight-gradient kernels read their gather indices in whole blocks
-    L.sorted_slot = take(sizeof(int32_t) * ((size_t)TKp + 64));
+    // sorted_slot (here and in the saved context) has 256 entries of padding:
+    // the GEMMs read their gather indices in whole blocks (up to a tile's rows
+    // or a K step's past the end)
+    L.sorted_slot = take(sizeof(int32_t) * ((size_t)TKp + 256));
     L.slot_pos = take(sizeof(int32_t) * (size_t)TK);
     L.ctr = take(sizeof(int32_t) * 2 * (size_t)L.max_mtiles);
     L.act = take(es * (size_t)TKp * (size_t)p.I);
@@ -212,7 +213,7 @@ FwdLayout fwd_layout(const moe_ffn_problem &p)
     L.s_hdr = take(sizeof(moe::SavedHeader));
     L.s_counts = take(sizeof(int32_t) * (size_t)Ep);
     L.s_offsets = take(sizeof(int32_t) * (size_t)(Ep + 1));
-    L.s_sorted = take(sizeof(int32_t) * ((size_t)TKp + 64));
+    L.s_sorted = take(sizeof(int32_t) * ((size_t)TKp + 256));
     L.s_slotpos = take(sizeof(int32_t) * (size_t)TK);
     L.s_h = take(es * (size_t)TKp * (size_t)(2 * p.I));
     L.saved_total = off;

@@ -324,8 +324,8 @@ __device__ __forceinline__ void fetch_gather(const EngineArgs &a, const TileInfo
     if constexpr (G::ON_A || G::ON_B) {
         // the wave's NCH x KPC k-rows are consecutive, so their indices are one
         // block of sorted_slot, read as one wide scalar load; the block may run
-        // past the expert's rows (and up to 64 entries past the array, which
-        // is padded for this): those rows copy zeros whatever their index
+        // past the expert's rows (and up to a K step past the array, which is
+        // padded for this): those rows copy zeros whatever their index
         const int base = uni(t.seg0 + kb * Cfg<KIND, BM, WM>::BK + wave * G::NCH * G::KPC);
         const __attribute__((address_space(4))) int32_t *src =
             (const __attribute__((address_space(4))) int32_t *)a.sorted_slot + base;

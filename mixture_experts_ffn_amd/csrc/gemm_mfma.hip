@@ -338,12 +338,17 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
             const int r = c * C::RPC + lane / C::PIECES;
             const int piece = aswz<C::PIECES>(r, lane % C::PIECES);
             if (g1) {
-                // the chunk's row indices are wave-uniform: scalar loads
+                // the chunk's row indices are wave-uniform and consecutive: one
+                // wide scalar load (sorted_slot is padded past its end by more
+                // than a tile); rows past the expert's count copy row 0
+                const __attribute__((address_space(4))) int32_t *ix =
+                    (const __attribute__((address_space(4))) int32_t *)args.sorted_slot +
+                    uni(t.row0 + c * C::RPC);
+                const int idx0 = ldc(args.sorted_slot, t.row0);
                 int v = 0;
 #pragma unroll
                 for (int j = 0; j < C::RPC; ++j) {
-                    const int rj = c * C::RPC + j < t.rows ? c * C::RPC + j : 0; // tail rows copy row 0
-                    const int idx = ldc(args.sorted_slot, t.row0 + rj);
+                    const int idx = c * C::RPC + j < t.rows ? ix[j] : idx0;
                     v = lane / C::PIECES == j ? idx : v;
                 }
                 const int64_t grow = v / args.K;
