@@ -526,21 +526,27 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
         }
     };
 
-    // GEMM2's output tile of the bulk launch, written through LDS: in the MFMA
+    // The output tiles of the bulk launches, written through LDS: in the MFMA
     // layout a lane holds 4 columns of one row, so direct stores write 32-byte
     // pieces of 16 rows per instruction, and those stores measured a fifth of
-    // GEMM2's time.  Instead the tile passes through the LDS stage the last K
-    // step used (no copy of the next tile targets it before the next tile's
-    // first barrier) PR rows at a time, and is stored as whole 512-byte rows,
-    // 16 bytes per lane.  Same values, same rounding as the direct stores.
+    // GEMM2's time and a fourteenth of GEMM1's.  Instead the tile passes
+    // through the LDS stage the last K step used (no copy of the next tile
+    // targets it before the next tile's first barrier) PR rows at a time and
+    // is stored as whole rows, 16 bytes per lane: GEMM2's 256 output columns,
+    // GEMM1's 128 act columns (a GEMM1 that also saves the pre-activation for
+    // the backward keeps the direct stores).  Same values, same rounding.
     auto epilogue_staged = [&](const Tile &t, unsigned char *stg) {
-        constexpr int RS = TILE_N2 * 2 + 16; // bytes per staged row (padded against bank conflicts)
-        constexpr int PR = 32;               // rows per pass
-        constexpr int CPR = TILE_N2 * 2 / 16; // 16-byte chunks per row
-        constexpr int RD = PR * CPR / (NW * 64); // chunks each lane stores per pass
-        static_assert(PR * RS <= C::STAGE_BYTES && BM % PR == 0 && PR % 16 == 0, "staging");
-        static_assert(PR * CPR % (NW * 64) == 0, "staging reads");
-        bf16 *__restrict__ Cout = static_cast<bf16 *>(args.o);
+        const bool g1 = kind_of(t.kind) == KIND_G1;
+        constexpr int PR = 32;                                 // rows per pass
+        const int ncol = g1 ? TILE_N1 : TILE_N2;                // output columns of the tile
+        const int rs = ncol * 2 + 16;                           // bytes per staged row (padded)
+        const int cpr = ncol * 2 / 16;                          // 16-byte chunks per row
+        const int rd = PR * cpr / (NW * 64);                    // chunks each lane stores per pass
+        static_assert(PR * (TILE_N2 * 2 + 16) <= C::STAGE_BYTES && BM % PR == 0 && PR % 16 == 0,
+                      "staging");
+        static_assert(PR * (TILE_N1 * 2 / 16) % (NW * 64) == 0, "staging reads");
+        bf16 *__restrict__ Cout = static_cast<bf16 *>(g1 ? args.act : args.o);
+        const int ldo = g1 ? I : H;
         lds_barrier(); // every wave is done with the last K step's stage
 #pragma unroll 1
         for (int q = 0; q < BM / PR; ++q) {
@@ -551,28 +557,37 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
                     continue;
                 const int rl = rt - q * PR + (lane & 15);
 #pragma unroll
-                for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-                    for (int pn = 0; pn < 2; ++pn) {
-                        const int col = pn * PW + wn * C::WTN + fn * 16 + 4 * (lane >> 4);
+                for (int fn = 0; fn < C::FN; ++fn) {
+                    const int cw = wn * C::WTN + fn * 16 + 4 * (lane >> 4);
+                    if (g1) {
                         u32x2 outv;
                         bf16 *o = reinterpret_cast<bf16 *>(&outv);
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            o[i] = static_cast<bf16>(acc[pn][fm][fn][i]);
-                        *reinterpret_cast<u32x2 *>(stg + rl * RS + col * 2) = outv;
+                            o[i] = static_cast<bf16>(silu_f(acc[0][fm][fn][i]) * acc[1][fm][fn][i]);
+                        *reinterpret_cast<u32x2 *>(stg + rl * rs + cw * 2) = outv;
+                    } else {
+#pragma unroll
+                        for (int pn = 0; pn < 2; ++pn) {
+                            u32x2 outv;
+                            bf16 *o = reinterpret_cast<bf16 *>(&outv);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                o[i] = static_cast<bf16>(acc[pn][fm][fn][i]);
+                            *reinterpret_cast<u32x2 *>(stg + rl * rs + (pn * PW + cw) * 2) = outv;
+                        }
                     }
+                }
             }
             __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's rows are in LDS
             lds_barrier();
-#pragma unroll
-            for (int j = 0; j < RD; ++j) {
+            for (int j = 0; j < rd; ++j) {
                 const int ch = (j * NW + wave) * 64 + lane;
-                const int rl = ch / CPR, cc = ch % CPR;
+                const int rl = ch / cpr, cc = ch - rl * cpr;
                 const int r = q * PR + rl;
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + rl * RS + cc * 16);
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + rl * rs + cc * 16);
                 if (r < t.rows)
-                    *reinterpret_cast<u32x4 *>(Cout + (int64_t)(t.row0 + r) * H + t.n0 + cc * 8) = v;
+                    *reinterpret_cast<u32x4 *>(Cout + (int64_t)(t.row0 + r) * ldo + t.n0 + cc * 8) = v;
             }
             lds_barrier(); // the stage is read before the next pass (or the next tile's copies) writes it
         }
@@ -689,7 +704,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
             } else {
                 kloop(IC<C::FM>{});
             }
-            if (!PIPE && kind_of(cur.kind) == KIND_G2)
+            if (!PIPE && !(kind_of(cur.kind) == KIND_G1 && args.hsave))
                 epilogue_staged(cur, smem + ((s_cur + NSTAGE - 1) % NSTAGE) * C::STAGE_BYTES);
             else
                 epilogue(cur);
