@@ -699,6 +699,75 @@ __device__ __forceinline__ void epilogue(const EngineArgs &a, const TileInfo &t,
     }
 }
 
+// Epilogue of the kinds with one bf16 output array (the input gradient, the
+// shared expert's second GEMM, both weight gradients).  In the MFMA layout a
+// lane holds 4 columns of one row, so direct stores write 8-byte pieces of 16
+// rows per instruction.  Instead the tile passes through the LDS stage that
+// the last K step consumed (the copies in flight target the other two stages,
+// and the next tile's first barrier precedes the next copy into this one),
+// PR rows per pass, and is stored as whole rows, 16 bytes per lane.  Same
+// values, same rounding as the direct stores.
+template <int KIND, int BM, int WM>
+__device__ __forceinline__ void epilogue_staged(const EngineArgs &a, const TileInfo &t,
+                                                f32x4 (&acc)[Cfg<KIND, BM, WM>::NPANEL]
+                                                            [Cfg<KIND, BM, WM>::FM][Cfg<KIND, BM, WM>::FN],
+                                                int wm, int wn, int wave, int lane, unsigned char *stg)
+{
+    using C = Cfg<KIND, BM, WM>;
+    constexpr int PR = 32;                     // rows per pass
+    constexpr int RS = C::OUT_N * 2 + 16;      // bytes per staged row (padded)
+    constexpr int CPR = C::OUT_N * 2 / 16;     // 16-byte chunks per row
+    constexpr int RD = PR * CPR / (C::NW * 64); // chunks each lane stores per pass
+    static_assert(C::NPANEL == 1 && PR * RS <= C::STAGE_BYTES && BM % PR == 0 && PR % 16 == 0 &&
+                      RD * C::NW * 64 == PR * CPR,
+                  "staging");
+    bf16 *out = a.C;
+    int64_t ld = a.ldc;
+    int cjump = 0;
+    if constexpr (KIND == B5 || KIND == B7) {
+        // dW[e] [M, N]; a shared-expert chunk writes its rows (B5) or its gate
+        // and up column chunks (B7) of the shared gradient
+        const bool shd = a.Cs && t.e >= a.Er;
+        out = shd ? a.Cs + (int64_t)(t.e - a.Er) * a.cs_cstride : a.C + (int64_t)t.e * a.M * a.N;
+        ld = shd ? a.cs_ldc : a.N;
+        cjump = shd ? a.cs_cjump : 0;
+    }
+    const int cl = 4 * (lane >> 4);
+    lds_barrier(); // every wave is done reading the last K step's stage
+#pragma unroll 1
+    for (int q = 0; q < BM / PR; ++q) {
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int rt = wm * C::WTM + fm * 16; // first tile row of the 16-row block
+            if (rt < q * PR || rt >= (q + 1) * PR)
+                continue;
+            const int rl = rt - q * PR + (lane & 15);
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) {
+                u32x2 v;
+                bf16 *o = reinterpret_cast<bf16 *>(&v);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    o[i] = static_cast<bf16>(acc[0][fm][fn][i]);
+                *reinterpret_cast<u32x2 *>(stg + rl * RS + (wn * C::WTN + fn * 16 + cl) * 2) = v;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's rows are in LDS
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < RD; ++j) {
+            const int ch = (j * C::NW + wave) * 64 + lane;
+            const int rl = ch / CPR, cc = ch - rl * CPR;
+            const int r = q * PR + rl, c = t.n0 + cc * 8; // N is a multiple of 8
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + rl * RS + cc * 16);
+            if (r < t.rows && c < a.N)
+                *reinterpret_cast<u32x4 *>(out + (int64_t)(t.m0 + r) * ld + c +
+                                           (c >= (a.N >> 1) ? cjump : 0)) = v;
+        }
+        lds_barrier(); // read before the next pass (or the next tile's copies) writes the stage
+    }
+}
+
 template <int KIND, int BM, int WM>
 __global__ __launch_bounds__(64 * Shape<KIND>::NW, Shape<KIND>::WGPC) void engine_kernel(EngineArgs a)
 {
@@ -854,7 +923,11 @@ __global__ __launch_bounds__(64 * Shape<KIND>::NW, Shape<KIND>::WGPC) void engin
                 fetch();
             }
         }
-        epilogue<KIND, BM, WM>(a, t, acc, wm, wn, lane);
+        if constexpr (KIND == B2 || KIND == F1)
+            epilogue<KIND, BM, WM>(a, t, acc, wm, wn, lane);
+        else
+            epilogue_staged<KIND, BM, WM>(a, t, acc, wm, wn, wave, lane,
+                                          smem + (cstage == 0 ? NSTAGE - 1 : cstage - 1) * C::STAGE_BYTES);
     }
 }
 
