@@ -768,6 +768,123 @@ __device__ __forceinline__ void epilogue_staged(const EngineArgs &a, const TileI
     }
 }
 
+// Act-gradient epilogue through LDS.  The fp32 tile of u = dy W2^T passes
+// through the last K step's stage PR rows at a time; each lane then finishes
+// 8 consecutive columns of one row, so the saved pre-activation is read and
+// the three outputs (both halves of dh, act_g) are written 16 bytes per lane
+// as whole rows.  The row partial of Σ u act keeps its layout, one value per
+// 64 columns, now summed over 8 lanes of 8 columns each.  Every gate, slot and
+// pre-activation load of the tile is issued before the first pass (rows and
+// columns outside the tile read row 0 / the first column instead).
+template <int BM, int WM>
+__device__ __forceinline__ void epilogue_b2_staged(const EngineArgs &a, const TileInfo &t,
+                                                   f32x4 (&acc)[1][Cfg<B2, BM, WM>::FM][Cfg<B2, BM, WM>::FN],
+                                                   int wm, int wn, int wave, int lane, unsigned char *stg)
+{
+    using C = Cfg<B2, BM, WM>;
+    constexpr int PR = 32;                      // rows per pass
+    constexpr int NP = BM / PR;                 // passes
+    constexpr int RS = C::OUT_N * 4 + 16;       // bytes per staged fp32 row (padded)
+    constexpr int CPR = C::OUT_N / 8;           // 8-column chunks per row
+    constexpr int RPW = 64 / CPR;               // rows a wave finishes per read step
+    constexpr int RD = PR / (C::NW * RPW);      // read steps per pass
+    static_assert(PR * RS <= C::STAGE_BYTES && BM % PR == 0 && PR % 16 == 0 && CPR == 32 &&
+                      RD * C::NW * RPW == PR && C::WTN == 64 && C::OUT_N == C::WAVES_N * 64,
+                  "staging");
+    const int I = a.N;
+    const int cc = lane % CPR;                  // this lane's chunk of every row it finishes
+    const int c = t.n0 + cc * 8;
+    const bool cok = c < I;                     // I is a multiple of 8
+    const int cs = cok ? c : t.n0;
+    auto row_of = [&](int q, int j) { return q * PR + (j * C::NW + wave) * RPW + lane / CPR; };
+    float gv[NP][RD];
+    u32x4 hav[NP][RD], hbv[NP][RD];
+    {
+        int slot[NP][RD];
+#pragma unroll
+        for (int q = 0; q < NP; ++q)
+#pragma unroll
+            for (int j = 0; j < RD; ++j) {
+                const int r = row_of(q, j);
+                const int64_t p = t.m0 + (r < t.rows ? r : 0);
+                slot[q][j] = a.sorted_slot[p];
+                hav[q][j] = *reinterpret_cast<const u32x4 *>(a.Hs + p * 2 * I + cs);
+                hbv[q][j] = *reinterpret_cast<const u32x4 *>(a.Hs + p * 2 * I + I + cs);
+            }
+        // rows of the shared expert's chunks (from offsets[Er] on) have gate 1
+        const int64_t shared_row0 = a.Bs && a.Er < a.E ? (int64_t)ldc(a.offsets, a.Er) : INT64_MAX;
+#pragma unroll
+        for (int q = 0; q < NP; ++q)
+#pragma unroll
+            for (int j = 0; j < RD; ++j)
+                gv[q][j] = t.m0 + row_of(q, j) >= shared_row0 ? 1.0f : a.gates[slot[q][j]];
+    }
+    const int cl = 4 * (lane >> 4);
+    lds_barrier(); // every wave is done reading the last K step's stage
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int rt = wm * C::WTM + fm * 16;
+            if (rt < q * PR || rt >= (q + 1) * PR)
+                continue;
+            const int rl = rt - q * PR + (lane & 15);
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn)
+                *reinterpret_cast<f32x4 *>(stg + rl * RS + (wn * C::WTN + fn * 16 + cl) * 4) = acc[0][fm][fn];
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's rows are in LDS
+        lds_barrier();
+        // Every load of the epilogue has landed before the first store.  The
+        // stores are conditional, so a wait placed by the compiler after one
+        // cannot count it and would drain every store issued so far.
+        if (q == 0)
+            wait_vm<0>();
+#pragma unroll
+        for (int j = 0; j < RD; ++j) {
+            const int r = row_of(q, j);
+            const bool ok = r < t.rows && cok;
+            const int64_t p = t.m0 + (r < t.rows ? r : 0);
+            const f32x4 u0 = *reinterpret_cast<const f32x4 *>(stg + (r - q * PR) * RS + cc * 32);
+            const f32x4 u1 = *reinterpret_cast<const f32x4 *>(stg + (r - q * PR) * RS + cc * 32 + 16);
+            const bf16 *ha = reinterpret_cast<const bf16 *>(&hav[q][j]);
+            const bf16 *hb = reinterpret_cast<const bf16 *>(&hbv[q][j]);
+            const float g = gv[q][j];
+            u32x4 oa, ob, og;
+            bf16 *pa = reinterpret_cast<bf16 *>(&oa), *pb = reinterpret_cast<bf16 *>(&ob),
+                 *pg = reinterpret_cast<bf16 *>(&og);
+            float dg = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                // dact = g u; dh = [dact b σ(a)(1 + a(1-σ(a))), dact silu(a)]; act_g = g silu(a) b
+                const float u = i < 4 ? u0[i] : u1[i - 4];
+                const float av = static_cast<float>(ha[i]), bv = static_cast<float>(hb[i]);
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-av));
+                const float sl = av * sg;
+                const float act = sl * bv;
+                const float dact = g * u;
+                pa[i] = static_cast<bf16>(dact * bv * sg * (1.0f + av * (1.0f - sg)));
+                pb[i] = static_cast<bf16>(dact * sl);
+                pg[i] = static_cast<bf16>(g * act);
+                dg += u * act;
+            }
+            if (ok) {
+                *reinterpret_cast<u32x4 *>(a.C + p * 2 * I + c) = oa;
+                *reinterpret_cast<u32x4 *>(a.C + p * 2 * I + I + c) = ob;
+                *reinterpret_cast<u32x4 *>(a.C2 + p * I + c) = og;
+            }
+            // per-row partial over the 64 columns of 8 neighbouring lanes
+            dg = ok ? dg : 0.f;
+            dg += __shfl_xor(dg, 1, 64);
+            dg += __shfl_xor(dg, 2, 64);
+            dg += __shfl_xor(dg, 4, 64);
+            if (r < t.rows && (lane & 7) == 0)
+                a.dgp[p * a.dgp_stride + (t.n0 / C::OUT_N) * C::WAVES_N + cc / 8] = dg;
+        }
+        lds_barrier(); // read before the next pass (or the next tile's copies) writes the stage
+    }
+}
+
 template <int KIND, int BM, int WM>
 __global__ __launch_bounds__(64 * Shape<KIND>::NW, Shape<KIND>::WGPC) void engine_kernel(EngineArgs a)
 {
@@ -923,7 +1040,10 @@ __global__ __launch_bounds__(64 * Shape<KIND>::NW, Shape<KIND>::WGPC) void engin
                 fetch();
             }
         }
-        if constexpr (KIND == B2 || KIND == F1)
+        if constexpr (KIND == B2 && BM == 128)
+            epilogue_b2_staged<BM, WM>(a, t, acc, wm, wn, wave, lane,
+                                       smem + (cstage == 0 ? NSTAGE - 1 : cstage - 1) * C::STAGE_BYTES);
+        else if constexpr (KIND == B2 || KIND == F1)
             epilogue<KIND, BM, WM>(a, t, acc, wm, wn, lane);
         else
             epilogue_staged<KIND, BM, WM>(a, t, acc, wm, wn, wave, lane,
