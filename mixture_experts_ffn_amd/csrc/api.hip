@@ -513,7 +513,7 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
             return MOE_FFN_OK;
         }
         record(ev, MOE_FFN_STAGE_GEMM1, true, s);
-        HIP_TRY(moe::launch_fast_fwd(moe::FAST_G1, BM, a, num_cus, s), "gemm1 launch");
+        HIP_TRY(moe::launch_fast_fwd(a.hsave ? moe::FAST_G1H : moe::FAST_G1, BM, a, num_cus, s), "gemm1 launch");
         record(ev, MOE_FFN_STAGE_GEMM1, false, s);
         record(ev, MOE_FFN_STAGE_GEMM2, true, s);
         HIP_TRY(moe::launch_fast_fwd(moe::FAST_G2, BM, a, num_cus, s), "gemm2 launch");

@@ -12,6 +12,8 @@
 // One tile engine serves both, in three modes:
 //   FAST_G1, FAST_G2  one grouped GEMM per launch (the bulk forward: route,
 //                     GEMM1, GEMM2 and combine as separate launches);
+//   FAST_G1H          FAST_G1 that also saves the pre-activation h for the
+//                     backward;
 //   FAST_PIPE         one launch runs every GEMM1 tile, then every GEMM2 tile,
 //                     then the combine, with device counters in place of the
 //                     launch boundaries (the overlap explainer page, sections
@@ -286,6 +288,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * C::STAGE_BYTES];
 
     constexpr bool PIPE = MODE == FAST_PIPE;
+    constexpr bool G1ONLY = MODE == FAST_G1 || MODE == FAST_G1H;
     const int H = args.H, I = args.I;
     const int ntn1 = I / TILE_N1, ntn2 = H / TILE_N2;
     const int mtiles = uni(ldc(args.mtile_off, args.E));
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
     int32_t *const ctr2 = args.ctr + args.max_mtiles; // GEMM2 N-tiles done per M-tile
 
     auto kind_of = [&](int k) {
-        return MODE == FAST_G1 ? (int)KIND_G1 : MODE == FAST_G2 ? (int)KIND_G2 : k;
+        return G1ONLY ? (int)KIND_G1 : MODE == FAST_G2 ? (int)KIND_G2 : k;
     };
     auto phase_begin = [&](int kind, Cursor &c) {
         const int total = mtiles * (kind == KIND_G1 ? ntn1 : ntn2);
@@ -533,10 +536,11 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
     // through the LDS stage the last K step used (no copy of the next tile
     // targets it before the next tile's first barrier) PR rows at a time and
     // is stored as whole rows, 16 bytes per lane: GEMM2's 256 output columns,
-    // GEMM1's 128 act columns (a GEMM1 that also saves the pre-activation for
-    // the backward keeps the direct stores).  Same values, same rounding.
-    auto epilogue_staged = [&](const Tile &t, unsigned char *stg) {
-        const bool g1 = kind_of(t.kind) == KIND_G1;
+    // GEMM1's 128 act columns and, when GEMM1 saves the pre-activation for the
+    // backward, in a second sweep its gate and up panels (`hpart`) into the
+    // two halves of h.  Same values, same rounding.
+    auto epilogue_staged = [&](const Tile &t, unsigned char *stg, bool hpart) {
+        const bool g1 = kind_of(t.kind) == KIND_G1 && !hpart;
         constexpr int PR = 32;                                 // rows per pass
         const int ncol = g1 ? TILE_N1 : TILE_N2;                // output columns of the tile
         const int rs = ncol * 2 + 16;                           // bytes per staged row (padded)
@@ -545,8 +549,8 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
         static_assert(PR * (TILE_N2 * 2 + 16) <= C::STAGE_BYTES && BM % PR == 0 && PR % 16 == 0,
                       "staging");
         static_assert(PR * (TILE_N1 * 2 / 16) % (NW * 64) == 0, "staging reads");
-        bf16 *__restrict__ Cout = static_cast<bf16 *>(g1 ? args.act : args.o);
-        const int ldo = g1 ? I : H;
+        bf16 *__restrict__ Cout = static_cast<bf16 *>(hpart ? args.hsave : g1 ? args.act : args.o);
+        const int ldo = hpart ? 2 * I : g1 ? I : H;
         lds_barrier(); // every wave is done with the last K step's stage
 #pragma unroll 1
         for (int q = 0; q < BM / PR; ++q) {
@@ -586,8 +590,10 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
                 const int rl = ch / cpr, cc = ch - rl * cpr;
                 const int r = q * PR + rl;
                 const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + rl * rs + cc * 16);
+                // h: the tile's up panel (staged columns PW..2PW) goes to the second half
+                const int dc = hpart && cc * 8 >= PW ? I - PW : 0;
                 if (r < t.rows)
-                    *reinterpret_cast<u32x4 *>(Cout + (int64_t)(t.row0 + r) * ldo + t.n0 + cc * 8) = v;
+                    *reinterpret_cast<u32x4 *>(Cout + (int64_t)(t.row0 + r) * ldo + t.n0 + dc + cc * 8) = v;
             }
             lds_barrier(); // the stage is read before the next pass (or the next tile's copies) writes it
         }
@@ -613,7 +619,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
     bool have = false;
     if (MODE != FAST_G2)
         have = phase_begin(KIND_G1, cc);
-    if (!have && MODE != FAST_G1)
+    if (!have && !G1ONLY)
         have = phase_begin(KIND_G2, cc);
 
     if (have) {
@@ -704,9 +710,12 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
             } else {
                 kloop(IC<C::FM>{});
             }
-            if (!PIPE && !(kind_of(cur.kind) == KIND_G1 && args.hsave))
-                epilogue_staged(cur, smem + ((s_cur + NSTAGE - 1) % NSTAGE) * C::STAGE_BYTES);
-            else
+            if (!PIPE) {
+                unsigned char *stg = smem + ((s_cur + NSTAGE - 1) % NSTAGE) * C::STAGE_BYTES;
+                epilogue_staged(cur, stg, false);
+                if constexpr (MODE == FAST_G1H)
+                    epilogue_staged(cur, stg, true);
+            } else
                 epilogue(cur);
             const int done = release_index(cur);
             if (!has_next) {
@@ -853,6 +862,7 @@ hipError_t launch_fast_fwd(int mode, int BM, const FastFwdArgs &a, int num_cus, 
         return hipErrorInvalidValue;
     switch (mode) {
     case FAST_G1: return launch_bm<FAST_G1>(BM, a, num_cus, stream);
+    case FAST_G1H: return launch_bm<FAST_G1H>(BM, a, num_cus, stream);
     case FAST_G2: return launch_bm<FAST_G2>(BM, a, num_cus, stream);
     default: return launch_bm<FAST_PIPE>(BM, a, num_cus, stream);
     }

@@ -144,7 +144,7 @@ struct FastFwdArgs {
     int drop_mt;                 // test hook: M-tile whose first GEMM1 release is dropped (-1)
     SharedExperts sh;            // E counts the shared chunks too (sh.Er routed)
 };
-enum { FAST_G1 = 0, FAST_G2 = 1, FAST_PIPE = 2 };
+enum { FAST_G1 = 0, FAST_G2 = 1, FAST_PIPE = 2, FAST_G1H = 3 }; // FAST_G1H: FAST_G1 saving h
 hipError_t launch_fast_fwd(int mode, int BM, const FastFwdArgs &a, int num_cus,
                            hipStream_t stream);
 
