@@ -73,14 +73,22 @@ def test_grid_size_does_not_change_the_result(gpu_lib, case):
         assert torch.equal(y_pipe, y_small)
 
 
-def test_small_grid_saved_context_drives_the_backward(gpu_lib):
-    inp = make_inputs(workload(CASES[0]), with_dy=True)
+# one case per tile height: the GEMM1 that saves h is its own kernel per height
+SAVED_CASES = [CASES[0], CASES[2], CASES[3]]
+
+
+@pytest.mark.parametrize("case", SAVED_CASES, ids=[c[0] for c in SAVED_CASES])
+def test_small_grid_saved_context_drives_the_backward(gpu_lib, case):
+    inp = make_inputs(workload(case), with_dy=True)
     d = to_device(inp)
-    say("[tiles] backward from a 16-workgroup forward")
-    _, saved = fwd(gpu_lib, d, gpu_lib.TEST_SMALL_GRID, save_for_backward=True)
+    say(f"[tiles] case={case[0]} backward from a 16-workgroup forward")
+    y_inf = fwd(gpu_lib, d)
+    y_saved, saved = fwd(gpu_lib, d, gpu_lib.TEST_SMALL_GRID, save_for_backward=True)
     grads = gpu_lib.moe_ffn_bwd(d["dy"], d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
                                 d["down_proj"], saved)
     torch.cuda.synchronize()
+    # saving h changes nothing in the forward's arithmetic
+    assert torch.equal(y_saved, y_inf)
     ref = oracle.backward(inp["dy"], inp["x"], inp["topk_ids"], inp["topk_weights"],
                           inp["up_proj"], inp["down_proj"])
     for n, g, r in zip(("dx", "d_up", "d_down", "d_topk"), grads, ref):
