@@ -552,13 +552,17 @@ __device__ __forceinline__ bf16x8 frag_kcol(const unsigned char *tile, int nb, i
 // epilogues ------------------------------------------------------------------
 // lane (fm, fn) element i: row wm*WTM + fm*16 + (lane % 16) of the tile,
 // column wn*WTN + fn*16 + 4 (lane / 16) + i of panel p.
+// Epilogue of F1 (the ragged-shape GEMM1): act = silu(gate) * up from the two
+// panels' accumulators, and with a saved-h buffer the raw gate and up halves,
+// stored directly (8 bytes per lane: row lane & 15, columns 4 * (lane >> 4)).
 template <int KIND, int BM, int WM>
-__device__ __forceinline__ void epilogue(const EngineArgs &a, const TileInfo &t,
-                                         f32x4 (&acc)[Cfg<KIND, BM, WM>::NPANEL][Cfg<KIND, BM, WM>::FM]
-                                                     [Cfg<KIND, BM, WM>::FN],
-                                         int wm, int wn, int lane)
+__device__ __forceinline__ void epilogue_f1(const EngineArgs &a, const TileInfo &t,
+                                            f32x4 (&acc)[Cfg<KIND, BM, WM>::NPANEL][Cfg<KIND, BM, WM>::FM]
+                                                        [Cfg<KIND, BM, WM>::FN],
+                                            int wm, int wn, int lane)
 {
     using C = Cfg<KIND, BM, WM>;
+    static_assert(KIND == F1 && C::NPANEL == 2, "F1 only");
     auto pack4 = [](float v0, float v1, float v2, float v3) {
         u32x2 r;
         bf16 *o = reinterpret_cast<bf16 *>(&r);
@@ -569,131 +573,27 @@ __device__ __forceinline__ void epilogue(const EngineArgs &a, const TileInfo &t,
         return r;
     };
     const int cl = 4 * (lane >> 4);
-    if constexpr (KIND == B2) {
-        // dact = g u; dh = [dact b σ(a)(1 + a(1-σ(a))), dact silu(a)]; act_g = g silu(a) b;
-        // per-row partial of Σ_i u act over this wave's columns (d_g = g-free row dot)
-        const int I = a.N;
-        // Every load of the epilogue is issued, unconditionally (rows and
-        // columns outside the tile read its first row / column instead), before
-        // any store: the tile then pays two memory round trips (slot, then gate
-        // and the saved h) instead of a dependent chain per 16-row block and a
-        // load-store round trip per 16x16 block.
-        int slot[C::FM];
-        u32x2 hav[C::FM][C::FN], hbv[C::FM][C::FN];
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-            const int r = wm * C::WTM + fm * 16 + (lane & 15);
-            const int64_t p = t.m0 + (r < t.rows ? r : 0);
-            slot[fm] = a.sorted_slot[p];
+    for (int fm = 0; fm < C::FM; ++fm) {
+        const int r = wm * C::WTM + fm * 16 + (lane & 15);
+        if (r >= t.rows)
+            continue;
+        const int64_t p = t.m0 + r;
 #pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn) {
-                const int c = t.n0 + wn * C::WTN + fn * 16 + cl;
-                const int cc = c < I ? c : t.n0;
-                hav[fm][fn] = *reinterpret_cast<const u32x2 *>(a.Hs + p * 2 * I + cc);
-                hbv[fm][fn] = *reinterpret_cast<const u32x2 *>(a.Hs + p * 2 * I + I + cc);
-            }
-        }
-        // rows of the shared expert's chunks (from offsets[Er] on) have gate 1
-        const int64_t shared_row0 = a.Bs && a.Er < a.E ? (int64_t)ldc(a.offsets, a.Er) : INT64_MAX;
-        float gv[C::FM];
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-            const int r = wm * C::WTM + fm * 16 + (lane & 15);
-            gv[fm] = t.m0 + r >= shared_row0 ? 1.0f : a.gates[slot[fm]];
-        }
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-            const int r = wm * C::WTM + fm * 16 + (lane & 15);
-            const bool rok = r < t.rows;
-            const int64_t p = t.m0 + (rok ? r : 0);
-            const float g = rok ? gv[fm] : 0.f;
-            float dg = 0.f;
-#pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn) {
-                const int c = t.n0 + wn * C::WTN + fn * 16 + cl;
-                if (rok && c < I) {
-                    const bf16 *ha = reinterpret_cast<const bf16 *>(&hav[fm][fn]);
-                    const bf16 *hb = reinterpret_cast<const bf16 *>(&hbv[fm][fn]);
-                    float da[4], db[4], ag[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float u = acc[0][fm][fn][i];
-                        const float av = static_cast<float>(ha[i]), bv = static_cast<float>(hb[i]);
-                        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-av));
-                        const float sl = av * sg;
-                        const float act = sl * bv;
-                        const float dact = g * u;
-                        da[i] = dact * bv * sg * (1.0f + av * (1.0f - sg));
-                        db[i] = dact * sl;
-                        ag[i] = g * act;
-                        dg += u * act;
-                    }
-                    *reinterpret_cast<u32x2 *>(a.C + p * 2 * I + c) = pack4(da[0], da[1], da[2], da[3]);
-                    *reinterpret_cast<u32x2 *>(a.C + p * 2 * I + I + c) =
-                        pack4(db[0], db[1], db[2], db[3]);
-                    *reinterpret_cast<u32x2 *>(a.C2 + p * I + c) = pack4(ag[0], ag[1], ag[2], ag[3]);
-                }
-            }
-            // the 4 lanes sharing this row hold disjoint columns
-            dg += __shfl_xor(dg, 16, 64);
-            dg += __shfl_xor(dg, 32, 64);
-            if (rok && lane < 16)
-                a.dgp[p * a.dgp_stride + (t.n0 / C::OUT_N) * C::WAVES_N + wn] = dg;
-        }
-    } else if constexpr (KIND == B5 || KIND == B7) {
-        // weight gradient tile of expert e: rows m, columns n of dW[e] [M, N]
-        // a shared-expert chunk writes its rows (B5) or its gate and up column
-        // chunks (B7) of the shared gradient
-        const bool shd = a.Cs && t.e >= a.Er;
-        bf16 *dW = shd ? a.Cs + (int64_t)(t.e - a.Er) * a.cs_cstride : a.C + (int64_t)t.e * a.M * a.N;
-        const int64_t ldw = shd ? a.cs_ldc : a.N;
-        const int cjump = shd ? a.cs_cjump : 0;
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-            const int r = wm * C::WTM + fm * 16 + (lane & 15);
-            if (r >= t.rows)
+        for (int fn = 0; fn < C::FN; ++fn) {
+            const int c = t.n0 + wn * C::WTN + fn * 16 + cl;
+            if (c >= a.N)
                 continue;
-            const int64_t m = t.m0 + r;
+            float o[4];
 #pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn) {
-                const int c = t.n0 + wn * C::WTN + fn * 16 + cl;
-                if (c < a.N)
-                    *reinterpret_cast<u32x2 *>(dW + m * ldw + c + (c >= (a.N >> 1) ? cjump : 0)) =
-                        pack4(acc[0][fm][fn][0], acc[0][fm][fn][1], acc[0][fm][fn][2],
-                              acc[0][fm][fn][3]);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-            const int r = wm * C::WTM + fm * 16 + (lane & 15);
-            if (r >= t.rows)
-                continue;
-            const int64_t p = t.m0 + r;
-#pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn) {
-                const int c = t.n0 + wn * C::WTN + fn * 16 + cl;
-                if (c >= a.N)
-                    continue;
-                if constexpr (KIND == F1) {
-                    float o[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        o[i] = silu_f(acc[0][fm][fn][i]) * acc[1][fm][fn][i];
-                    *reinterpret_cast<u32x2 *>(a.C + p * a.ldc + c) = pack4(o[0], o[1], o[2], o[3]);
-                    if (a.C2) {
-                        *reinterpret_cast<u32x2 *>(a.C2 + p * 2 * a.N + c) =
-                            pack4(acc[0][fm][fn][0], acc[0][fm][fn][1], acc[0][fm][fn][2],
-                                  acc[0][fm][fn][3]);
-                        *reinterpret_cast<u32x2 *>(a.C2 + p * 2 * a.N + a.N + c) =
-                            pack4(acc[1][fm][fn][0], acc[1][fm][fn][1], acc[1][fm][fn][2],
-                                  acc[1][fm][fn][3]);
-                    }
-                } else {
-                    *reinterpret_cast<u32x2 *>(a.C + p * a.ldc + c) =
-                        pack4(acc[0][fm][fn][0], acc[0][fm][fn][1], acc[0][fm][fn][2],
-                              acc[0][fm][fn][3]);
-                }
+            for (int i = 0; i < 4; ++i)
+                o[i] = silu_f(acc[0][fm][fn][i]) * acc[1][fm][fn][i];
+            *reinterpret_cast<u32x2 *>(a.C + p * a.ldc + c) = pack4(o[0], o[1], o[2], o[3]);
+            if (a.C2) {
+                *reinterpret_cast<u32x2 *>(a.C2 + p * 2 * a.N + c) =
+                    pack4(acc[0][fm][fn][0], acc[0][fm][fn][1], acc[0][fm][fn][2], acc[0][fm][fn][3]);
+                *reinterpret_cast<u32x2 *>(a.C2 + p * 2 * a.N + a.N + c) =
+                    pack4(acc[1][fm][fn][0], acc[1][fm][fn][1], acc[1][fm][fn][2], acc[1][fm][fn][3]);
             }
         }
     }
@@ -1040,11 +940,11 @@ __global__ __launch_bounds__(64 * Shape<KIND>::NW, Shape<KIND>::WGPC) void engin
                 fetch();
             }
         }
-        if constexpr (KIND == B2 && BM == 128)
+        if constexpr (KIND == B2)
             epilogue_b2_staged<BM, WM>(a, t, acc, wm, wn, wave, lane,
                                        smem + (cstage == 0 ? NSTAGE - 1 : cstage - 1) * C::STAGE_BYTES);
-        else if constexpr (KIND == B2 || KIND == F1)
-            epilogue<KIND, BM, WM>(a, t, acc, wm, wn, lane);
+        else if constexpr (KIND == F1)
+            epilogue_f1<KIND, BM, WM>(a, t, acc, wm, wn, lane);
         else
             epilogue_staged<KIND, BM, WM>(a, t, acc, wm, wn, wave, lane,
                                           smem + (cstage == 0 ? NSTAGE - 1 : cstage - 1) * C::STAGE_BYTES);
