@@ -475,9 +475,10 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
         __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
     };
 
-    // epilogue: lane owns row (lane & 15) and columns 4*(lane >> 4) + [0, 4)
-    // of each 16x16 block of this wave
-    auto epilogue = [&](const Tile &t) {
+    // Epilogue of the pipelined launch (device-coherent stores that another
+    // workgroup of the launch reads): lane owns row (lane & 15) and columns
+    // 4*(lane >> 4) + [0, 4) of each 16x16 block of this wave.
+    auto epilogue_pipe = [&](const Tile &t) {
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm) {
             const int r = wm * C::WTM + fm * 16 + (lane & 15);
@@ -502,10 +503,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
                         go[i] = static_cast<bf16>(g);
                         uo[i] = static_cast<bf16>(u);
                     }
-                    if (PIPE)
-                        store_coherent(Cout + p * I + c, outv);
-                    else
-                        *reinterpret_cast<u32x2 *>(Cout + p * I + c) = outv;
+                    store_coherent(Cout + p * I + c, outv);
                     if (Hs) {
                         *reinterpret_cast<u32x2 *>(Hs + p * 2 * I + c) = gv;
                         *reinterpret_cast<u32x2 *>(Hs + p * 2 * I + I + c) = uv;
@@ -519,10 +517,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
                             o[i] = static_cast<bf16>(acc[pn][fm][fn][i]);
-                        if (PIPE)
-                            store_coherent(Cout + p * H + t.n0 + pn * PW + cw, outv);
-                        else
-                            *reinterpret_cast<u32x2 *>(Cout + p * H + t.n0 + pn * PW + cw) = outv;
+                        store_coherent(Cout + p * H + t.n0 + pn * PW + cw, outv);
                     }
                 }
             }
@@ -716,7 +711,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
                 if constexpr (MODE == FAST_G1H)
                     epilogue_staged(cur, stg, true);
             } else
-                epilogue(cur);
+                epilogue_pipe(cur);
             const int done = release_index(cur);
             if (!has_next) {
                 if (done >= 0) {
