@@ -186,14 +186,18 @@ __device__ __forceinline__ void lds_barrier()
 // device-coherent stores and read with device-coherent loads (the sc1 scope
 // bit; the encoding of device-scope relaxed atomics), so no cache holds a
 // stale or a dirty private copy of it and no whole-cache write-back or
-// invalidate is needed.  A producer waits until its stores are acknowledged
-// (vmcnt 0), the workgroup meets at a barrier, and one lane bumps the tile's
-// counter; a consumer polls the counter with device-coherent loads, bounded
-// by the watchdog, and issues its loads only after the poll has returned.
-__device__ __forceinline__ void store_coherent(void *p, u32x2 v)
+// invalidate is needed.  Each producer wave waits until its own stores of a
+// tile are acknowledged (vmcnt) and its lane 0 bumps the tile's counter, so a
+// tile is complete at NW bumps per N-tile; a consumer polls the counter with
+// device-coherent loads, bounded by the watchdog, and issues its loads only
+// after the poll has returned.
+__device__ __forceinline__ void store_coherent16(void *p, u32x4 v)
 {
-    __hip_atomic_store(static_cast<uint64_t *>(p), __builtin_bit_cast(uint64_t, v),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t *q = static_cast<uint64_t *>(p);
+    __hip_atomic_store(q, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ u32x4 load_coherent16(const void *p)
 {
@@ -475,65 +479,17 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
         __builtin_amdgcn_sched_group_barrier(0x008, NMF - PAIRS, 0);
     };
 
-    // Epilogue of the pipelined launch (device-coherent stores that another
-    // workgroup of the launch reads): lane owns row (lane & 15) and columns
-    // 4*(lane >> 4) + [0, 4) of each 16x16 block of this wave.
-    auto epilogue_pipe = [&](const Tile &t) {
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-            const int r = wm * C::WTM + fm * 16 + (lane & 15);
-            if (r >= t.rows)
-                continue;
-            const int64_t p = t.row0 + r;
-#pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn) {
-                const int cw = wn * C::WTN + fn * 16 + 4 * (lane >> 4);
-                if (kind_of(t.kind) == KIND_G1) {
-                    bf16 *__restrict__ Cout = static_cast<bf16 *>(args.act);
-                    bf16 *__restrict__ Hs = static_cast<bf16 *>(args.hsave);
-                    const int c = t.n0 + cw;
-                    u32x2 outv, gv, uv;
-                    bf16 *o = reinterpret_cast<bf16 *>(&outv);
-                    bf16 *go = reinterpret_cast<bf16 *>(&gv);
-                    bf16 *uo = reinterpret_cast<bf16 *>(&uv);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float g = acc[0][fm][fn][i], u = acc[1][fm][fn][i];
-                        o[i] = static_cast<bf16>(silu_f(g) * u);
-                        go[i] = static_cast<bf16>(g);
-                        uo[i] = static_cast<bf16>(u);
-                    }
-                    store_coherent(Cout + p * I + c, outv);
-                    if (Hs) {
-                        *reinterpret_cast<u32x2 *>(Hs + p * 2 * I + c) = gv;
-                        *reinterpret_cast<u32x2 *>(Hs + p * 2 * I + I + c) = uv;
-                    }
-                } else {
-                    bf16 *__restrict__ Cout = static_cast<bf16 *>(args.o);
-#pragma unroll
-                    for (int pn = 0; pn < 2; ++pn) {
-                        u32x2 outv;
-                        bf16 *o = reinterpret_cast<bf16 *>(&outv);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            o[i] = static_cast<bf16>(acc[pn][fm][fn][i]);
-                        store_coherent(Cout + p * H + t.n0 + pn * PW + cw, outv);
-                    }
-                }
-            }
-        }
-    };
-
-    // The output tiles of the bulk launches, written through LDS: in the MFMA
-    // layout a lane holds 4 columns of one row, so direct stores write 32-byte
-    // pieces of 16 rows per instruction, and those stores measured a fifth of
-    // GEMM2's time and a fourteenth of GEMM1's.  Instead the tile passes
+    // The output tiles, written through LDS: in the MFMA layout a lane holds
+    // 4 columns of one row, so direct stores write 32-byte pieces of 16 rows
+    // per instruction, and those stores measured a fifth of GEMM2's time and a
+    // fourteenth of GEMM1's.  Instead the tile passes
     // through the LDS stage the last K step used (no copy of the next tile
     // targets it before the next tile's first barrier) PR rows at a time and
     // is stored as whole rows, 16 bytes per lane: GEMM2's 256 output columns,
     // GEMM1's 128 act columns and, when GEMM1 saves the pre-activation for the
     // backward, in a second sweep its gate and up panels (`hpart`) into the
-    // two halves of h.  Same values, same rounding.
+    // two halves of h.  Same values, same rounding.  The pipelined launch
+    // stores device-coherently (other workgroups of the launch read the rows).
     auto epilogue_staged = [&](const Tile &t, unsigned char *stg, bool hpart) {
         const bool g1 = kind_of(t.kind) == KIND_G1 && !hpart;
         constexpr int PR = 32;                                 // rows per pass
@@ -587,8 +543,13 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
                 const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + rl * rs + cc * 16);
                 // h: the tile's up panel (staged columns PW..2PW) goes to the second half
                 const int dc = hpart && cc * 8 >= PW ? I - PW : 0;
-                if (r < t.rows)
-                    *reinterpret_cast<u32x4 *>(Cout + (int64_t)(t.row0 + r) * ldo + t.n0 + dc + cc * 8) = v;
+                bf16 *dst = Cout + (int64_t)(t.row0 + r) * ldo + t.n0 + dc + cc * 8;
+                if (r < t.rows) {
+                    if (PIPE) // read by other workgroups of this launch
+                        store_coherent16(dst, v);
+                    else
+                        *reinterpret_cast<u32x4 *>(dst) = v;
+                }
             }
             lds_barrier(); // the stage is read before the next pass (or the next tile's copies) writes it
         }
@@ -705,13 +666,12 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
             } else {
                 kloop(IC<C::FM>{});
             }
-            if (!PIPE) {
+            {
                 unsigned char *stg = smem + ((s_cur + NSTAGE - 1) % NSTAGE) * C::STAGE_BYTES;
                 epilogue_staged(cur, stg, false);
-                if constexpr (MODE == FAST_G1H)
+                if (MODE == FAST_G1H || (PIPE && args.hsave && kind_of(cur.kind) == KIND_G1))
                     epilogue_staged(cur, stg, true);
-            } else
-                epilogue_pipe(cur);
+            }
             const int done = release_index(cur);
             if (!has_next) {
                 if (done >= 0) {
