@@ -191,13 +191,10 @@ __device__ __forceinline__ void lds_barrier()
 // tile is complete at NW bumps per N-tile; a consumer polls the counter with
 // device-coherent loads, bounded by the watchdog, and issues its loads only
 // after the poll has returned.
-__device__ __forceinline__ void store_coherent16(void *p, u32x4 v)
+__device__ __forceinline__ void store_coherent(void *p, u32x2 v)
 {
-    uint64_t *q = static_cast<uint64_t *>(p);
-    __hip_atomic_store(q, (uint64_t)v[0] | ((uint64_t)v[1] << 32), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(q + 1, (uint64_t)v[2] | ((uint64_t)v[3] << 32), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(static_cast<uint64_t *>(p), __builtin_bit_cast(uint64_t, v),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ u32x4 load_coherent16(const void *p)
 {
@@ -536,19 +533,31 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
             }
             __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's rows are in LDS
             lds_barrier();
-            for (int j = 0; j < rd; ++j) {
-                const int ch = (j * NW + wave) * 64 + lane;
-                const int rl = ch / cpr, cc = ch - rl * cpr;
-                const int r = q * PR + rl;
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + rl * rs + cc * 16);
-                // h: the tile's up panel (staged columns PW..2PW) goes to the second half
-                const int dc = hpart && cc * 8 >= PW ? I - PW : 0;
-                bf16 *dst = Cout + (int64_t)(t.row0 + r) * ldo + t.n0 + dc + cc * 8;
-                if (r < t.rows) {
-                    if (PIPE) // read by other workgroups of this launch
-                        store_coherent16(dst, v);
-                    else
-                        *reinterpret_cast<u32x4 *>(dst) = v;
+            if constexpr (PIPE) {
+                // rows other workgroups of this launch read: device-coherent
+                // stores, which are 8 bytes wide, so each lane takes an 8-byte
+                // piece and one store instruction covers whole rows
+                const int cpr8 = 2 * cpr, rd8 = 2 * rd;
+#pragma unroll 1
+                for (int j = 0; j < rd8; ++j) {
+                    const int ch = (j * NW + wave) * 64 + lane;
+                    const int rl = ch / cpr8, c8 = ch - rl * cpr8;
+                    const int r = q * PR + rl;
+                    const u32x2 v = *reinterpret_cast<const u32x2 *>(stg + rl * rs + c8 * 8);
+                    const int dc = hpart && c8 * 4 >= PW ? I - PW : 0;
+                    if (r < t.rows)
+                        store_coherent(Cout + (int64_t)(t.row0 + r) * ldo + t.n0 + dc + c8 * 4, v);
+                }
+            } else {
+                for (int j = 0; j < rd; ++j) {
+                    const int ch = (j * NW + wave) * 64 + lane;
+                    const int rl = ch / cpr, cc = ch - rl * cpr;
+                    const int r = q * PR + rl;
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + rl * rs + cc * 16);
+                    // h: the tile's up panel (staged columns PW..2PW) goes to the second half
+                    const int dc = hpart && cc * 8 >= PW ? I - PW : 0;
+                    if (r < t.rows)
+                        *reinterpret_cast<u32x4 *>(Cout + (int64_t)(t.row0 + r) * ldo + t.n0 + dc + cc * 8) = v;
                 }
             }
             lds_barrier(); // the stage is read before the next pass (or the next tile's copies) writes it
