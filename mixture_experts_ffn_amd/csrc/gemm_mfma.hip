@@ -35,8 +35,8 @@
 //    panels are 128 gate and the matching 128 up columns, so SwiGLU pairs two
 //    accumulators of one lane; GEMM2's panels are 256 adjacent output columns.
 //  * The matrix-core step computes C^T = W^T · X^T (weights as the first
-//    operand), so each lane owns 4 consecutive output columns of one row and
-//    the epilogue writes 8 bytes per lane.
+//    operand), so each lane owns 4 consecutive output columns of one row; the
+//    epilogue passes the tile through LDS and stores it as whole rows.
 //  * Block tile BM rows x 256 weight columns, two waves per SIMD (one wave's
 //    MFMAs cover the other's LDS waits):
 //      BM = 64:  one workgroup of 8 waves per CU, each wave all 64 rows and 16
