@@ -309,7 +309,10 @@ hipError_t launch_gemm2(int dtype, const FwdTiles &t, const GroupedGemmArgs &a,
             return launch_grouped<bf16, 64, 128, 64, 2, 2, false, false>(a, stream);
         return launch_grouped<bf16, 128, 128, 64, 2, 2, false, false>(a, stream);
     }
-    return launch_grouped<float, 64, 128, 32, 2, 2, false, false>(a, stream);
+    // fp32: 64-column tiles (BK = 64 so the B tile still splits evenly over the
+    // threads): twice the workgroups of 128-column tiles, which the small fp32
+    // shapes need to fill the device
+    return launch_grouped<float, 64, 64, 64, 2, 2, false, false>(a, stream);
 }
 
 } // namespace moe
