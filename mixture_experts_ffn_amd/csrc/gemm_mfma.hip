@@ -277,7 +277,7 @@ __device__ __forceinline__ Tile decode_tile(const FastFwdArgs &a, int kind, int 
 // XCD owns a contiguous eighth of the tile order; its workgroups take every
 // (gridDim.x / 8)-th tile of it.
 struct Cursor {
-    int kind, L, hi;
+    int kind, L, hi, step;
 };
 
 template <int BM, int MODE, int NWAVES>
@@ -308,12 +308,20 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
         const int total = mtiles * (kind == KIND_G1 ? ntn1 : ntn2);
         const int range = (total + 7) >> 3;
         c.kind = kind;
+        // 64-row tiles stream weights (HBM-bound): as many workgroups as make
+        // every round of the XCD's range full, so no round runs half-empty
+        int wg = per_xcd_wg;
+        if (!PIPE && BM == 64) {
+            const int rounds = (range + per_xcd_wg - 1) / per_xcd_wg;
+            wg = rounds > 0 ? (range + rounds - 1) / rounds : per_xcd_wg;
+        }
+        c.step = wg;
         c.L = xcd * range + slot;
         c.hi = min((xcd + 1) * range, total);
-        return c.L < c.hi;
+        return slot < wg && c.L < c.hi;
     };
     auto advance = [&](Cursor &c) {
-        c.L += per_xcd_wg;
+        c.L += c.step;
         if (c.L < c.hi)
             return true;
         if (PIPE && c.kind == KIND_G1)
