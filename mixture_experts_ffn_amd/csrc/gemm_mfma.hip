@@ -309,9 +309,11 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
         const int range = (total + 7) >> 3;
         c.kind = kind;
         // 64-row tiles stream weights (HBM-bound): as many workgroups as make
-        // every round of the XCD's range full, so no round runs half-empty
+        // every round of the XCD's range full, so no round runs half-empty.
+        // In the pipelined launch only for GEMM2: a workgroup left out goes
+        // on to the combine phase, whose waits other workgroups release.
         int wg = per_xcd_wg;
-        if (!PIPE && BM == 64) {
+        if (BM == 64 && (!PIPE || kind == KIND_G2)) {
             const int rounds = (range + per_xcd_wg - 1) / per_xcd_wg;
             wg = rounds > 0 ? (range + rounds - 1) / rounds : per_xcd_wg;
         }
