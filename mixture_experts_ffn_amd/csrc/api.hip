@@ -144,24 +144,48 @@ int check_device(int *num_cus = nullptr, int *clock_khz = nullptr)
     return MOE_FFN_OK;
 }
 
-// Tile height of the forward's M-tiles from the mean rows per expert: 64 for
-// small segments (decode); 128; 256 on the bf16 fast path when segments are
-// long (measured: 4 % faster at 2048 rows per expert, 6 % slower at 384,
-// where the coarser tiles leave more of the last round of tiles idle).
-moe::FwdTiles pick_tiles(const moe_ffn_problem &p)
+// Tile height of the forward's M-tiles from the mean rows per expert.  bf16
+// with whole tiles (the fast path): 64 for small segments (decode, bound by
+// weight streaming) and 128 (two workgroups per CU) up to 512 rows per expert
+// (gemm_mfma.hip); longer segments take 256-row tiles of the 256 x 256 tile
+// kernel (gemm_big.hip; measured: prefill's 384 rows per expert 345 vs 388 us
+// on GEMM1, forward+backward's 1024 rows 466 vs 446 us, the skewed shape's
+// 2048 rows 3.63 vs 3.35 ms).  The pipelined forward (one launch,
+// gemm_mfma.hip) keeps 128 up to 1024 rows, 256 above.  Other bf16 shapes
+// (the engine) use 64 or 128, fp32 64.  All fast-path kernels give the same
+// bits whatever the tile height.
+moe::FwdTiles pick_tiles(const moe_ffn_problem &p, uint32_t flags)
 {
     moe::FwdTiles t;
     t.num_cus = 0;
+    t.big = false;
     if (p.dtype == MOE_FFN_F32) {
         t.BM = 64;
+        return t;
+    }
+    const double avg_rows = (double)(p.T * p.K) / (double)p.E;
+    const bool fast = moe::fast_gemm_supported(p.dtype, p.H, p.I);
+    const bool pipe = (flags & MOE_FFN_PIPELINE) && p.Is == 0;
+    // the 256 x 256 kernel addresses token rows by 32-bit byte offsets
+    const int64_t TKp = p.T * (p.K + p.Is / p.I);
+    const bool offsets32 = p.T * p.H * 2 < (int64_t(1) << 32) && TKp * p.I * 2 < (int64_t(1) << 32);
+    if (avg_rows <= 64.0) {
+        t.BM = 64;
+    } else if (fast && !pipe && offsets32 && avg_rows > 512.0) {
+        t.BM = 256;
+        t.big = true;
     } else {
-        const double avg_rows = (double)(p.T * p.K) / (double)p.E;
-        const bool fast = moe::fast_gemm_supported(p.dtype, p.H, p.I);
-        // 128-row tiles (two workgroups per CU) up to 1024 rows per expert on
-        // average; longer segments amortise a 256-row tile's copies better
-        t.BM = avg_rows <= 64.0 ? 64 : (avg_rows <= 1024.0 || !fast) ? 128 : 256;
+        t.BM = (avg_rows <= 1024.0 || !fast) ? 128 : 256;
     }
     return t;
+}
+
+// the smallest tile height any call mode of this problem may use (sizes the
+// M-tile tables of the workspace, which serves every mode)
+int min_tile_rows(const moe_ffn_problem &p)
+{
+    const int a = pick_tiles(p, 0).BM, b = pick_tiles(p, MOE_FFN_PIPELINE).BM;
+    return a < b ? a : b;
 }
 
 // Region offsets inside the forward workspace (and the saved context).
@@ -176,7 +200,7 @@ struct FwdLayout {
     size_t s_hdr, s_counts, s_offsets, s_sorted, s_slotpos, s_h, saved_total;
 };
 
-FwdLayout fwd_layout(const moe_ffn_problem &p)
+FwdLayout fwd_layout(const moe_ffn_problem &p, uint32_t flags = 0)
 {
     FwdLayout L;
     const int64_t TK = p.T * p.K;
@@ -184,9 +208,9 @@ FwdLayout fwd_layout(const moe_ffn_problem &p)
     const int Ep = E + nshared(p);                  // experts of the plan
     const int64_t TKp = TK + (int64_t)nshared(p) * p.T; // permuted rows
     const size_t es = elem_size(p.dtype);
-    L.tiles = pick_tiles(p);
+    L.tiles = pick_tiles(p, flags);
     L.rp = moe::make_route_plan(TK, E);
-    L.max_mtiles = moe::max_mtiles_bound(TKp, Ep, L.tiles.BM);
+    L.max_mtiles = moe::max_mtiles_bound(TKp, Ep, min_tile_rows(p));
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -233,7 +257,7 @@ RouteLayout route_layout(const moe_ffn_problem &p)
     const int64_t TK = p.T * p.K;
     const int E = (int)p.E;
     R.rp = moe::make_route_plan(TK, E);
-    R.BM = pick_tiles(p).BM;
+    R.BM = pick_tiles(p, 0).BM;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -350,7 +374,7 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
     const int S = nshared(*p);
     if (S > 0 && !sh)
         return fail(MOE_FFN_ERR_NULL, "a problem with Is > 0 needs the shared-expert weights");
-    const FwdLayout L = fwd_layout(*p);
+    const FwdLayout L = fwd_layout(*p, flags);
     if (p->T == 0)
         return MOE_FFN_OK;
     if (S > 0 && ((rc = check_ptr(sh->up_proj_weight, "shared up_proj_weight")) ||
@@ -512,11 +536,16 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
             record(ev, MOE_FFN_STAGE_PIPELINE, false, s);
             return MOE_FFN_OK;
         }
+        const int g1mode = a.hsave ? moe::FAST_G1H : moe::FAST_G1;
         record(ev, MOE_FFN_STAGE_GEMM1, true, s);
-        HIP_TRY(moe::launch_fast_fwd(a.hsave ? moe::FAST_G1H : moe::FAST_G1, BM, a, num_cus, s), "gemm1 launch");
+        HIP_TRY(L.tiles.big ? moe::launch_fast_fwd_big(g1mode, a, num_cus, s)
+                            : moe::launch_fast_fwd(g1mode, BM, a, num_cus, s),
+                "gemm1 launch");
         record(ev, MOE_FFN_STAGE_GEMM1, false, s);
         record(ev, MOE_FFN_STAGE_GEMM2, true, s);
-        HIP_TRY(moe::launch_fast_fwd(moe::FAST_G2, BM, a, num_cus, s), "gemm2 launch");
+        HIP_TRY(L.tiles.big ? moe::launch_fast_fwd_big(moe::FAST_G2, a, num_cus, s)
+                            : moe::launch_fast_fwd(moe::FAST_G2, BM, a, num_cus, s),
+                "gemm2 launch");
         record(ev, MOE_FFN_STAGE_GEMM2, false, s);
     } else {
         // fp32: the generic kernels (gemm.hip)

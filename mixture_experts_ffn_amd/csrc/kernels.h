@@ -108,7 +108,8 @@ struct GroupedGemmArgs {
 
 // plan-level tile choice for the forward
 struct FwdTiles {
-    int BM;       // 64 or 128
+    int BM;       // 64, 128 or 256
+    bool big;     // bf16 fast path: the 256 x 256 tile kernel (BM = 256)
     int num_cus;  // compute units of the device (persistent grids)
 };
 
@@ -147,6 +148,10 @@ struct FastFwdArgs {
 enum { FAST_G1 = 0, FAST_G2 = 1, FAST_PIPE = 2, FAST_G1H = 3 }; // FAST_G1H: FAST_G1 saving h
 hipError_t launch_fast_fwd(int mode, int BM, const FastFwdArgs &a, int num_cus,
                            hipStream_t stream);
+// the same grouped GEMMs (FAST_G1, FAST_G1H, FAST_G2) on 256 x 256 tiles, one
+// 4-wave workgroup per CU (gemm_big.hip); the M-tile tables must be built for
+// 256-row tiles
+hipError_t launch_fast_fwd_big(int mode, const FastFwdArgs &a, int num_cus, hipStream_t stream);
 
 // bf16 engine (gemm_engine.hip): forward F1/F2 and backward B2/B4/B5/B7
 struct EngineArgs {
