@@ -176,6 +176,31 @@ int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids
  * moe_ffn_bwd_w take problems without a shared expert (Is == 0;
  * MOE_FFN_ERR_SHAPE otherwise). */
 
+/* ---- forward without allocation ------------------------------------------- */
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops and harnesses that forbid hipMalloc.  The
+ * inference forward (moe_ffn_fwd with saved = NULL) with its workspace taken
+ * from a scratch array the library keeps in device memory:
+ * MOE_FFN_NOALLOC_WS_BYTES (64 MiB) per GPU, one copy on each GPU the library
+ * runs on, held until the process ends.  Enough for decode-sized batches
+ * (T = 128, H = 7168, I = 2048, E = 32, K = 8 needs about 19 MB).  A problem
+ * whose workspace (moe_ffn_fwd_workspace_size) exceeds it is rejected with
+ * MOE_FFN_ERR_WORKSPACE before anything is launched; so is Is != 0 and
+ * MOE_FFN_CHECK_IDS (it copies to the host), with MOE_FFN_ERR_SHAPE.  The
+ * call allocates nothing (no hipMalloc, hipFree or allocating library call);
+ * the first call on a device resolves the array's address there.  Every
+ * call on one GPU uses the same array, which keeps the last call's contents
+ * (the forward initialises everything it reads): calls that overlap on one
+ * GPU (different streams, or threads) race and must be serialised by the
+ * caller.  Arguments, layout, ownership and the device status word
+ * (moe_ffn_read_status is not available: the workspace is private) are
+ * otherwise those of moe_ffn_fwd; y is written on `stream`. */
+#define MOE_FFN_NOALLOC_WS_BYTES ((size_t)64 << 20)
+int moe_ffn_fwd_noalloc(const moe_ffn_problem *p, const void *x, const void *topk_ids,
+                        const float *topk_weights, const void *up_proj_weight,
+                        const void *down_proj_weight, void *y, uint32_t flags, void *stream);
+
 /* ---- shared expert -------------------------------------------------------- */
 
 /* The optional shared expert (issue page, section 6.1 "shared-expert fused

@@ -33,6 +33,8 @@ __all__ = [
     "fwd_workspace_size",
     "route_workspace_size",
     "moe_ffn_fwd",
+    "moe_ffn_fwd_noalloc",
+    "NOALLOC_WS_BYTES",
     "moe_ffn_route",
     "read_status",
     "STAGES",
@@ -125,6 +127,7 @@ def load_library():
                                    ctypes.POINTER(StageEvents)],
             "moe_ffn_bwd_w": [pp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
             "moe_ffn_route": [pp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "moe_ffn_fwd_noalloc": [pp, vp, vp, vp, vp, vp, vp, u32, vp],
             "moe_ffn_read_status": [vp, vp, ctypes.POINTER(ctypes.c_int32)],
             "moe_ffn_event_create": [ctypes.POINTER(ctypes.c_void_p)],
             "moe_ffn_event_destroy": [vp],
@@ -285,6 +288,32 @@ def moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *,
     if return_ws:
         out += (ws,)
     return out[0] if len(out) == 1 else out
+
+
+def moe_ffn_fwd_noalloc(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, y, *,
+                        pipelined: bool = False, flags: int = 0):
+    """The inference forward into the caller's ``y`` [T, H] with no workspace:
+    the library's own per-GPU scratch (include/moe_ffn.h, moe_ffn_fwd_noalloc)
+    serves as the workspace, so nothing is allocated.  Raises MoEFFNError for
+    problems whose workspace exceeds NOALLOC_WS_BYTES."""
+    lib = load_library()
+    _require_gpu(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, y)
+    if topk_weights.dtype != torch.float32 or topk_weights.shape != topk_ids.shape:
+        raise MoEFFNError(3, "topk_weights must be float32 with the shape of topk_ids")
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
+        raise MoEFFNError(2, "y must be a contiguous tensor with the shape and dtype of x")
+    prob = make_problem(x, topk_ids, up_proj_weight, down_proj_weight)
+    flags |= PIPELINE if pipelined else 0
+    dev = x.device
+    with torch.cuda.device(dev):
+        rc = lib.moe_ffn_fwd_noalloc(ctypes.byref(prob), _ptr(x), _ptr(topk_ids),
+                                     _ptr(topk_weights), _ptr(up_proj_weight),
+                                     _ptr(down_proj_weight), _ptr(y), flags, _stream(dev))
+    _check(rc)
+    return y
+
+
+NOALLOC_WS_BYTES = 64 << 20  # MOE_FFN_NOALLOC_WS_BYTES
 
 
 def bwd_workspace_size(problem: Problem, flags: int = 0) -> int:

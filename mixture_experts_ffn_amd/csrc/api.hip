@@ -325,6 +325,34 @@ uint64_t problem_hash(const moe_ffn_problem &p)
     return h;
 }
 
+// Scratch of moe_ffn_fwd_noalloc: device memory that the library owns, one
+// copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address; noalloc_scratch() resolves, once per device
+// (with that device current), the device address of this GPU's copy.
+static __device__ __align__(256) unsigned char scratch[MOE_FFN_NOALLOC_WS_BYTES];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {};
+
+int noalloc_scratch(void **ptr)
+{
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return hip_fail(err, "hipGetDevice");
+    if (dev < 0 || dev >= 64)
+        return fail(MOE_FFN_ERR_DEVICE, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || !p)
+            return hip_fail(err, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MOE_FFN_OK;
+}
+
 template <typename P> P *at(void *base, size_t off)
 {
     return reinterpret_cast<P *>(static_cast<char *>(base) + off);
@@ -631,6 +659,36 @@ int moe_ffn_fwd(const moe_ffn_problem *p, const void *x, const void *topk_ids,
 {
     return moe_ffn_fwd_ex(p, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, y,
                           saved, ws, ws_bytes, flags, stream, nullptr);
+}
+
+int moe_ffn_fwd_noalloc(const moe_ffn_problem *p, const void *x, const void *topk_ids,
+                        const float *topk_weights, const void *up_proj_weight,
+                        const void *down_proj_weight, void *y, uint32_t flags, void *stream)
+{
+    g_err[0] = 0;
+    int rc = validate_problem(p);
+    if (rc)
+        return rc;
+    if (p->Is != 0)
+        return fail(MOE_FFN_ERR_SHAPE, "moe_ffn_fwd_noalloc: Is != 0 is not supported");
+    if (flags & MOE_FFN_CHECK_IDS)
+        return fail(MOE_FFN_ERR_SHAPE,
+                    "moe_ffn_fwd_noalloc: MOE_FFN_CHECK_IDS is not supported (it copies to the host)");
+    const FwdLayout L = fwd_layout(*p, flags);
+    if (L.ws_total > MOE_FFN_NOALLOC_WS_BYTES)
+        return fail(MOE_FFN_ERR_WORKSPACE,
+                    "moe_ffn_fwd_noalloc: this problem needs %zu bytes of scratch, more than the "
+                    "%zu the library holds per GPU; call moe_ffn_fwd with a workspace",
+                    L.ws_total, (size_t)MOE_FFN_NOALLOC_WS_BYTES);
+    if (p->T == 0)
+        return MOE_FFN_OK;
+    if ((rc = check_device()))
+        return rc;
+    void *ws = nullptr;
+    if ((rc = noalloc_scratch(&ws)))
+        return rc;
+    return fwd_run(p, x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, nullptr, y,
+                   nullptr, ws, MOE_FFN_NOALLOC_WS_BYTES, flags, stream, nullptr);
 }
 
 int moe_ffn_route_workspace_size(const moe_ffn_problem *p, size_t *ws_bytes)
