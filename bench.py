@@ -22,8 +22,15 @@ Besides tokens/s the line carries
   decode shape), its algorithmic work per launch divided by its average
   launch time, where the launch times come from HIP events that the library
   records around that kernel on the call's stream during the timed steps;
+* "stage_roofline": each bulk forward stage (GEMM1, GEMM2, combine) against
+  both bounds, from its algorithmic bytes and flops per launch;
 * "cpu_baseline": the CPU oracle on the host's cores over a bounded sample of
-  the same workload (its first tokens), unless --no-cpu-baseline.
+  the same workload (its first tokens), unless --no-cpu-baseline;
+* with the default workload, "decode": the same record (ms/step, the layer's
+  fraction of peak HBM bandwidth, roofline of each kernel, cpu_baseline) for
+  the weight-streaming decode shape (T=128, H=7168, I=2048, E=32, K=8),
+  measured in the same process after the prefill record (--no-decode skips
+  it).
 """
 
 from __future__ import annotations
@@ -57,6 +64,9 @@ def parse():
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="steps timed one by one after evicting the caches (512 MiB written "
                          "between steps, outside the timed region); 0 to skip")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="with the default prefill workload, skip the decode record that "
+                         "otherwise follows it in the same line")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one elementwise copy of this many MiB (for scaling HBM "
                          "byte counters against a kernel of known traffic)")
@@ -70,13 +80,32 @@ def main():
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
+    import torch  # noqa: F401
+
+    import mixture_experts_ffn_amd as m
+
+    m.load_library()
+    out = measure(args.workload, args, primary=True)
+    # The metric's HBM half: the weight-streaming decode shape, measured in the
+    # same process after the default (prefill) workload
+    if args.workload == "prefill_bf16" and not args.no_decode:
+        dec = measure("decode_bf16", args, primary=False)
+        out["decode"] = {k: dec[k] for k in ("value", "unit", "ms_per_step", "config", "layer",
+                                              "launch", "eager", "graph_replay",
+                                              "pipelined_twin", "roofline", "stage_roofline",
+                                              "cpu_baseline", "hbm_reference")
+                         if k in dec}
+    print(json.dumps(out), flush=True)
+
+
+def measure(workload_name, args, primary):
+    """Time one workload; returns the bench record (metric, value, roofline, ...)."""
     import torch
 
     import mixture_experts_ffn_amd as m
     from synth import make_inputs, workload
 
-    m.load_library()
-    w = workload(args.workload)
+    w = workload(workload_name)
     inp = make_inputs(w, with_dy=w.backward)
     dev = torch.device("cuda:0")
 
@@ -91,6 +120,7 @@ def main():
     prob.Is = w.Is
     ws_bytes, _ = m.fwd_workspace_size(prob)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    tile_rows, kernel_family = m.fwd_plan(prob)
 
     bws = None
     if w.backward:
@@ -98,7 +128,6 @@ def main():
 
     sh = ({"shared_up_proj_weight": d["shared_up"], "shared_down_proj_weight": d["shared_down"]}
           if w.Is else {})
-
     def step(ev=None, bev=None, pipelined=False):
         if not w.backward:
             return m.moe_ffn_fwd(d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
@@ -232,9 +261,11 @@ def main():
         k_bytes = ((live.sum() * w.I + w.Is) * w.H * 2 * es + w.T * w.H * es
                    + w.T * (w.K * w.I + w.Is) * es)
         k_ms = stage_ms["gemm1"]
-        kernel = ("moe::fast::moe_fwd_bf16<BM, FAST_G1> (gathered up_proj GEMM + SwiGLU)"
-                  if w.dtype == "bf16" and w.H % 256 == 0 and w.I % 128 == 0 else
-                  "up_proj GEMM + SwiGLU (engine / generic kernel)")
+        kernel = {"tiles": f"moe::fast::moe_fwd_bf16<{tile_rows}, FAST_G1> "
+                           "(gathered up_proj GEMM + SwiGLU)",
+                  "big_tiles": "moe::big::moe_fwd_bf16_big<FAST_G1> "
+                               "(gathered up_proj GEMM + SwiGLU, 256 x 256 tiles)",
+                  }.get(kernel_family, f"up_proj GEMM + SwiGLU ({kernel_family} kernel)")
     if w.name.startswith("decode"):
         roof = {"bound": "hbm", "achieved": k_bytes / (k_ms * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -243,9 +274,29 @@ def main():
         roof = {"bound": "mfma", "achieved": k_flops / (k_ms * 1e-3) / 1e12, "peak": peak,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(w.name, "pipeline" if pipelined else "gemm1")
+    roof["traffic"] = measured_traffic(w.name, "pipeline" if pipelined else "gemm1",
+                                       "gemm_big.hip" if kernel_family == "big_tiles"
+                                       else "gemm_mfma.hip")
     roof["kernel"] = kernel
     roof["avg_launch_ms"] = k_ms
+    # every stage of the bulk forward against its own bound: algorithmic bytes
+    # (weights of live experts, activations in and out) or flops per launch
+    stage_roof = {}
+    if not pipelined and "gemm2" in stage_ms:
+        nl = live.sum() * w.I + w.Is
+        TKp = w.T * (w.K + w.Is // w.I)
+        g1_bytes = nl * w.H * 2 * es + w.T * w.H * es + TKp * w.I * es
+        g2_bytes = nl * w.H * es + TKp * w.I * es + TKp * w.H * es
+        cb_bytes = TKp * w.H * es + w.T * w.H * es + w.T * w.K * 8
+        for name, nbytes, nflops in (("gemm1", g1_bytes, k_flops),
+                                     ("gemm2", g2_bytes, k_flops / 2),
+                                     ("combine", cb_bytes, 0.0)):
+            t = stage_ms[name] * 1e-3
+            stage_roof[name] = {"ms": stage_ms[name], "hbm_gbs": nbytes / t / 1e9,
+                                "hbm_frac": nbytes / t / 1e9 / PEAK_HBM_GBS,
+                                "tflops": nflops / t / 1e12,
+                                "mfma_frac": nflops / t / 1e12 / (
+                                    PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS)}
 
     out = {
         "metric": METRIC,
@@ -279,8 +330,12 @@ def main():
                            "tokens_per_s": w.T * args.steps / pipe_elapsed,
                            "stage_ms": pipe_stage_ms},
         "roofline": roof,
+        "stage_roofline": stage_roof,
         "cpu_baseline": None,
     }
+    if w.name.startswith("decode"):
+        # the HBM half of the metric: the whole layer's algorithmic bytes per step
+        out["layer"]["hbm_frac_alg"] = out["layer"]["hbm_gbs_alg"] / PEAK_HBM_GBS
 
     if w.dtype == "bf16" and not w.name.startswith("decode"):
         out["dense_reference"] = dense_reference(w, dev)
@@ -297,7 +352,7 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, y, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def dense_reference(w, dev, reps=20):
@@ -347,13 +402,13 @@ def hbm_reference(dev, mib=2048, reps=10):
     return {"bytes_moved": 2 * n * 4, "ms": ms, "gbs": 2 * n * 4 / (ms * 1e-3) / 1e9}
 
 
-def measured_traffic(workload_name, kernel):
+def measured_traffic(workload_name, kernel, source="gemm_mfma.hip"):
     """HBM bytes per launch of the dominant kernel from the committed PMC summary
     (profiles/traffic.txt), or None when the kernel source has changed since the
     counters were taken or no summary exists for this workload and kernel."""
     import hashlib
 
-    src = os.path.join(ROOT, "mixture_experts_ffn_amd", "csrc", "gemm_mfma.hip")
+    src = os.path.join(ROOT, "mixture_experts_ffn_amd", "csrc", source)
     table = os.path.join(ROOT, "profiles", "traffic.txt")
     if not (os.path.exists(src) and os.path.exists(table)):
         return None
@@ -361,7 +416,7 @@ def measured_traffic(workload_name, kernel):
     for line in open(table):
         parts = line.split()
         if (len(parts) == 5 and parts[0] == workload_name and parts[1] == kernel
-                and parts[2] == f"gemm_mfma.hip:{sha}"):
+                and parts[2] == f"{source}:{sha}"):
             vals = dict(p.split("=") for p in parts[3:])
             return float(vals["fetch_bytes"]) + float(vals["write_bytes"])
     return None

@@ -150,8 +150,11 @@ typedef struct {
 
 /* Sizes of the forward workspace and of the saved context that the backward
  * needs (a header naming the problem, the route arrays and the pre-activation
- * h = x·up_proj_weight in the problem dtype).  Pure host function; no device
- * is touched. */
+ * h = x·up_proj_weight in the problem dtype).  The query half of the
+ * two-phase operator interface (HyperMegaMoE issue page, section 2.3: a
+ * workspace-size entry and an execute entry per direction; section 5.3: the
+ * host computes the workspace size).  Pure host function; no device is
+ * touched; errors as moe_ffn_fwd's host checks. */
 int moe_ffn_fwd_workspace_size(const moe_ffn_problem *p, uint32_t flags, size_t *ws_bytes,
                                size_t *saved_bytes);
 
@@ -166,6 +169,30 @@ int moe_ffn_fwd(const moe_ffn_problem *p, const void *x, const void *topk_ids,
                 const float *topk_weights, const void *up_proj_weight,
                 const void *down_proj_weight, void *y, void *saved, void *ws, size_t ws_bytes,
                 uint32_t flags, void *stream);
+
+/* Where an inference forward (saved = NULL) leaves its intermediate stages in
+ * `ws`, for checking the path stage by stage against a reference (the overlap
+ * explainer page, section 6: validate a pipelined operator against the plain
+ * stage sequence one stage at a time).  Byte offsets into ws, valid for that
+ * problem and flags until ws is used again: counts [E] and offsets [E+1]
+ * (int32), sorted_slot [T·K] and slot_pos [T·K] (int32, the routing of
+ * moe_ffn_route), act [T·K, I] and o [T·K, H] (problem dtype, rows in the
+ * permuted, expert-major order of sorted_slot).  With a shared expert the
+ * arrays continue with its Is / I chunks of T rows each.  Also the tile
+ * height and the kernel family the forward runs for this problem and flags.
+ * Pure host function; a test and debugging hook, not needed to run the
+ * layer. */
+typedef struct {
+    size_t counts, offsets, sorted_slot, slot_pos, act, o;
+    int32_t tile_rows; /* rows per M-tile of the grouped GEMMs */
+    int32_t kernel;    /* their kernel: MOE_FFN_KERNEL_* */
+} moe_ffn_fwd_stage_layout;
+#define MOE_FFN_KERNEL_GENERIC 0   /* fp32 */
+#define MOE_FFN_KERNEL_ENGINE 1    /* bf16, H % 256 or I % 128 != 0 */
+#define MOE_FFN_KERNEL_TILES 2     /* bf16 tile kernel: 64 or 128-row tiles */
+#define MOE_FFN_KERNEL_BIG_TILES 3 /* bf16 256 x 256 tile kernel */
+#define MOE_FFN_KERNEL_PIPELINED 4 /* bf16 one-launch forward (MOE_FFN_PIPELINE) */
+int moe_ffn_fwd_stages(const moe_ffn_problem *p, uint32_t flags, moe_ffn_fwd_stage_layout *layout);
 
 /* moe_ffn_fwd with the per-stage timing hook (ev may be NULL). */
 int moe_ffn_fwd_ex(const moe_ffn_problem *p, const void *x, const void *topk_ids,
@@ -260,8 +287,10 @@ int moe_ffn_route(const moe_ffn_problem *p, const void *topk_ids, int32_t *count
 
 /* ---- backward ------------------------------------------------------------- */
 
-/* Size of the backward workspace. Pure host function.  The backward supports
- * bf16 problems (MOE_FFN_ERR_DTYPE for fp32). */
+/* Size of the backward workspace: the query half of the backward's
+ * two-phase interface (HyperMegaMoE issue page, section 2.3).  Pure host
+ * function.  The backward supports bf16 problems (MOE_FFN_ERR_DTYPE for
+ * fp32). */
 int moe_ffn_bwd_workspace_size(const moe_ffn_problem *p, uint32_t flags, size_t *ws_bytes);
 
 /* Gradients of y with respect to the inputs, given dy [T, H] and the `saved`
@@ -317,7 +346,12 @@ int moe_ffn_bwd_w(const moe_ffn_problem *p, const void *dy, const void *x, const
 /* Synchronises `stream`, then reads the device status word that the last
  * forward, route or backward call on this workspace left: 0, or an OR of
  * MOE_FFN_DEV_BAD_ID and MOE_FFN_DEV_TIMEOUT (forward, route) or
- * MOE_FFN_DEV_BAD_SAVED, MOE_FFN_DEV_BAD_WS (backward). */
+ * MOE_FFN_DEV_BAD_SAVED, MOE_FFN_DEV_BAD_WS (backward).  The status word lives
+ * in the caller's workspace of the two-phase interface (HyperMegaMoE issue
+ * page, section 2.3); conditions only the device can see (an expert id out
+ * of range, issue page section 4.2) are reported there instead of failing a
+ * call that has already returned.  `ws` is a device pointer; device_status a
+ * host pointer; MOE_FFN_ERR_NULL or MOE_FFN_ERR_HIP on failure. */
 int moe_ffn_read_status(const void *ws, void *stream, int32_t *device_status);
 
 /* Static text for a status code. */

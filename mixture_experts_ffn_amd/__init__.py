@@ -35,6 +35,8 @@ __all__ = [
     "moe_ffn_fwd",
     "moe_ffn_fwd_noalloc",
     "NOALLOC_WS_BYTES",
+    "fwd_stages",
+    "fwd_plan",
     "moe_ffn_route",
     "read_status",
     "STAGES",
@@ -88,6 +90,24 @@ class SharedGrads(ctypes.Structure):
     _fields_ = [("d_up_proj_weight", ctypes.c_void_p), ("d_down_proj_weight", ctypes.c_void_p)]
 
 
+class FwdStageLayout(ctypes.Structure):
+    """Byte offsets of the forward's intermediate stages in its workspace."""
+
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("counts", "offsets", "sorted_slot", "slot_pos", "act", "o")] + \
+               [("tile_rows", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+
+
+KERNELS = {0: "generic", 1: "engine", 2: "tiles", 3: "big_tiles", 4: "pipelined"}
+
+
+def fwd_plan(problem: Problem, flags: int = 0):
+    """(tile rows, kernel family name) the forward runs for this problem."""
+    lay = FwdStageLayout()
+    _check(load_library().moe_ffn_fwd_stages(ctypes.byref(problem), flags, ctypes.byref(lay)))
+    return lay.tile_rows, KERNELS[lay.kernel]
+
+
 class StageEvents(ctypes.Structure):
     _fields_ = [("begin", ctypes.c_void_p * 8), ("end", ctypes.c_void_p * 8)]
 
@@ -128,6 +148,7 @@ def load_library():
             "moe_ffn_bwd_w": [pp, vp, vp, vp, vp, vp, vp, sz, u32, vp],
             "moe_ffn_route": [pp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_ffn_fwd_noalloc": [pp, vp, vp, vp, vp, vp, vp, u32, vp],
+            "moe_ffn_fwd_stages": [pp, u32, ctypes.POINTER(FwdStageLayout)],
             "moe_ffn_read_status": [vp, vp, ctypes.POINTER(ctypes.c_int32)],
             "moe_ffn_event_create": [ctypes.POINTER(ctypes.c_void_p)],
             "moe_ffn_event_destroy": [vp],
@@ -288,6 +309,28 @@ def moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *,
     if return_ws:
         out += (ws,)
     return out[0] if len(out) == 1 else out
+
+
+def fwd_stages(x, topk_ids, up_proj_weight, down_proj_weight, ws, flags: int = 0):
+    """Views of the intermediate stages an inference forward left in ``ws``:
+    counts, offsets, sorted_slot, slot_pos (int32) and act [TK, I], o [TK, H]
+    in the problem dtype, rows in permuted (expert-major) order."""
+    prob = make_problem(x, topk_ids, up_proj_weight, down_proj_weight)
+    lay = FwdStageLayout()
+    _check(load_library().moe_ffn_fwd_stages(ctypes.byref(prob), flags, ctypes.byref(lay)))
+    T, K, E = prob.T, prob.K, prob.E
+    I, H = prob.I, prob.H
+
+    def view(off, n, dtype, shape):
+        nb = n * torch.empty((), dtype=dtype).element_size()
+        return ws[off:off + nb].view(dtype).view(shape)
+
+    return dict(counts=view(lay.counts, E, torch.int32, (E,)),
+                offsets=view(lay.offsets, E + 1, torch.int32, (E + 1,)),
+                sorted_slot=view(lay.sorted_slot, T * K, torch.int32, (T * K,)),
+                slot_pos=view(lay.slot_pos, T * K, torch.int32, (T * K,)),
+                act=view(lay.act, T * K * I, x.dtype, (T * K, I)),
+                o=view(lay.o, T * K * H, x.dtype, (T * K, H)))
 
 
 def moe_ffn_fwd_noalloc(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, y, *,

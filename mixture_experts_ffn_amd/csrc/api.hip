@@ -388,6 +388,31 @@ int moe_ffn_fwd_workspace_size(const moe_ffn_problem *p, uint32_t flags, size_t 
     return MOE_FFN_OK;
 }
 
+int moe_ffn_fwd_stages(const moe_ffn_problem *p, uint32_t flags, moe_ffn_fwd_stage_layout *layout)
+{
+    g_err[0] = 0;
+    int rc = validate_problem(p);
+    if (rc)
+        return rc;
+    if (!layout)
+        return fail(MOE_FFN_ERR_NULL, "layout is NULL");
+    const FwdLayout L = fwd_layout(*p, flags);
+    layout->counts = L.counts;
+    layout->offsets = L.offsets;
+    layout->sorted_slot = L.sorted_slot;
+    layout->slot_pos = L.slot_pos;
+    layout->act = L.act;
+    layout->o = L.o;
+    layout->tile_rows = L.tiles.BM;
+    const bool fast = moe::fast_gemm_supported(p->dtype, p->H, p->I);
+    layout->kernel = p->dtype == MOE_FFN_F32 ? MOE_FFN_KERNEL_GENERIC
+                     : !fast                 ? MOE_FFN_KERNEL_ENGINE
+                     : ((flags & MOE_FFN_PIPELINE) && p->Is == 0) ? MOE_FFN_KERNEL_PIPELINED
+                     : L.tiles.big           ? MOE_FFN_KERNEL_BIG_TILES
+                                             : MOE_FFN_KERNEL_TILES;
+    return MOE_FFN_OK;
+}
+
 // The forward, with or without a shared expert (sh: its weights; p->Is > 0).
 static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids,
                    const float *topk_weights, const void *up_proj_weight,
