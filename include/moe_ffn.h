@@ -297,7 +297,12 @@ int moe_ffn_bwd_workspace_size(const moe_ffn_problem *p, uint32_t flags, size_t 
  * context written by moe_ffn_fwd for the same problem and inputs (section 2.2):
  * dx [T, H], d_up_proj_weight [E, H, 2I], d_down_proj_weight [E, I, H] in the
  * problem dtype and d_topk_weights [T, K] fp32.  Outputs are overwritten, not
- * accumulated; an expert that received no slot gets exact zero gradients. */
+ * accumulated; an expert that received no slot gets exact zero gradients.
+ * The weight gradients run beside input_grad and the dx combine (section
+ * 2.2): on a second stream the library creates per device (default
+ * priority, on the first call), forked from and joined back to `stream` by
+ * events, so the outputs are valid once `stream` reaches the call and the
+ * call can be captured into a graph like any single-stream work. */
 int moe_ffn_bwd(const moe_ffn_problem *p, const void *dy, const void *x, const void *topk_ids,
                 const float *topk_weights, const void *up_proj_weight,
                 const void *down_proj_weight, const void *saved, void *dx,

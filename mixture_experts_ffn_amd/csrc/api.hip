@@ -353,6 +353,46 @@ int noalloc_scratch(void **ptr)
     return MOE_FFN_OK;
 }
 
+// The backward's second stream (default priority, like every stream here):
+// the weight-gradient branch runs on it beside input_grad and the dx combine.
+// Created once per device, with its two events, on the first whole backward
+// (normally an eager call, before any graph capture).
+// The events are shared by the calls on one device, so a call holds the
+// device's enqueue lock from its first record to its last wait.
+struct SideStream {
+    hipStream_t s;
+    hipEvent_t ready; // the main stream reached the branch point
+    hipEvent_t done;  // the side stream finished its branch
+};
+std::mutex g_side_mu;
+std::mutex g_side_enqueue[64];
+SideStream g_side[64];
+bool g_side_ok[64] = {};
+
+int side_stream(SideStream *out, std::unique_lock<std::mutex> *enqueue_lock)
+{
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return hip_fail(err, "hipGetDevice");
+    if (dev < 0 || dev >= 64)
+        return fail(MOE_FFN_ERR_DEVICE, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    if (!g_side_ok[dev]) {
+        SideStream ss{};
+        if ((err = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess)
+            return hip_fail(err, "hipStreamCreateWithFlags");
+        if ((err = hipEventCreateWithFlags(&ss.ready, hipEventDisableTiming)) != hipSuccess ||
+            (err = hipEventCreateWithFlags(&ss.done, hipEventDisableTiming)) != hipSuccess)
+            return hip_fail(err, "hipEventCreateWithFlags");
+        g_side[dev] = ss;
+        g_side_ok[dev] = true;
+    }
+    *out = g_side[dev];
+    *enqueue_lock = std::unique_lock<std::mutex>(g_side_enqueue[dev]);
+    return MOE_FFN_OK;
+}
+
 template <typename P> P *at(void *base, size_t off)
 {
     return reinterpret_cast<P *>(static_cast<char *>(base) + off);
@@ -914,6 +954,18 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
     base.E = Ep;
     base.Er = E;
 
+    // The whole backward overlaps its two branches (issue page, section 2.2:
+    // W2Grad beside the activation-gradient branch, W1Grad beside the dx
+    // combine): after act_grad, the weight gradients (which need only act_g,
+    // dh, dY and x) run on a second stream of the same priority while
+    // input_grad and the dx combine run on the caller's stream, joined by
+    // events.  The split entry points keep one stream (their caller schedules).
+    const bool overlap = do_d && do_w;
+    SideStream side{};
+    std::unique_lock<std::mutex> enqueue_lock;
+    if (overlap && (rc = side_stream(&side, &enqueue_lock)))
+        return rc;
+    hipStream_t sw = overlap ? side.s : s; // stream of the weight-gradient branch
     if (do_d) {
         // act_grad with the SwiGLU backward in its epilogue: dh, act_g, d_g partials
         moe::EngineArgs a2 = base;
@@ -939,6 +991,12 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
         HIP_TRY(moe::launch_engine(moe::ENG_B2, B.BM, a2, num_cus, s), "act_grad launch");
         record(ev, MOE_FFN_STAGE_BWD_ACT_GRAD, false, s);
 
+        if (overlap) {
+            HIP_TRY(hipEventRecord(side.ready, s), "event record");
+            HIP_TRY(hipStreamWaitEvent(sw, side.ready, 0), "stream wait");
+        }
+    }
+    if (do_d) {
         // input_grad: dx_perm = dh W1[e]^T
         moe::EngineArgs a4 = base;
         a4.A = dh;
@@ -982,9 +1040,9 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
             a5.cs_cstride = (int64_t)I * H;
             a5.cs_ldc = H;
         }
-        record(ev, MOE_FFN_STAGE_BWD_W2_GRAD, true, s);
-        HIP_TRY(moe::launch_engine(moe::ENG_B5, B.BM, a5, num_cus, s), "W2Grad launch");
-        record(ev, MOE_FFN_STAGE_BWD_W2_GRAD, false, s);
+        record(ev, MOE_FFN_STAGE_BWD_W2_GRAD, true, sw);
+        HIP_TRY(moe::launch_engine(moe::ENG_B5, B.BM, a5, num_cus, sw), "W2Grad launch");
+        record(ev, MOE_FFN_STAGE_BWD_W2_GRAD, false, sw);
 
         // W1Grad: dW1[e] = x_perm^T dh
         moe::EngineArgs a7 = base;
@@ -1002,10 +1060,14 @@ static int bwd_run(const moe_ffn_problem *p, int stage, const void *dy, const vo
             a7.cs_ldc = (int)(2 * Is);
             a7.cs_cjump = (int)(Is - I);
         }
-        record(ev, MOE_FFN_STAGE_BWD_W1_GRAD, true, s);
-        HIP_TRY(moe::launch_engine(moe::ENG_B7, B.BM, a7, num_cus, s), "W1Grad launch");
-        record(ev, MOE_FFN_STAGE_BWD_W1_GRAD, false, s);
+        record(ev, MOE_FFN_STAGE_BWD_W1_GRAD, true, sw);
+        HIP_TRY(moe::launch_engine(moe::ENG_B7, B.BM, a7, num_cus, sw), "W1Grad launch");
+        record(ev, MOE_FFN_STAGE_BWD_W1_GRAD, false, sw);
     }
+    if (overlap)
+        HIP_TRY(hipEventRecord(side.done, sw), "event record");
+    if (overlap)
+        HIP_TRY(hipStreamWaitEvent(s, side.done, 0), "stream wait");
     return MOE_FFN_OK;
 }
 
