@@ -9,7 +9,7 @@ combine as separate launches).  The step is timed eagerly (with per-stage HIP
 events) and as a HIP graph replay of the same calls (every kernel runs every
 step; only the host-side launch work is gone); the headline is the replay when
 its output equals the eager output bit for bit.  The pipelined twin (the two
-grouped GEMMs and the combine in one launch with tile-granular release) is
+grouped GEMMs in one launch with tile-granular release, then the combine) is
 timed after it and reported as "pipelined_twin".  Prints ONE JSON line.
 
 Default workload: prefill, bf16 with fp32 accumulation, T=4096 tokens,
@@ -17,9 +17,8 @@ H=2048, I=1408, E=64 experts, K=6, uniform routing.  Other workloads:
 --workload {tiny_f32,prefill_bf16,skewed_bf16,decode_bf16,fwdbwd_bf16}.
 
 Besides tokens/s the line carries
-* "roofline": the dominant kernel (the pipelined forward launch, else the
-  up_proj GEMM with SwiGLU epilogue; against HBM bandwidth for the HBM-bound
-  decode shape), its algorithmic work per launch divided by its average
+* "roofline": the dominant kernel (the up_proj GEMM with its SwiGLU epilogue;
+  against HBM bandwidth for the HBM-bound decode shape), its algorithmic work per launch divided by its average
   launch time, where the launch times come from HIP events that the library
   records around that kernel on the call's stream during the timed steps;
 * "stage_roofline": each bulk forward stage (GEMM1, GEMM2, combine) against
@@ -232,7 +231,6 @@ def measure(workload_name, args, primary):
     cold_stats = cold(args.cold_steps) if args.cold_steps > 0 else None
     y_graph, graph_elapsed = graphed()
     graph_ok = bool(torch.equal(y_graph, y))
-    pipelined = "pipeline" in stage_ms
 
     eager_ms = elapsed / args.steps * 1e3
     # the headline: graph replay of the default step when it reproduces the
@@ -246,26 +244,22 @@ def measure(workload_name, args, primary):
     layer_flops = w.fwd_flops() + (w.bwd_flops() if w.backward else 0.0)
     layer_bytes = ((live.sum() * w.I + w.Is) * 3 * w.H * es + 2 * w.T * w.H * es
                    + w.T * w.K * 8)
-    if pipelined:
-        # dominant kernel: the pipelined forward's one launch (both grouped GEMMs
-        # and the combine); algorithmic work = the forward's flops, or for the
-        # HBM-bound decode shape the forward's algorithmic bytes
-        k_flops = w.fwd_flops()
-        k_bytes = layer_bytes
-        k_ms = stage_ms["pipeline"]
-        kernel = "moe::fast::moe_fwd_bf16<BM, FAST_PIPE> (GEMM1+SwiGLU, GEMM2, combine)"
-    else:
-        # dominant kernel: the gathered up_proj GEMM with the SwiGLU epilogue
-        # (one launch covers the routed experts and the shared expert's chunks)
-        k_flops = 4.0 * w.T * w.H * (w.K * w.I + w.Is)
-        k_bytes = ((live.sum() * w.I + w.Is) * w.H * 2 * es + w.T * w.H * es
-                   + w.T * (w.K * w.I + w.Is) * es)
-        k_ms = stage_ms["gemm1"]
-        kernel = {"tiles": f"moe::fast::moe_fwd_bf16<{tile_rows}, FAST_G1> "
-                           "(gathered up_proj GEMM + SwiGLU)",
-                  "big_tiles": "moe::big::moe_fwd_bf16_big<FAST_G1> "
-                               "(gathered up_proj GEMM + SwiGLU, 256 x 256 tiles)",
-                  }.get(kernel_family, f"up_proj GEMM + SwiGLU ({kernel_family} kernel)")
+    nl = live.sum() * w.I + w.Is
+    TKp = w.T * (w.K + w.Is // w.I)
+    g1_bytes = nl * w.H * 2 * es + w.T * w.H * es + TKp * w.I * es
+    g2_bytes = nl * w.H * es + TKp * w.I * es + TKp * w.H * es
+    cb_bytes = TKp * w.H * es + w.T * w.H * es + w.T * w.K * 8
+    # dominant kernel: the gathered up_proj GEMM with the SwiGLU epilogue
+    # (one launch covers the routed experts and the shared expert's chunks)
+    k_flops = 4.0 * w.T * w.H * (w.K * w.I + w.Is)
+    k_bytes = ((live.sum() * w.I + w.Is) * w.H * 2 * es + w.T * w.H * es
+               + w.T * (w.K * w.I + w.Is) * es)
+    k_ms = stage_ms["gemm1"]
+    kernel = {"tiles": f"moe::fast::moe_fwd_bf16<{tile_rows}, FAST_G1> "
+                       "(gathered up_proj GEMM + SwiGLU)",
+              "big_tiles": "moe::big::moe_fwd_bf16_big<FAST_G1> "
+                           "(gathered up_proj GEMM + SwiGLU, 256 x 256 tiles)",
+              }.get(kernel_family, f"up_proj GEMM + SwiGLU ({kernel_family} kernel)")
     if w.name.startswith("decode"):
         roof = {"bound": "hbm", "achieved": k_bytes / (k_ms * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -274,7 +268,7 @@ def measure(workload_name, args, primary):
         roof = {"bound": "mfma", "achieved": k_flops / (k_ms * 1e-3) / 1e12, "peak": peak,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(w.name, "pipeline" if pipelined else "gemm1",
+    roof["traffic"] = measured_traffic(w.name, "gemm1",
                                        "gemm_big.hip" if kernel_family == "big_tiles"
                                        else "gemm_mfma.hip")
     roof["kernel"] = kernel
@@ -282,12 +276,7 @@ def measure(workload_name, args, primary):
     # every stage of the bulk forward against its own bound: algorithmic bytes
     # (weights of live experts, activations in and out) or flops per launch
     stage_roof = {}
-    if not pipelined and "gemm2" in stage_ms:
-        nl = live.sum() * w.I + w.Is
-        TKp = w.T * (w.K + w.Is // w.I)
-        g1_bytes = nl * w.H * 2 * es + w.T * w.H * es + TKp * w.I * es
-        g2_bytes = nl * w.H * es + TKp * w.I * es + TKp * w.H * es
-        cb_bytes = TKp * w.H * es + w.T * w.H * es + w.T * w.K * 8
+    if "gemm2" in stage_ms:
         for name, nbytes, nflops in (("gemm1", g1_bytes, k_flops),
                                      ("gemm2", g2_bytes, k_flops / 2),
                                      ("combine", cb_bytes, 0.0)):
@@ -326,7 +315,9 @@ def measure(workload_name, args, primary):
         "graph_replay": {"ms_per_step": graph_elapsed / args.steps * 1e3,
                          "tokens_per_s": w.T * args.steps / graph_elapsed,
                          "output_equals_eager": graph_ok},
-        "pipelined_twin": {"ms_per_step": pipe_elapsed / args.steps * 1e3,
+        "pipelined_twin": {"kernel": f"moe::fast::moe_fwd_bf16<{m.fwd_plan(prob, m.PIPELINE)[0]}, "
+                                     "FAST_PIPE> (GEMM1+SwiGLU, GEMM2 in one launch)",
+                           "ms_per_step": pipe_elapsed / args.steps * 1e3,
                            "tokens_per_s": w.T * args.steps / pipe_elapsed,
                            "stage_ms": pipe_stage_ms},
         "roofline": roof,

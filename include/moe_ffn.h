@@ -79,22 +79,31 @@ typedef struct {
 #define MOE_FFN_CHECK_IDS 0x1u /* fwd: after routing, synchronise the stream and return
                                   MOE_FFN_ERR_EXPERT_ID before any GEMM runs if an id was
                                   out of range (the call is then synchronous). */
-/* fwd, bf16 with H % 256 == 0 and I % 128 == 0: run GEMM1, GEMM2 and the
- * combine as ONE persistent launch with tile-granular release (the overlap
- * explainer page, sections 5-6: a consumer tile starts once the producer tiles
- * it reads have signalled, instead of at a launch boundary).  Device counters
- * in `ws`, zeroed by the routing step of the same call, record per GEMM1 /
- * GEMM2 M-tile how many of its N-tiles are done; a GEMM2 tile waits for all
- * GEMM1 N-tiles of its M-tile, a combine unit for the GEMM2 M-tiles of its
- * slots.  Every wait is bounded by a watchdog (2 s): on expiry the status
- * word gets MOE_FFN_DEV_TIMEOUT and the kernel still runs to its end, so a
- * stream never hangs.  The launch assumes that one workgroup per CU can be
- * resident at once (nothing else running on the device); if not, waits may
- * time out.  Without the flag (and for other shapes) the forward is the bulk
- * twin: GEMM1, GEMM2 and combine as separate launches.  Both give bitwise
- * identical outputs; the bulk twin is the default because it is currently
- * the faster of the two on compute-bound shapes. */
+/* fwd, bf16 with H % 256 == 0 and I % 128 == 0: run GEMM1 and GEMM2 as ONE
+ * persistent launch with tile-granular release (the overlap explainer page,
+ * sections 5-6: a consumer tile starts once the producer tiles it reads have
+ * signalled, instead of at a launch boundary), followed by the combine
+ * launch.  Device counters in `ws`, zeroed by the routing step of the same
+ * call, record per GEMM1 M-tile how many of its N-tiles are done, and a
+ * GEMM2 tile waits for all GEMM1 N-tiles of its M-tile.  Tiles are handed out
+ * by ticket counters (one per XCD slice of the tile order, a workgroup whose
+ * slice is exhausted drawing from the others), and GEMM2 tickets only after
+ * every GEMM1 tile has been claimed: a tile is only ever waited for once a
+ * running workgroup owns it, so the waits do not depend on how many of the
+ * launch's workgroups are resident (another stream's kernel, a partitioned
+ * device).  Every wait is also bounded by a watchdog (2 s): on expiry the
+ * status word gets MOE_FFN_DEV_TIMEOUT and the kernel still runs to its end,
+ * so a stream never hangs; read it with moe_ffn_read_status, or pass
+ * MOE_FFN_CHECK_STATUS.  Without the flag (and for other shapes) GEMM1 and
+ * GEMM2 are separate launches.  Both give bitwise identical outputs; the
+ * separate launches are the default because they are currently the faster of
+ * the two. */
 #define MOE_FFN_PIPELINE 0x2u
+/* fwd: after the launches, synchronise the stream and read the device status
+ * word: MOE_FFN_ERR_TIMEOUT if a pipelined wait hit its watchdog (y is then
+ * unreliable), MOE_FFN_ERR_EXPERT_ID if an expert id was out of range (its
+ * slot was dropped).  The call is then synchronous. */
+#define MOE_FFN_CHECK_STATUS 0x8u
 /* Test hook, never for production: the pipelined forward drops the release
  * of one GEMM1 tile and uses a 20 ms watchdog, so that the waits behind it
  * time out (status MOE_FFN_DEV_TIMEOUT) while every kernel still ends. */
@@ -103,6 +112,10 @@ typedef struct {
  * so that each workgroup walks many tiles (and, in the pipelined launch, waits
  * on many releases) at sizes a CPU reference checks in full. */
 #define MOE_FFN_TEST_SMALL_GRID 0x200u
+/* Test hook: the pipelined forward runs as ONE workgroup, which must then
+ * claim every tile of every XCD slice itself (its ticket draws move on to the
+ * other slices) and still end with the exact result. */
+#define MOE_FFN_TEST_ONE_WORKGROUP 0x400u
 /* bwd: read the saved context's header on the host first (synchronising the
  * stream) and return MOE_FFN_ERR_SAVED, before anything is launched, if it was
  * not written by a forward of this problem.  Without the flag the same check

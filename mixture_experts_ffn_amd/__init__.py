@@ -58,6 +58,8 @@ _lib = None
 F32, BF16, I32, I64 = 0, 1, 2, 3
 CHECK_IDS = 0x1
 PIPELINE = 0x2
+CHECK_STATUS = 0x8
+TEST_ONE_WORKGROUP = 0x400
 TEST_DROP_RELEASE = 0x100
 TEST_SMALL_GRID = 0x200
 CHECK_SAVED = 0x4

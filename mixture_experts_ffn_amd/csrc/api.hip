@@ -188,6 +188,9 @@ int min_tile_rows(const moe_ffn_problem &p)
     return a < b ? a : b;
 }
 
+// ticket counters of the pipelined launch, after its release counters
+constexpr int kTickets = 16;
+
 // Region offsets inside the forward workspace (and the saved context).
 struct FwdLayout {
     moe::FwdTiles tiles;
@@ -229,7 +232,7 @@ FwdLayout fwd_layout(const moe_ffn_problem &p, uint32_t flags = 0)
     // or a K step's past the end)
     L.sorted_slot = take(sizeof(int32_t) * ((size_t)TKp + 256));
     L.slot_pos = take(sizeof(int32_t) * (size_t)TK);
-    L.ctr = take(sizeof(int32_t) * 2 * (size_t)L.max_mtiles);
+    L.ctr = take(sizeof(int32_t) * (2 * (size_t)L.max_mtiles + kTickets));
     L.act = take(es * (size_t)TKp * (size_t)p.I);
     L.o = take(es * (size_t)TKp * (size_t)p.H);
     L.ws_total = off;
@@ -498,7 +501,7 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
     rb.mtile_expert = at<int32_t>(ws, L.mtile_expert);
     rb.status = at<int32_t>(ws, L.status);
     rb.ctr = at<int32_t>(ws, L.ctr);
-    rb.nctr = (int)(2 * L.max_mtiles);
+    rb.nctr = (int)(2 * L.max_mtiles + kTickets);
     rb.saved_hdr = saved ? at<moe::SavedHeader>(saved, L.s_hdr) : nullptr;
     rb.problem_hash = problem_hash(*p);
     rb.epoch = saved ? g_epoch.fetch_add(1) : 0;
@@ -604,6 +607,7 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
         a.mtile_off = rb.mtile_off;
         a.mtile_expert = rb.mtile_expert;
         a.ctr = rb.ctr;
+        a.tickets = rb.ctr + 2 * L.max_mtiles;
         a.status = rb.status;
         const int64_t watchdog_ms = (flags & MOE_FFN_TEST_DROP_RELEASE) ? 20 : 2000;
         a.timeout_ticks = watchdog_ms * (int64_t)clock_khz;
@@ -624,22 +628,27 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
         // the pipelined launch serves routed experts only; with a shared expert
         // the bulk launches run
         if ((flags & MOE_FFN_PIPELINE) && S == 0) {
+            // GEMM1 and GEMM2 in one launch; the combine follows as its own
+            // launch (no token block's combine could start before the last
+            // experts' GEMM2 tiles anyway)
+            if (flags & MOE_FFN_TEST_ONE_WORKGROUP)
+                a.grid = 1;
             record(ev, MOE_FFN_STAGE_PIPELINE, true, s);
             HIP_TRY(moe::launch_fast_fwd(moe::FAST_PIPE, BM, a, num_cus, s), "pipeline launch");
             record(ev, MOE_FFN_STAGE_PIPELINE, false, s);
-            return MOE_FFN_OK;
+        } else {
+            const int g1mode = a.hsave ? moe::FAST_G1H : moe::FAST_G1;
+            record(ev, MOE_FFN_STAGE_GEMM1, true, s);
+            HIP_TRY(L.tiles.big ? moe::launch_fast_fwd_big(g1mode, a, num_cus, s)
+                                : moe::launch_fast_fwd(g1mode, BM, a, num_cus, s),
+                    "gemm1 launch");
+            record(ev, MOE_FFN_STAGE_GEMM1, false, s);
+            record(ev, MOE_FFN_STAGE_GEMM2, true, s);
+            HIP_TRY(L.tiles.big ? moe::launch_fast_fwd_big(moe::FAST_G2, a, num_cus, s)
+                                : moe::launch_fast_fwd(moe::FAST_G2, BM, a, num_cus, s),
+                    "gemm2 launch");
+            record(ev, MOE_FFN_STAGE_GEMM2, false, s);
         }
-        const int g1mode = a.hsave ? moe::FAST_G1H : moe::FAST_G1;
-        record(ev, MOE_FFN_STAGE_GEMM1, true, s);
-        HIP_TRY(L.tiles.big ? moe::launch_fast_fwd_big(g1mode, a, num_cus, s)
-                            : moe::launch_fast_fwd(g1mode, BM, a, num_cus, s),
-                "gemm1 launch");
-        record(ev, MOE_FFN_STAGE_GEMM1, false, s);
-        record(ev, MOE_FFN_STAGE_GEMM2, true, s);
-        HIP_TRY(L.tiles.big ? moe::launch_fast_fwd_big(moe::FAST_G2, a, num_cus, s)
-                            : moe::launch_fast_fwd(moe::FAST_G2, BM, a, num_cus, s),
-                "gemm2 launch");
-        record(ev, MOE_FFN_STAGE_GEMM2, false, s);
     } else {
         // fp32: the generic kernels (gemm.hip)
         moe::GroupedGemmArgs g1{};
@@ -693,6 +702,17 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
                                 (int)p->H, (int)p->K, rb.offsets, E, S, s),
             "combine launch");
     record(ev, MOE_FFN_STAGE_COMBINE, false, s);
+    if (flags & MOE_FFN_CHECK_STATUS) {
+        int32_t st = 0;
+        HIP_TRY(hipMemcpyAsync(&st, rb.status, sizeof st, hipMemcpyDeviceToHost, s),
+                "status copy");
+        HIP_TRY(hipStreamSynchronize(s), "stream sync");
+        if (st & moe::MOE_DEV_TIMEOUT)
+            return fail(MOE_FFN_ERR_TIMEOUT, "a wait of the pipelined forward hit its watchdog; "
+                                             "y is unreliable");
+        if (st & moe::MOE_DEV_BAD_ID)
+            return fail(MOE_FFN_ERR_EXPERT_ID, "topk_ids holds a value outside [0, %d)", E);
+    }
     return MOE_FFN_OK;
 }
 
@@ -736,9 +756,9 @@ int moe_ffn_fwd_noalloc(const moe_ffn_problem *p, const void *x, const void *top
         return rc;
     if (p->Is != 0)
         return fail(MOE_FFN_ERR_SHAPE, "moe_ffn_fwd_noalloc: Is != 0 is not supported");
-    if (flags & MOE_FFN_CHECK_IDS)
-        return fail(MOE_FFN_ERR_SHAPE,
-                    "moe_ffn_fwd_noalloc: MOE_FFN_CHECK_IDS is not supported (it copies to the host)");
+    if (flags & (MOE_FFN_CHECK_IDS | MOE_FFN_CHECK_STATUS))
+        return fail(MOE_FFN_ERR_SHAPE, "moe_ffn_fwd_noalloc: MOE_FFN_CHECK_IDS and "
+                                       "MOE_FFN_CHECK_STATUS are not supported (they copy to the host)");
     const FwdLayout L = fwd_layout(*p, flags);
     if (L.ws_total > MOE_FFN_NOALLOC_WS_BYTES)
         return fail(MOE_FFN_ERR_WORKSPACE,

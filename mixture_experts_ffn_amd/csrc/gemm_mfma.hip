@@ -161,9 +161,11 @@ __device__ __forceinline__ void wait_counters(const int32_t *p, int need, const 
 
 // Position of a workgroup in one phase (the tiles of one grouped GEMM): each
 // XCD owns a contiguous eighth of the tile order; its workgroups take every
-// (gridDim.x / 8)-th tile of it.
+// (gridDim.x / 8)-th tile of it (separate launches), or claim its tiles from
+// the XCD's ticket counter (the pipelined launch; `tried` counts the XCD
+// slices this workgroup has found exhausted in the current phase).
 struct Cursor {
-    int kind, L, hi, step;
+    int kind, L, hi, step, tried;
 };
 
 template <int BM, int MODE, int NWAVES>
@@ -195,11 +197,9 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
         const int range = (total + 7) >> 3;
         c.kind = kind;
         // 64-row tiles stream weights (HBM-bound): as many workgroups as make
-        // every round of the XCD's range full, so no round runs half-empty.
-        // In the pipelined launch only for GEMM2: a workgroup left out goes
-        // on to the combine phase, whose waits other workgroups release.
+        // every round of the XCD's range full, so no round runs half-empty
         int wg = per_xcd_wg;
-        if (BM == 64 && (!PIPE || kind == KIND_G2)) {
+        if (BM == 64) {
             const int rounds = (range + per_xcd_wg - 1) / per_xcd_wg;
             wg = rounds > 0 ? (range + rounds - 1) / rounds : per_xcd_wg;
         }
@@ -208,12 +208,50 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
         c.hi = min((xcd + 1) * range, total);
         return slot < wg && c.L < c.hi;
     };
+    // The pipelined launch hands out its tiles by tickets, so that any tile a
+    // GEMM2 tile waits for has been claimed by a workgroup that is running:
+    // per-XCD counters over the same XCD slices (tiles in flight on one XCD
+    // still share panels in its L2); a workgroup whose slice is exhausted
+    // claims from the other XCDs' counters in turn, and GEMM2 tickets are only
+    // drawn once every GEMM1 slice is exhausted.  GEMM1 tiles wait for
+    // nothing, so every claimed tile completes whether or not the other
+    // workgroups of the launch are resident.  Wave 0 draws the ticket and
+    // passes it to the other waves through LDS.
+    __shared__ int tick_bcast[2];
+    int tick_par = 0;
+    auto claim = [&](Cursor &c) {
+        while (true) {
+            const int total = mtiles * (c.kind == KIND_G1 ? ntn1 : ntn2);
+            const int range = (total + 7) >> 3;
+            const int x = (xcd + c.tried) & 7;
+            const int lo = min(x * range, total), hi = min(lo + range, total);
+            if (wave == 0 && lane == 0)
+                tick_bcast[tick_par] =
+                    lo < hi ? __hip_atomic_fetch_add(args.tickets + (c.kind == KIND_G1 ? 0 : 8) + x,
+                                                     1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : 0x7fffffff;
+            __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): the ticket is in LDS
+            lds_barrier();
+            const int t = tick_bcast[tick_par];
+            tick_par ^= 1;
+            if (t < hi - lo) {
+                c.L = lo + t;
+                return true;
+            }
+            if (++c.tried < 8)
+                continue;
+            if (c.kind == KIND_G2)
+                return false;
+            c.kind = KIND_G2;
+            c.tried = 0;
+        }
+    };
     auto advance = [&](Cursor &c) {
+        if (PIPE)
+            return claim(c);
         c.L += c.step;
         if (c.L < c.hi)
             return true;
-        if (PIPE && c.kind == KIND_G1)
-            return phase_begin(KIND_G2, c);
         return false;
     };
     auto decode = [&](const Cursor &c) {
@@ -429,10 +467,10 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
             }
             __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): this wave's rows are in LDS
             lds_barrier();
-            if constexpr (PIPE) {
-                // rows other workgroups of this launch read: device-coherent
-                // stores, which are 8 bytes wide, so each lane takes an 8-byte
-                // piece and one store instruction covers whole rows
+            if (PIPE && g1) {
+                // act rows, which GEMM2 tiles of this launch read: device-
+                // coherent stores, which are 8 bytes wide, so each lane takes
+                // an 8-byte piece and one store instruction covers whole rows
                 const int cpr8 = 2 * cpr, rd8 = 2 * rd;
 #pragma unroll 1
                 for (int j = 0; j < rd8; ++j) {
@@ -464,11 +502,9 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
     // once its own stores of the tile are acknowledged, so a tile is complete
     // at NW bumps per N-tile; the test hook drops one wave's bump.
     auto release_index = [&](const Tile &t) {
-        if (!PIPE)
+        if (!PIPE || t.kind != KIND_G1)
             return -1;
-        if (t.kind == KIND_G1)
-            return (t.mt == args.drop_mt && t.nt == 0 && wave == 0) ? -1 : t.mt;
-        return args.max_mtiles + t.mt;
+        return (t.mt == args.drop_mt && t.nt == 0 && wave == 0) ? -1 : t.mt;
     };
     // a GEMM2 tile reads the act rows of its M-tile: every GEMM1 N-tile of it
     auto wait_ready = [&](const Tile &t) {
@@ -477,11 +513,17 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
         wait_counters(ctr1 + t.mt, NW * ntn1, args);
     };
     Cursor cc;
+    cc.tried = 0;
     bool have = false;
-    if (MODE != FAST_G2)
-        have = phase_begin(KIND_G1, cc);
-    if (!have && !G1ONLY)
-        have = phase_begin(KIND_G2, cc);
+    if (PIPE) {
+        cc.kind = KIND_G1;
+        have = claim(cc);
+    } else {
+        if (MODE != FAST_G2)
+            have = phase_begin(KIND_G1, cc);
+        if (!have && !G1ONLY)
+            have = phase_begin(KIND_G2, cc);
+    }
 
     if (have) {
         Tile cur = decode(cc);
@@ -614,77 +656,8 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
         }
     }
 
-    if constexpr (PIPE) {
-        // Combine (issue page, section 2.1 "Combine"): a unit is a block of BT
-        // tokens (its BT*K slots fit one wave) times 512 columns (one 16-byte
-        // chunk per lane).  It waits for the GEMM2 M-tiles holding its slots,
-        // then sums each token's K rows in k order in fp32 and rounds once (the
-        // arithmetic of the bulk combine kernel); the rows of a token are
-        // loaded 8 at a time so their latencies overlap.
-        const int K = args.K, T = args.T;
-        const int BT = 64 / K;
-        const int nch = H / 8; // 16-byte chunks per row
-        const int ntb = (T + BT - 1) / BT;
-        const int ncb = (nch + 63) / 64;
-        const int nunits = ntb * ncb;
-        const int TW = gridDim.x * NW;
-        bf16 *__restrict__ y = static_cast<bf16 *>(args.y);
-        const bf16 *o = static_cast<const bf16 *>(args.o);
-        for (int u = blockIdx.x * NW + wave; u < nunits; u += TW) {
-            const int tb = u / ncb, cb = u - (u / ncb) * ncb;
-            const int t0 = tb * BT;
-            const int t = t0 + lane / K;
-            const int32_t *dep = nullptr;
-            if (lane < BT * K && t < T) {
-                const int64_t s = (int64_t)t0 * K + lane;
-                const int p = args.slot_pos[s];
-                if (p >= 0) {
-                    const int e = args.ids64 ? (int)static_cast<const int64_t *>(args.ids)[s]
-                                             : static_cast<const int32_t *>(args.ids)[s];
-                    dep = ctr2 + args.mtile_off[e] + (p - args.offsets[e]) / BM;
-                }
-            }
-            wait_counters(dep, NW * ntn2, args);
-            const int c = cb * 64 + lane;
-            const bool live = c < nch;
-            const int64_t col = (int64_t)(live ? c : 0) * 8;
-            const int t1 = min(t0 + BT, T);
-            for (int tt = t0; tt < t1; ++tt) {
-                float accv[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    accv[j] = 0.f;
-                for (int k0 = 0; k0 < K; k0 += 8) {
-                    int pk[8];
-                    u32x4 v[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int k = min(k0 + j, K - 1);
-                        pk[j] = k0 + j < K ? ldc(args.slot_pos, tt * K + k) : -1;
-                        v[j] = load_coherent16(o + (int64_t)max(pk[j], 0) * H + col);
-                    }
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        if (pk[j] < 0)
-                            continue;
-                        const float g = ldcf(args.gates, tt * K + k0 + j);
-                        const bf16 *vv = reinterpret_cast<const bf16 *>(&v[j]);
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            accv[i] += g * static_cast<float>(vv[i]);
-                    }
-                }
-                if (live) {
-                    u32x4 out;
-                    bf16 *oo = reinterpret_cast<bf16 *>(&out);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        oo[i] = static_cast<bf16>(accv[i]);
-                    *reinterpret_cast<u32x4 *>(y + (int64_t)tt * H + col) = out;
-                }
-            }
-        }
-    }
+    if (PIPE)
+        wait_vm<0>(); // no copy into this workgroup's LDS outlives it
 }
 
 template <int BM, int MODE, int NWAVES = waves_for(BM)>

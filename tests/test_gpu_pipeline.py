@@ -1,14 +1,16 @@
 """The pipelined forward (tile-granular release) against its bulk twin and the oracle.
 
-The pipelined forward runs GEMM1, GEMM2 and the combine as one persistent
-launch in which device counters replace the launch boundaries (overlap
-explainer page, sections 5-6; HyperMegaMoE issue page, tile-level
-pipelining).  It performs exactly the arithmetic of the bulk forward (the same
-tiles, the same accumulation order, the same combine), so its outputs must be
-bitwise equal to the bulk twin's, and within the bf16 tolerance of the oracle.
-The watchdog is exercised from the host: a test flag drops one release and
-shortens the watchdog, every wait behind it must time out and report it, and
-every kernel still ends.
+The pipelined forward runs GEMM1 and GEMM2 as one persistent launch in which
+device counters replace the launch boundary (overlap explainer page, sections
+5-6; HyperMegaMoE issue page, tile-level pipelining), then the combine.  It
+performs exactly the arithmetic of the bulk forward (the same tiles, the same
+accumulation order, the same combine), so its outputs must be bitwise equal to
+the bulk twin's, and within the bf16 tolerance of the oracle.  Its tiles are
+handed out by tickets, so a single workgroup must also complete it (a test
+flag launches one).  The watchdog is exercised from the host: a test flag
+drops one release and shortens the watchdog, every wait behind it must time
+out and report it (through the status word, and as an error with
+MOE_FFN_CHECK_STATUS), and every kernel still ends.
 """
 
 import numpy as np
@@ -113,6 +115,20 @@ def test_out_of_range_ids_dropped_like_bulk(gpu_lib):
     assert torch.equal(y_p, y_b)
 
 
+@pytest.mark.parametrize("case", CASES[:3], ids=[c[0] for c in CASES[:3]])
+def test_one_workgroup_completes_the_pipelined_launch(gpu_lib, case):
+    name, T, H, I, E, K, routing = case
+    w = Workload(name, 400 + CASES.index(case), T=T, H=H, I=I, E=E, K=K, routing=routing,
+                 n_empty=3 if routing == "zipf" else 0)
+    d = to_device(make_inputs(w))
+    say(f"[pipe] one workgroup case={name}")
+    y_1, ws = fwd(gpu_lib, d, return_ws=True, flags=gpu_lib.TEST_ONE_WORKGROUP)
+    y_b = fwd(gpu_lib, d, pipelined=False)
+    torch.cuda.synchronize()
+    assert gpu_lib.read_status(ws) == 0
+    assert torch.equal(y_1, y_b)
+
+
 def test_watchdog_reports_a_dropped_release(gpu_lib):
     w = Workload("drop", 424, T=256, H=256, I=256, E=4, K=2)
     d = to_device(make_inputs(w))
@@ -120,6 +136,10 @@ def test_watchdog_reports_a_dropped_release(gpu_lib):
     _, ws = fwd(gpu_lib, d, return_ws=True, flags=gpu_lib.TEST_DROP_RELEASE)
     torch.cuda.synchronize()
     assert gpu_lib.read_status(ws) & gpu_lib.DEV_TIMEOUT
+    # with MOE_FFN_CHECK_STATUS the call itself fails with MOE_FFN_ERR_TIMEOUT
+    with pytest.raises(gpu_lib.MoEFFNError) as ei:
+        fwd(gpu_lib, d, flags=gpu_lib.TEST_DROP_RELEASE | gpu_lib.CHECK_STATUS)
+    assert ei.value.status == 10
     # the next call on the same workspace starts clean and is exact again
     y = fwd(gpu_lib, d, ws=ws)
     y_b = fwd(gpu_lib, d, pipelined=False)
