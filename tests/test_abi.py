@@ -49,6 +49,27 @@ def test_workspace_query_rejects_bad_problems(bad, code):
     assert ei.value.status == code
 
 
+@pytest.mark.parametrize("shape,plan", [
+    # (T, H, I, E, K): decode, prefill, skewed shapes; rows per expert 32, 384, 2048
+    ((128, 7168, 2048, 32, 8), (64, "tiles")),
+    ((4096, 2048, 1408, 64, 6), (128, "tiles")),
+    ((8192, 7168, 2048, 32, 8), (256, "big_tiles")),
+    # ragged H: the engine
+    ((600, 264, 256, 8, 2), (128, "engine")),
+])
+def test_forward_plan_picks_the_tile_height_from_rows_per_expert(shape, plan):
+    T, H, I, E, K = shape
+    p = prob(T=T, H=H, I=I, E=E, K=K)
+    assert m.fwd_plan(p) == plan
+    # the pipelined launch keeps the tile height of the two-launch forward for
+    # 64 and 128-row tiles and never takes the 256 x 256 kernel
+    rows, fam = m.fwd_plan(p, m.PIPELINE)
+    if plan[1] == "tiles":
+        assert (rows, fam) == (plan[0], "pipelined")
+    elif plan[1] == "big_tiles":
+        assert fam == "pipelined" and rows in (128, 256)
+
+
 def test_workspace_size_grows_with_tokens():
     small, saved_small = m.fwd_workspace_size(prob(T=64))
     big, saved_big = m.fwd_workspace_size(prob(T=4096))
