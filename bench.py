@@ -4,22 +4,25 @@
 One step = one full forward of the layer (route -> gathered up_proj GEMM with
 SwiGLU -> down_proj GEMM -> combine) on a seeded synthetic batch that is
 already resident in HBM; for the forward+backward workload also the backward.
-The forward runs as the library does by default (route, GEMM1, GEMM2 and
-combine as separate launches).  The step is timed eagerly (with per-stage HIP
-events) and as a HIP graph replay of the same calls (every kernel runs every
-step; only the host-side launch work is gone); the headline is the replay when
-its output equals the eager output bit for bit.  The pipelined twin (the two
-grouped GEMMs in one launch with tile-granular release, then the combine) is
-timed after it and reported as "pipelined_twin".  Prints ONE JSON line.
+The forward runs as the library does by default: route, the two grouped
+GEMMs and the combine as separate launches, or on 64-row tiles (the
+weight-streaming decode shape) route, the two GEMMs as one pipelined launch
+with tile-granular release, and the combine.  The step is timed eagerly (with
+per-stage HIP events) and as a HIP graph replay of the same calls (every
+kernel runs every step; only the host-side launch work is gone); the headline
+is the replay when its output equals the eager output bit for bit.  The other
+mode (pipelined or two launches) is timed eagerly after it and reported as
+"twin".  Prints ONE JSON line.
 
 Default workload: prefill, bf16 with fp32 accumulation, T=4096 tokens,
 H=2048, I=1408, E=64 experts, K=6, uniform routing.  Other workloads:
 --workload {tiny_f32,prefill_bf16,skewed_bf16,decode_bf16,fwdbwd_bf16}.
 
 Besides tokens/s the line carries
-* "roofline": the dominant kernel (the up_proj GEMM with its SwiGLU epilogue;
-  against HBM bandwidth for the HBM-bound decode shape), its algorithmic work per launch divided by its average
-  launch time, where the launch times come from HIP events that the library
+* "roofline": the dominant kernel (the up_proj GEMM with its SwiGLU epilogue,
+  or the pipelined launch where it is the default; against HBM bandwidth for
+  the HBM-bound decode shape), its algorithmic work per launch divided by its
+  average launch time, where the launch times come from HIP events that the library
   records around that kernel on the call's stream during the timed steps;
 * "stage_roofline": each bulk forward stage (GEMM1, GEMM2, combine) against
   both bounds, from its algorithmic bytes and flops per launch;
@@ -91,7 +94,7 @@ def main():
         dec = measure("decode_bf16", args, primary=False)
         out["decode"] = {k: dec[k] for k in ("value", "unit", "ms_per_step", "config", "layer",
                                               "launch", "eager", "graph_replay",
-                                              "pipelined_twin", "roofline", "stage_roofline",
+                                              "twin", "roofline", "stage_roofline",
                                               "cpu_baseline", "hbm_reference")
                          if k in dec}
     print(json.dumps(out), flush=True)
@@ -127,7 +130,7 @@ def measure(workload_name, args, primary):
 
     sh = ({"shared_up_proj_weight": d["shared_up"], "shared_down_proj_weight": d["shared_down"]}
           if w.Is else {})
-    def step(ev=None, bev=None, pipelined=False):
+    def step(ev=None, bev=None, pipelined=None):
         if not w.backward:
             return m.moe_ffn_fwd(d["x"], d["topk_ids"], d["topk_weights"], d["up_proj"],
                                  d["down_proj"], ws=ws, stage_events=ev, pipelined=pipelined,
@@ -202,8 +205,9 @@ def measure(workload_name, args, primary):
     torch.cuda.synchronize()
     first_call_ms = fa.elapsed_time(fb)
 
-    # the library's default forward (the bulk launches) is the measured one; the
-    # pipelined twin (one launch, tile-granular release) runs after it
+    # the library's default forward is the measured one (for this workload the
+    # one pipelined launch or the two GEMM launches, whichever it picks); the
+    # other mode, its twin, is timed after it
     def graphed():
         """The default step captured once into a HIP graph and replayed: the same
         kernels every step, without per-launch host work.  Returns the replayed
@@ -226,8 +230,10 @@ def measure(workload_name, args, primary):
         torch.cuda.synchronize()
         return yg, time.perf_counter() - t0
 
-    y, elapsed, stage_ms, step_stats = timed(pipelined=False)
-    _, pipe_elapsed, pipe_stage_ms, _ = timed(pipelined=True)
+    default_pipelined = m.fwd_plan(prob)[1] == "pipelined"
+    y, elapsed, stage_ms, step_stats = timed(pipelined=None)
+    twin_pipelined = not default_pipelined
+    _, twin_elapsed, twin_stage_ms, _ = timed(pipelined=twin_pipelined)
     cold_stats = cold(args.cold_steps) if args.cold_steps > 0 else None
     y_graph, graph_elapsed = graphed()
     graph_ok = bool(torch.equal(y_graph, y))
@@ -249,17 +255,25 @@ def measure(workload_name, args, primary):
     g1_bytes = nl * w.H * 2 * es + w.T * w.H * es + TKp * w.I * es
     g2_bytes = nl * w.H * es + TKp * w.I * es + TKp * w.H * es
     cb_bytes = TKp * w.H * es + w.T * w.H * es + w.T * w.K * 8
-    # dominant kernel: the gathered up_proj GEMM with the SwiGLU epilogue
-    # (one launch covers the routed experts and the shared expert's chunks)
-    k_flops = 4.0 * w.T * w.H * (w.K * w.I + w.Is)
-    k_bytes = ((live.sum() * w.I + w.Is) * w.H * 2 * es + w.T * w.H * es
-               + w.T * (w.K * w.I + w.Is) * es)
-    k_ms = stage_ms["gemm1"]
-    kernel = {"tiles": f"moe::fast::moe_fwd_bf16<{tile_rows}, FAST_G1> "
-                       "(gathered up_proj GEMM + SwiGLU)",
-              "big_tiles": "moe::big::moe_fwd_bf16_big<FAST_G1> "
-                           "(gathered up_proj GEMM + SwiGLU, 256 x 256 tiles)",
-              }.get(kernel_family, f"up_proj GEMM + SwiGLU ({kernel_family} kernel)")
+    if "pipeline" in stage_ms:
+        # dominant kernel: the pipelined launch (both grouped GEMMs; the
+        # combine is a launch of its own)
+        k_flops = w.fwd_flops()
+        k_bytes = g1_bytes + g2_bytes
+        k_ms = stage_ms["pipeline"]
+        kernel = (f"moe::fast::moe_fwd_bf16<{tile_rows}, FAST_PIPE> "
+                  "(GEMM1+SwiGLU, GEMM2 in one launch)")
+    else:
+        # dominant kernel: the gathered up_proj GEMM with the SwiGLU epilogue
+        # (one launch covers the routed experts and the shared expert's chunks)
+        k_flops = 4.0 * w.T * w.H * (w.K * w.I + w.Is)
+        k_bytes = g1_bytes
+        k_ms = stage_ms["gemm1"]
+        kernel = {"tiles": f"moe::fast::moe_fwd_bf16<{tile_rows}, FAST_G1> "
+                           "(gathered up_proj GEMM + SwiGLU)",
+                  "big_tiles": "moe::big::moe_fwd_bf16_big<FAST_G1> "
+                               "(gathered up_proj GEMM + SwiGLU, 256 x 256 tiles)",
+                  }.get(kernel_family, f"up_proj GEMM + SwiGLU ({kernel_family} kernel)")
     if w.name.startswith("decode"):
         roof = {"bound": "hbm", "achieved": k_bytes / (k_ms * 1e-3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
@@ -268,7 +282,7 @@ def measure(workload_name, args, primary):
         roof = {"bound": "mfma", "achieved": k_flops / (k_ms * 1e-3) / 1e12, "peak": peak,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(w.name, "gemm1",
+    roof["traffic"] = measured_traffic(w.name, "pipeline" if "pipeline" in stage_ms else "gemm1",
                                        "gemm_big.hip" if kernel_family == "big_tiles"
                                        else "gemm_mfma.hip")
     roof["kernel"] = kernel
@@ -276,10 +290,12 @@ def measure(workload_name, args, primary):
     # every stage of the bulk forward against its own bound: algorithmic bytes
     # (weights of live experts, activations in and out) or flops per launch
     stage_roof = {}
-    if "gemm2" in stage_ms:
-        for name, nbytes, nflops in (("gemm1", g1_bytes, k_flops),
-                                     ("gemm2", g2_bytes, k_flops / 2),
-                                     ("combine", cb_bytes, 0.0)):
+    g1_flops = 4.0 * w.T * w.H * (w.K * w.I + w.Is)
+    for name, nbytes, nflops in (("gemm1", g1_bytes, g1_flops),
+                                 ("gemm2", g2_bytes, g1_flops / 2),
+                                 ("pipeline", g1_bytes + g2_bytes, 1.5 * g1_flops),
+                                 ("combine", cb_bytes, 0.0)):
+        if name in stage_ms:
             t = stage_ms[name] * 1e-3
             stage_roof[name] = {"ms": stage_ms[name], "hbm_gbs": nbytes / t / 1e9,
                                 "hbm_frac": nbytes / t / 1e9 / PEAK_HBM_GBS,
@@ -315,11 +331,11 @@ def measure(workload_name, args, primary):
         "graph_replay": {"ms_per_step": graph_elapsed / args.steps * 1e3,
                          "tokens_per_s": w.T * args.steps / graph_elapsed,
                          "output_equals_eager": graph_ok},
-        "pipelined_twin": {"kernel": f"moe::fast::moe_fwd_bf16<{m.fwd_plan(prob, m.PIPELINE)[0]}, "
-                                     "FAST_PIPE> (GEMM1+SwiGLU, GEMM2 in one launch)",
-                           "ms_per_step": pipe_elapsed / args.steps * 1e3,
-                           "tokens_per_s": w.T * args.steps / pipe_elapsed,
-                           "stage_ms": pipe_stage_ms},
+        "twin": {"mode": "pipelined" if twin_pipelined else "bulk",
+                 "plan": m.fwd_plan(prob, m.PIPELINE if twin_pipelined else m.BULK),
+                 "ms_per_step": twin_elapsed / args.steps * 1e3,
+                 "tokens_per_s": w.T * args.steps / twin_elapsed,
+                 "stage_ms": twin_stage_ms},
         "roofline": roof,
         "stage_roofline": stage_roof,
         "cpu_baseline": None,

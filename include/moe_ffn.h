@@ -94,11 +94,17 @@ typedef struct {
  * device).  Every wait is also bounded by a watchdog (2 s): on expiry the
  * status word gets MOE_FFN_DEV_TIMEOUT and the kernel still runs to its end,
  * so a stream never hangs; read it with moe_ffn_read_status, or pass
- * MOE_FFN_CHECK_STATUS.  Without the flag (and for other shapes) GEMM1 and
- * GEMM2 are separate launches.  Both give bitwise identical outputs; the
- * separate launches are the default because they are currently the faster of
- * the two. */
+ * MOE_FFN_CHECK_STATUS.  Otherwise (and for other shapes, or with a shared
+ * expert) GEMM1 and GEMM2 are separate launches.  Both give bitwise identical
+ * outputs.  Without MOE_FFN_PIPELINE or MOE_FFN_BULK the library chooses: the
+ * pipelined launch for problems on 64-row tiles (at most 64 routed rows per
+ * expert on average, where streaming the weights from HBM bounds both GEMMs
+ * and the one launch measured faster), the separate launches otherwise. */
 #define MOE_FFN_PIPELINE 0x2u
+/* fwd: always run GEMM1 and GEMM2 as separate launches (the bulk twin of the
+ * pipelined forward).  MOE_FFN_PIPELINE and MOE_FFN_BULK together are
+ * rejected with MOE_FFN_ERR_SHAPE. */
+#define MOE_FFN_BULK 0x10u
 /* fwd: after the launches, synchronise the stream and read the device status
  * word: MOE_FFN_ERR_TIMEOUT if a pipelined wait hit its watchdog (y is then
  * unreliable), MOE_FFN_ERR_EXPERT_ID if an expert id was out of range (its

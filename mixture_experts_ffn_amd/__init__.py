@@ -58,6 +58,7 @@ _lib = None
 F32, BF16, I32, I64 = 0, 1, 2, 3
 CHECK_IDS = 0x1
 PIPELINE = 0x2
+BULK = 0x10
 CHECK_STATUS = 0x8
 TEST_ONE_WORKGROUP = 0x400
 TEST_DROP_RELEASE = 0x100
@@ -260,18 +261,27 @@ def _shared_problem(prob, x, shared_up_proj_weight, shared_down_proj_weight):
     return SharedWeights(shared_up_proj_weight.data_ptr(), shared_down_proj_weight.data_ptr())
 
 
+def _mode_flag(pipelined):
+    """MOE_FFN_PIPELINE for True, MOE_FFN_BULK for False, nothing for None."""
+    if pipelined is None:
+        return 0
+    return PIPELINE if pipelined else BULK
+
+
 def moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *,
                 save_for_backward: bool = False, check_ids: bool = False, ws=None,
                 stage_events: StageEvents | None = None, return_ws: bool = False,
-                pipelined: bool = False, flags: int = 0, shared_up_proj_weight=None,
+                pipelined: bool | None = None, flags: int = 0, shared_up_proj_weight=None,
                 shared_down_proj_weight=None):
     """y [T, H] of the MoE expert-FFN layer (see include/moe_ffn.h).
 
     With ``save_for_backward`` also returns the saved context (a uint8 device
     tensor) that the backward consumes.  ``ws`` may pass a preallocated
     workspace (uint8 tensor of at least ``fwd_workspace_size`` bytes).
-    ``pipelined`` selects the one-launch forward with tile-granular release
-    (bf16, H % 256 == 0, I % 128 == 0; other shapes ignore it);
+    ``pipelined`` True asks for the one-launch forward with tile-granular
+    release (bf16, H % 256 == 0, I % 128 == 0; other shapes ignore it), False
+    for the two separate GEMM launches, None (the default) leaves the choice
+    to the library;
     ``flags`` passes further MOE_FFN_* bits through.  ``shared_up_proj_weight``
     [H, 2Is] and ``shared_down_proj_weight`` [Is, H] (Is a multiple of I) add the
     shared expert's SwiGLU FFN to y; the saved context then covers it too.
@@ -290,7 +300,7 @@ def moe_ffn_fwd(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, *,
     elif ws.numel() < ws_bytes:
         raise MoEFFNError(5, f"workspace has {ws.numel()} bytes, {ws_bytes} needed")
     saved = torch.empty(saved_bytes, dtype=torch.uint8, device=dev) if save_for_backward else None
-    flags |= (CHECK_IDS if check_ids else 0) | (PIPELINE if pipelined else 0)
+    flags |= (CHECK_IDS if check_ids else 0) | _mode_flag(pipelined)
     ev = ctypes.byref(stage_events) if stage_events is not None else None
     with torch.cuda.device(dev):
         if sw is not None:
@@ -336,7 +346,7 @@ def fwd_stages(x, topk_ids, up_proj_weight, down_proj_weight, ws, flags: int = 0
 
 
 def moe_ffn_fwd_noalloc(x, topk_ids, topk_weights, up_proj_weight, down_proj_weight, y, *,
-                        pipelined: bool = False, flags: int = 0):
+                        pipelined: bool | None = None, flags: int = 0):
     """The inference forward into the caller's ``y`` [T, H] with no workspace:
     the library's own per-GPU scratch (include/moe_ffn.h, moe_ffn_fwd_noalloc)
     serves as the workspace, so nothing is allocated.  Raises MoEFFNError for
@@ -348,7 +358,7 @@ def moe_ffn_fwd_noalloc(x, topk_ids, topk_weights, up_proj_weight, down_proj_wei
     if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
         raise MoEFFNError(2, "y must be a contiguous tensor with the shape and dtype of x")
     prob = make_problem(x, topk_ids, up_proj_weight, down_proj_weight)
-    flags |= PIPELINE if pipelined else 0
+    flags |= _mode_flag(pipelined)
     dev = x.device
     with torch.cuda.device(dev):
         rc = lib.moe_ffn_fwd_noalloc(ctypes.byref(prob), _ptr(x), _ptr(topk_ids),

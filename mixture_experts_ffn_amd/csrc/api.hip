@@ -180,6 +180,18 @@ moe::FwdTiles pick_tiles(const moe_ffn_problem &p, uint32_t flags)
     return t;
 }
 
+// Whether a forward of this problem runs GEMM1 and GEMM2 as the one pipelined
+// launch: on request, and by default for problems on 64-row tiles (HBM-bound
+// weight streaming, where it measured faster than the two launches); never
+// with a shared expert or off the bf16 tile path.
+bool use_pipeline(const moe_ffn_problem &p, uint32_t flags)
+{
+    if (p.Is != 0 || p.dtype != MOE_FFN_BF16 || !moe::fast_gemm_supported(p.dtype, p.H, p.I) ||
+        (flags & MOE_FFN_BULK))
+        return false;
+    return (flags & MOE_FFN_PIPELINE) || pick_tiles(p, 0).BM == 64;
+}
+
 // the smallest tile height any call mode of this problem may use (sizes the
 // M-tile tables of the workspace, which serves every mode)
 int min_tile_rows(const moe_ffn_problem &p)
@@ -450,7 +462,7 @@ int moe_ffn_fwd_stages(const moe_ffn_problem *p, uint32_t flags, moe_ffn_fwd_sta
     const bool fast = moe::fast_gemm_supported(p->dtype, p->H, p->I);
     layout->kernel = p->dtype == MOE_FFN_F32 ? MOE_FFN_KERNEL_GENERIC
                      : !fast                 ? MOE_FFN_KERNEL_ENGINE
-                     : ((flags & MOE_FFN_PIPELINE) && p->Is == 0) ? MOE_FFN_KERNEL_PIPELINED
+                     : use_pipeline(*p, flags) ? MOE_FFN_KERNEL_PIPELINED
                      : L.tiles.big           ? MOE_FFN_KERNEL_BIG_TILES
                                              : MOE_FFN_KERNEL_TILES;
     return MOE_FFN_OK;
@@ -467,6 +479,8 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
     int rc = validate_problem(p);
     if (rc)
         return rc;
+    if ((flags & MOE_FFN_PIPELINE) && (flags & MOE_FFN_BULK))
+        return fail(MOE_FFN_ERR_SHAPE, "flags: MOE_FFN_PIPELINE and MOE_FFN_BULK exclude each other");
     const int S = nshared(*p);
     if (S > 0 && !sh)
         return fail(MOE_FFN_ERR_NULL, "a problem with Is > 0 needs the shared-expert weights");
@@ -627,7 +641,7 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
         const int BM = L.tiles.BM;
         // the pipelined launch serves routed experts only; with a shared expert
         // the bulk launches run
-        if ((flags & MOE_FFN_PIPELINE) && S == 0) {
+        if (use_pipeline(*p, flags)) {
             // GEMM1 and GEMM2 in one launch; the combine follows as its own
             // launch (no token block's combine could start before the last
             // experts' GEMM2 tiles anyway)

@@ -51,7 +51,7 @@ def test_workspace_query_rejects_bad_problems(bad, code):
 
 @pytest.mark.parametrize("shape,plan", [
     # (T, H, I, E, K): decode, prefill, skewed shapes; rows per expert 32, 384, 2048
-    ((128, 7168, 2048, 32, 8), (64, "tiles")),
+    ((128, 7168, 2048, 32, 8), (64, "pipelined")),
     ((4096, 2048, 1408, 64, 6), (128, "tiles")),
     ((8192, 7168, 2048, 32, 8), (256, "big_tiles")),
     # ragged H: the engine
@@ -62,12 +62,16 @@ def test_forward_plan_picks_the_tile_height_from_rows_per_expert(shape, plan):
     p = prob(T=T, H=H, I=I, E=E, K=K)
     assert m.fwd_plan(p) == plan
     # the pipelined launch keeps the tile height of the two-launch forward for
-    # 64 and 128-row tiles and never takes the 256 x 256 kernel
+    # 64 and 128-row tiles and never takes the 256 x 256 kernel; the library
+    # picks it by default on 64-row tiles only
     rows, fam = m.fwd_plan(p, m.PIPELINE)
-    if plan[1] == "tiles":
+    bulk = m.fwd_plan(p, m.BULK)
+    if plan[1] in ("tiles", "pipelined"):
         assert (rows, fam) == (plan[0], "pipelined")
+        assert bulk == (plan[0], "tiles")
     elif plan[1] == "big_tiles":
         assert fam == "pipelined" and rows in (128, 256)
+        assert bulk == plan
 
 
 def test_workspace_size_grows_with_tokens():
@@ -81,10 +85,15 @@ def test_workspace_size_grows_with_tokens():
 
 
 def _fwd(lib, p, x=FAKE, ids=FAKE, g=FAKE, w1=FAKE, w2=FAKE, y=FAKE, saved=None, ws=FAKE,
-         ws_bytes=1 << 40):
+         ws_bytes=1 << 40, flags=0):
     vp = lambda a: None if a is None else ctypes.c_void_p(a)
     return lib.moe_ffn_fwd(ctypes.byref(p), vp(x), vp(ids), vp(g), vp(w1), vp(w2), vp(y),
-                           vp(saved), vp(ws), ws_bytes, 0, None)
+                           vp(saved), vp(ws), ws_bytes, flags, None)
+
+
+def test_fwd_rejects_pipeline_and_bulk_together(lib):
+    assert _fwd(lib, prob(), flags=m.PIPELINE | m.BULK) == 2
+    assert b"exclude" in lib.moe_ffn_last_error()
 
 
 def test_fwd_rejects_null_and_misaligned_pointers_before_launch(lib):
