@@ -269,9 +269,10 @@ def measure(workload_name, args, primary):
         k_flops = 4.0 * w.T * w.H * (w.K * w.I + w.Is)
         k_bytes = g1_bytes
         k_ms = stage_ms["gemm1"]
-        kernel = {"tiles": f"moe::fast::moe_fwd_bf16<{tile_rows}, FAST_G1> "
+        mode = "FAST_G1H" if w.backward else "FAST_G1"  # the training forward also saves h
+        kernel = {"tiles": f"moe::fast::moe_fwd_bf16<{tile_rows}, {mode}> "
                            "(gathered up_proj GEMM + SwiGLU)",
-                  "big_tiles": "moe::big::moe_fwd_bf16_big<FAST_G1> "
+                  "big_tiles": f"moe::big::moe_fwd_bf16_big<{mode}> "
                                "(gathered up_proj GEMM + SwiGLU, 256 x 256 tiles)",
                   }.get(kernel_family, f"up_proj GEMM + SwiGLU ({kernel_family} kernel)")
     if w.name.startswith("decode"):

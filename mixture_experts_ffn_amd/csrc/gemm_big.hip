@@ -37,9 +37,10 @@
 //    major, groups of M-tiles with N outer), its workgroups strided through
 //    it, so tiles in flight on one XCD share weight panels and token rows in
 //    its L2; a tile's last steps already copy the next tile's first steps.
-// A wave whose 128 rows end early multiplies only the 16-row blocks that hold
-// rows (rounded up to an even count; none for the second row half of a tile
-// of 128 rows or fewer).
+// A tile's rows are split between the two wave rows in 32-row steps (a tile
+// of r rows gives the first ceil(r / 64) * 32 of them to wave row 0 and the
+// rest to wave row 1), and each wave multiplies only the 16-row blocks that
+// hold rows (rounded up to an even count).
 #include "common.h"
 #include "kernels.h"
 #include "tile_common.h"
