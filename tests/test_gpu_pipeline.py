@@ -71,6 +71,26 @@ def test_pipelined_equals_bulk_and_oracle(gpu_lib, case):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("case", [("default_bm64", 300, 256, 256, 16, 2),
+                                  ("default_bm128", 600, 512, 384, 8, 3)],
+                         ids=["bm64", "bm128"])
+def test_default_mode_equals_both_forced_modes(gpu_lib, case):
+    # the library's own choice (the pipelined launch on 64-row tiles, the two
+    # launches otherwise) gives the same bits as either mode forced
+    name, T, H, I, E, K = case
+    w = Workload(name, 440 + T, T=T, H=H, I=I, E=E, K=K)
+    d = to_device(make_inputs(w))
+    prob = gpu_lib.make_problem(d["x"], d["topk_ids"], d["up_proj"], d["down_proj"])
+    rows, family = gpu_lib.fwd_plan(prob)
+    assert family == ("pipelined" if rows == 64 else "tiles")
+    say(f"[pipe] default vs forced modes case={name} plan=({rows}, {family})")
+    y_d = fwd(gpu_lib, d, pipelined=None)
+    y_p = fwd(gpu_lib, d, pipelined=True)
+    y_b = fwd(gpu_lib, d, pipelined=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y_d, y_p) and torch.equal(y_d, y_b)
+
+
 def test_workspace_reuse_sees_fresh_data(gpu_lib):
     # two different batches through one workspace: the second call's consumers
     # must read the second call's tiles, never lines left from the first
