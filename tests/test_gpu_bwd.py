@@ -25,6 +25,8 @@ SMALL = [
     ("bwd_dups", 129, 128, 64, 4, 3, "replace"),
     ("bwd_one_token", 1, 256, 128, 8, 2, "uniform"),
     ("bwd_wide_k", 150, 384, 136, 5, 5, "uniform"),
+    # 8 rows per expert: the saving forward runs the pipelined launch by default
+    ("bwd_decode_like", 64, 512, 256, 32, 4, "uniform"),
 ]
 NAMES = ("dx", "d_up", "d_down", "d_topk")
 

@@ -27,6 +27,8 @@ SMALL = [
     ("bf16_ragged", 333, 264, 200, 6, 2, "bf16", "uniform"),
     ("bf16_tiles", 700, 512, 384, 8, 3, "bf16", "uniform"),
     ("bf16_bm64", 40, 512, 256, 16, 4, "bf16", "uniform"),
+    # 1024 experts, 4 slots each on average: many empty, the pipelined default
+    ("bf16_many_experts", 512, 256, 128, 1024, 8, "bf16", "uniform"),
     ("bf16_zipf_empty", 515, 256, 128, 16, 4, "bf16", "zipf"),
     ("bf16_dups", 129, 128, 64, 4, 3, "bf16", "replace"),
     ("bf16_one_token", 1, 256, 128, 8, 2, "bf16", "uniform"),
