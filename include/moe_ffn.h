@@ -42,6 +42,12 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden symbol visibility on the host side; the
+ * declarations below are its exported interface. */
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility push(default)
+#endif
+
 /* Element types. x, both weights, y, dy, dx and the weight gradients share
  * one floating-point dtype; topk_weights and d_topk_weights are fp32. */
 typedef enum {
@@ -395,6 +401,10 @@ int moe_ffn_event_elapsed_ms(void *begin, void *end, float *ms);
 
 /* Library version, "major.minor.patch". */
 const char *moe_ffn_version(void);
+
+#if defined(__GNUC__) || defined(__clang__)
+#pragma GCC visibility pop
+#endif
 
 #ifdef __cplusplus
 }

@@ -244,7 +244,7 @@ FwdLayout fwd_layout(const moe_ffn_problem &p, uint32_t flags = 0)
     // or a K step's past the end)
     L.sorted_slot = take(sizeof(int32_t) * ((size_t)TKp + 256));
     L.slot_pos = take(sizeof(int32_t) * (size_t)TK);
-    L.ctr = take(sizeof(int32_t) * (2 * (size_t)L.max_mtiles + kTickets));
+    L.ctr = take(sizeof(int32_t) * ((size_t)L.max_mtiles + kTickets));
     L.act = take(es * (size_t)TKp * (size_t)p.I);
     L.o = take(es * (size_t)TKp * (size_t)p.H);
     L.ws_total = off;
@@ -515,7 +515,7 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
     rb.mtile_expert = at<int32_t>(ws, L.mtile_expert);
     rb.status = at<int32_t>(ws, L.status);
     rb.ctr = at<int32_t>(ws, L.ctr);
-    rb.nctr = (int)(2 * L.max_mtiles + kTickets);
+    rb.nctr = (int)(L.max_mtiles + kTickets);
     rb.saved_hdr = saved ? at<moe::SavedHeader>(saved, L.s_hdr) : nullptr;
     rb.problem_hash = problem_hash(*p);
     rb.epoch = saved ? g_epoch.fetch_add(1) : 0;
@@ -621,7 +621,7 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
         a.mtile_off = rb.mtile_off;
         a.mtile_expert = rb.mtile_expert;
         a.ctr = rb.ctr;
-        a.tickets = rb.ctr + 2 * L.max_mtiles;
+        a.tickets = rb.ctr + L.max_mtiles;
         a.status = rb.status;
         const int64_t watchdog_ms = (flags & MOE_FFN_TEST_DROP_RELEASE) ? 20 : 2000;
         a.timeout_ticks = watchdog_ms * (int64_t)clock_khz;

@@ -186,8 +186,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = uni(tid >> 6);
     const int wm = wave / C::WN, wn = wave % C::WN; // this wave's block of the tile
-    int32_t *const ctr1 = args.ctr;                   // GEMM1 N-tiles done per M-tile
-    int32_t *const ctr2 = args.ctr + args.max_mtiles; // GEMM2 N-tiles done per M-tile
+    int32_t *const ctr1 = args.ctr; // GEMM1 N-tiles done per M-tile
 
     auto kind_of = [&](int k) {
         return G1ONLY ? (int)KIND_G1 : MODE == FAST_G2 ? (int)KIND_G2 : k;

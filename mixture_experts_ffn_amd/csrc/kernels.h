@@ -135,7 +135,7 @@ struct FastFwdArgs {
     const int32_t *offsets;      // [E + 1]
     const int32_t *mtile_off;    // [E + 1]
     const int32_t *mtile_expert; // [max_mtiles]
-    int32_t *ctr;                // pipelined: [2 * max_mtiles] zeroed counters
+    int32_t *ctr;                // pipelined: [max_mtiles] zeroed GEMM1 release counters
     int32_t *tickets;            // pipelined: [16] zeroed ticket counters (8 per GEMM, one per XCD)
     int grid;                    // workgroups of the launch (0: the persistent default)
     int32_t *status;             // device status word (MOE_DEV_* bits)
