@@ -19,8 +19,10 @@ namespace moe {
 
 // Grid: (token, block of 256 16-byte chunks).  Each thread owns one chunk of
 // one token's output row; its K source rows are loaded 8 at a time before
-// they are accumulated in k order, so their latencies overlap.
-template <typename T>
+// they are accumulated in k order, so their latencies overlap.  NT: the rows
+// are read with the non-temporal hint (o larger than the last-level cache,
+// where the GEMM that wrote it leaves no useful copy behind).
+template <typename T, bool NT>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ o,
                                                       const int32_t *__restrict__ slot_pos,
                                                       const float *__restrict__ gates,
@@ -45,7 +47,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ o,
         for (int i = 0; i < 8; ++i) {
             pk[i] = k0 + i < K ? slot_pos[t * K + k0 + i] : -1;
             const int64_t row = pk[i] > 0 ? pk[i] : 0;
-            v[i] = *reinterpret_cast<const u32x4 *>(o + row * H + (int64_t)c * VEC);
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(o + row * H + (int64_t)c * VEC);
+            v[i] = NT ? __builtin_nontemporal_load(src) : *src;
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -200,14 +203,21 @@ hipError_t launch_combine(int dtype, const void *o, const int32_t *slot_pos, con
         return hipSuccess;
     const int vec = dtype == 1 ? 8 : 4;
     const unsigned cblocks = (unsigned)((H / vec + 255) / 256);
-    if (dtype == 1)
-        hipLaunchKernelGGL(combine_kernel<bf16>, dim3((unsigned)T, cblocks), dim3(256), 0, stream,
-                           static_cast<const bf16 *>(o), slot_pos, gates, static_cast<bf16 *>(y), H,
-                           K, offsets, Er, S, T);
-    else
-        hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)T, cblocks), dim3(256), 0, stream,
-                           static_cast<const float *>(o), slot_pos, gates, static_cast<float *>(y),
-                           H, K, offsets, Er, S, T);
+    const dim3 grid((unsigned)T, cblocks);
+    // o of more than 192 MB does not stay in the 256 MB last-level cache
+    // behind the GEMM that wrote it: stream it (skewed shape, 939 MB: the
+    // combine 216 -> 184 us); smaller o is re-read from that cache, where
+    // the hint made it slower (134 MB: 31 -> 37 us)
+    const bool nt = T * (K + S) * (int64_t)H * (dtype == 1 ? 2 : 4) > ((int64_t)192 << 20);
+    if (dtype == 1) {
+        auto k = nt ? combine_kernel<bf16, true> : combine_kernel<bf16, false>;
+        hipLaunchKernelGGL(k, grid, dim3(256), 0, stream, static_cast<const bf16 *>(o), slot_pos,
+                           gates, static_cast<bf16 *>(y), H, K, offsets, Er, S, T);
+    } else {
+        auto k = nt ? combine_kernel<float, true> : combine_kernel<float, false>;
+        hipLaunchKernelGGL(k, grid, dim3(256), 0, stream, static_cast<const float *>(o), slot_pos,
+                           gates, static_cast<float *>(y), H, K, offsets, Er, S, T);
+    }
     return hipGetLastError();
 }
 

@@ -81,6 +81,18 @@ __device__ __forceinline__ void g2l16s(const void *base, uint32_t voff, lds_void
                  : "memory", "m0");
 }
 
+// The same copy with the non-temporal hint: for weight panels a launch
+// streams from HBM once, so that they do not displace the token rows the
+// tiles of the same expert re-read from L2.
+__device__ __forceinline__ void g2l16_nt(const void *g, lds_void *l)
+{
+    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)l);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 :
+                 : "s"(lds_addr), "v"(g)
+                 : "memory", "m0");
+}
+
 // The same copy as a device-coherent load (sc1: served at the device's
 // coherence point, never from a stale cache line), for data that another
 // workgroup of the same launch wrote with device-coherent stores.
