@@ -359,29 +359,54 @@ __global__ __launch_bounds__(1024) void route_block_kernel(
             bef[e] = 0;
         }
     } else {
-        // wave w reads the rows of experts w, w + 16, ...; the loads of one
-        // row segment are issued together, the sums are wave reductions
-        for (int e = wave; e < E; e += 16) {
-            const int32_t *row = hist + (int64_t)e * NB;
-            int32_t t = 0, bs = 0;
-            for (int j0 = 0; j0 < NB; j0 += 64) {
-                const int j = j0 + lane;
-                const int32_t v = j < NB ? row[j] : 0;
-                t += v;
-                bs += j < b0 ? v : 0;
-                if (j >= b0 && j < b0 + 16)
-                    tab[e * 16 + (j - b0)] = v;
-            }
-            if (lane < 16 && b0 + lane >= NB)
-                tab[e * 16 + lane] = 0;
+        // wave w reads the rows of experts w, w + 16, ...; RB rows x JB
+        // 64-chunk segments of them are loaded before any is summed, so that
+        // one memory round trip serves them (E = 64 and up to 256 chunks: all
+        // of a wave's loads at once); the sums are wave reductions
+        constexpr int RB = 4, JB = 4;
+        for (int e0 = wave; e0 < E; e0 += 16 * RB) {
+            int32_t t[RB], bs[RB];
 #pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) {
-                t += __shfl_xor(t, d, 64);
-                bs += __shfl_xor(bs, d, 64);
+            for (int r = 0; r < RB; ++r)
+                t[r] = bs[r] = 0;
+            for (int j0 = 0; j0 < NB; j0 += 64 * JB) {
+                int32_t v[RB][JB];
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
+#pragma unroll
+                    for (int q = 0; q < JB; ++q) {
+                        const int e = e0 + 16 * r, j = j0 + 64 * q + lane;
+                        v[r][q] = e < E && j < NB ? hist[(int64_t)e * NB + j] : 0;
+                    }
+#pragma unroll
+                for (int r = 0; r < RB; ++r) {
+                    const int e = e0 + 16 * r;
+#pragma unroll
+                    for (int q = 0; q < JB; ++q) {
+                        const int j = j0 + 64 * q + lane;
+                        t[r] += v[r][q];
+                        bs[r] += j < b0 ? v[r][q] : 0;
+                        if (e < E && j >= b0 && j < b0 + 16)
+                            tab[e * 16 + (j - b0)] = v[r][q];
+                    }
+                }
             }
-            if (lane == 0) {
-                tot[e] = t;
-                bef[e] = bs;
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const int e = e0 + 16 * r;
+                if (e >= E)
+                    break;
+                if (lane < 16 && b0 + lane >= NB)
+                    tab[e * 16 + lane] = 0;
+#pragma unroll
+                for (int d = 32; d >= 1; d >>= 1) {
+                    t[r] += __shfl_xor(t[r], d, 64);
+                    bs[r] += __shfl_xor(bs[r], d, 64);
+                }
+                if (lane == 0) {
+                    tot[e] = t[r];
+                    bef[e] = bs[r];
+                }
             }
         }
         if (lead)
