@@ -78,8 +78,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not supported "
-              "(--gpus must be 1)", file=sys.stderr)
+        print("bench.py: the layer is measured on exactly one GPU (one GPU's share of the "
+              "experts); multi-GPU runs are not supported (--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch  # noqa: F401
