@@ -22,10 +22,13 @@
 //            bits, so the rank inside the round is a popcount and the order
 //            stays stable.
 // Launches: one 1024-thread block does all three when the slots fit 16
-// chunks (decode-sized batches); otherwise a hist launch, then 1024-thread
-// blocks of 16 chunks that each redo the (small) scan for themselves and
-// scatter.  With more than 910 experts the per-block table would not fit
-// 64 KB of LDS, and hist, scan and scatter run as three launches.
+// chunks (decode-sized batches); up to 32768 slots, 1024-thread blocks of 16
+// chunks that each count all the ids themselves, scan and scatter their own
+// chunks; beyond that a hist launch first, whose table the blocks read
+// instead of counting (also from 863 experts on, where the self-counting
+// table of 19 x E words would not fit 64 KB of LDS).  With more than 910
+// experts the per-block table would not fit either, and hist, scan and
+// scatter run as three launches.
 #include "common.h"
 #include "kernels.h"
 
@@ -121,6 +124,23 @@ __device__ inline int32_t block_excl_scan(int32_t v, int32_t *s_w, int32_t *tota
     return s_w[16 + wave] + incl - v;
 }
 
+// Exclusive scan of one value per expert, held by threads 0 .. n-1 of a
+// 1024-thread block (the others hold 0).  With n <= 64 the values all sit in
+// wave 0, which scans them with shuffles and no barrier: only wave 0's
+// results (and *total) are defined then.  Otherwise the block scan, whose
+// results every thread has.
+__device__ inline int32_t expert_excl_scan(int32_t v, int n, int32_t *s_w, int32_t *total)
+{
+    if (n <= 64) {
+        if (threadIdx.x >= 64)
+            return 0;
+        const int32_t incl = wave_incl_scan(v);
+        *total = __shfl(incl, 63, 64);
+        return incl - v;
+    }
+    return block_excl_scan(v, s_w, total);
+}
+
 // Start-of-forward bookkeeping done by the first routing block: the saved
 // context's header and the zeroed release counters of the pipelined forward.
 __device__ inline void write_header_and_counters(SavedHeader *hdr, uint64_t problem_hash,
@@ -150,14 +170,16 @@ __device__ inline void publish_plan(int32_t c, int32_t off, int32_t total, bool 
                                     int32_t *__restrict__ status, int32_t *s_w, int32_t *s_moff,
                                     int nsh, int64_t T, int K, int32_t *__restrict__ sorted_slot)
 {
+    // off and total come from expert_excl_scan: with E <= 64 only wave 0
+    // holds them, and wave 0 does all the per-expert work here
     const int e = threadIdx.x;
     if (e < E) {
         counts[e] = c;
         offsets[e] = off;
     }
     const int32_t mt = (c + BM - 1) / BM;
-    int32_t mtotal;
-    const int32_t moff = block_excl_scan(mt, s_w, &mtotal);
+    int32_t mtotal = 0;
+    const int32_t moff = expert_excl_scan(mt, E, s_w, &mtotal);
     if (e < E) {
         mtile_off[e] = moff;
         s_moff[e] = moff;
@@ -166,9 +188,13 @@ __device__ inline void publish_plan(int32_t c, int32_t off, int32_t total, bool 
         offsets[E] = total;
         mtile_off[E] = mtotal;
         s_moff[E] = mtotal;
+        s_w[36] = total;
+        s_w[37] = mtotal;
         status[0] = anybad ? MOE_DEV_BAD_ID : 0;
     }
     __syncthreads();
+    total = s_w[36];
+    mtotal = s_w[37];
     // owner expert of every M-tile: the last e with s_moff[e] <= j
     for (int j = threadIdx.x; j < mtotal; j += 1024) {
         int lo = 0, hi = E;
@@ -299,16 +325,24 @@ __global__ __launch_bounds__(64) void route_scatter_kernel(
 
 // Fused routing: a 1024-thread block owns the 16 consecutive chunks
 // 16 b .. 16 b + 15, wave w the chunk 16 b + w.
-//  ONE = true  (NB <= 16, one block): each wave first counts its chunk per
-//              expert into the block's table, so routing is one launch.
-//  ONE = false: the table comes from route_hist_kernel; every block reads
-//              each expert's row of it (all loads issued at once) for the
-//              total and the sum over chunks before its own, which replaces
-//              the separate scan launch.
+//  ROUTE_ONE  (NB <= 16, one block): each wave first counts its chunk per
+//             expert into the block's table, so routing is one launch.
+//  ROUTE_SELF (up to kSelfCountSlots slots): every block counts ALL the ids
+//             itself, per expert before its chunks, per (expert, chunk) in
+//             them and after them, so routing is one launch and no block
+//             waits on another's counts (the redundant reads are L2 hits).
+//  ROUTE_HIST: the table comes from route_hist_kernel; every block reads
+//             each expert's row of it (all loads issued at once) for the
+//             total and the sum over chunks before its own, which replaces
+//             the separate scan launch.
 // Every block then scans the totals into offsets and turns its table into
 // per-(expert, chunk) bases; block 0 also publishes counts, offsets, the
-// M-tile tables and the status word.  LDS: tab[E][16], tot[E], bef[E].
-template <typename Id, bool ONE>
+// M-tile tables and the status word.  LDS: tab[E][16], tot[E], bef[E] (and
+// aft[E] in ROUTE_SELF).
+enum { ROUTE_ONE = 0, ROUTE_SELF = 1, ROUTE_HIST = 2 };
+constexpr int64_t kSelfCountSlots = 32768;
+
+template <typename Id, int MODE>
 __global__ __launch_bounds__(1024) void route_block_kernel(
     const Id *__restrict__ ids, int64_t TK, int E, int nbits, int RC, int NB, int BM,
     const int32_t *__restrict__ hist, const int32_t *__restrict__ bad,
@@ -329,7 +363,48 @@ __global__ __launch_bounds__(1024) void route_block_kernel(
     if (lead)
         write_header_and_counters(hdr, problem_hash, epoch, ctr, nctr);
     int anybad = 0;
-    if constexpr (ONE) {
+    if constexpr (MODE == ROUTE_SELF) {
+        int32_t *aft = bef + E; // [E]: slots of expert e after this block's chunks
+        for (int i = threadIdx.x; i < E * 16; i += 1024)
+            tab[i] = 0;
+        for (int i = threadIdx.x; i < E; i += 1024)
+            bef[i] = aft[i] = 0;
+        __syncthreads();
+        const int64_t lo = (int64_t)b0 * RC;
+        const int64_t hi = lo + 16 * (int64_t)RC < TK ? lo + 16 * (int64_t)RC : TK;
+        // thread t counts slots t, t + 1024, ...; 8 loads in flight per round
+        for (int64_t s0 = threadIdx.x; s0 < TK; s0 += 8 * 1024) {
+            Id raw[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t sl = s0 + 1024 * j;
+                raw[j] = ids[sl < TK ? sl : TK - 1];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t sl = s0 + 1024 * j;
+                const int64_t e = (int64_t)raw[j];
+                if (sl >= TK)
+                    continue;
+                if (e < 0 || e >= E)
+                    anybad = 1;
+                else if (sl < lo)
+                    atomicAdd(&bef[e], 1);
+                else if (sl < hi)
+                    atomicAdd(&tab[e * 16 + (int)((sl - lo) / RC)], 1);
+                else
+                    atomicAdd(&aft[e], 1);
+            }
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += 1024) {
+            int32_t t = bef[e] + aft[e];
+#pragma unroll
+            for (int w = 0; w < 16; ++w)
+                t += tab[e * 16 + w];
+            tot[e] = t;
+        }
+    } else if constexpr (MODE == ROUTE_ONE) {
         for (int i = threadIdx.x; i < E * 16; i += 1024)
             tab[i] = 0;
         __syncthreads();
@@ -417,8 +492,10 @@ __global__ __launch_bounds__(1024) void route_block_kernel(
 
     const int e = threadIdx.x; // E + nsh <= 1024
     const int32_t c = e < E ? tot[e] : e < E + nsh ? (int32_t)T : 0;
-    int32_t total;
-    const int32_t off = block_excl_scan(c, s_w, &total);
+    int32_t total = 0;
+    // with E + nsh <= 64 only wave 0 gets off and total; it is also the only
+    // wave that uses them (publish_plan's per-expert work, the bases below)
+    const int32_t off = expert_excl_scan(c, E + nsh, s_w, &total);
     if (lead)
         publish_plan(c, off, total, anybad, E + nsh, BM, counts, offsets, mtile_off,
                      mtile_expert, status, s_w, s_moff, nsh, T, K, sorted_slot);
@@ -625,25 +702,25 @@ static void launch_route_t(const Id *ids, int64_t TK, int E, int BM, const Route
 {
     const size_t lds = sizeof(int32_t) * (size_t)E;
     const size_t lds_block = sizeof(int32_t) * (size_t)E * 18; // tab[E][16], tot[E], bef[E]
+    const size_t lds_self = lds_block + sizeof(int32_t) * (size_t)E; // and aft[E]
     const int K = rb.T > 0 ? (int)(TK / rb.T) : 1;
     const int nctr = rb.ctr ? rb.nctr : 0;
     if (TK > 0 && lds_block <= 65536) {
-        if (rp.NB > 16)
+        const int nblk = (rp.NB + 15) / 16;
+        const int mode = nblk == 1 ? ROUTE_ONE
+                         : TK <= kSelfCountSlots && lds_self <= 65536 ? ROUTE_SELF
+                                                                     : ROUTE_HIST;
+        if (mode == ROUTE_HIST)
             hipLaunchKernelGGL(route_hist_kernel<Id>, dim3(rp.NB), dim3(64), lds, stream, ids, TK, E,
                                rp.RC, rp.NB, rb.hist, rb.bad);
-        const int nblk = (rp.NB + 15) / 16;
-        if (nblk == 1)
-            hipLaunchKernelGGL((route_block_kernel<Id, true>), dim3(1), dim3(1024), lds_block, stream,
-                               ids, TK, E, rp.nbits, rp.RC, rp.NB, BM, rb.hist, rb.bad, rb.counts,
-                               rb.offsets, rb.mtile_off, rb.mtile_expert, rb.status, rb.ctr, nctr,
-                               rb.saved_hdr, rb.problem_hash, rb.epoch, rb.nshared, rb.T, K,
-                               rb.sorted_slot, rb.slot_pos);
-        else
-            hipLaunchKernelGGL((route_block_kernel<Id, false>), dim3(nblk), dim3(1024), lds_block,
-                               stream, ids, TK, E, rp.nbits, rp.RC, rp.NB, BM, rb.hist, rb.bad,
-                               rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert, rb.status,
-                               rb.ctr, nctr, rb.saved_hdr, rb.problem_hash, rb.epoch,
-                               rb.nshared, rb.T, K, rb.sorted_slot, rb.slot_pos);
+        auto kern = mode == ROUTE_ONE    ? route_block_kernel<Id, ROUTE_ONE>
+                    : mode == ROUTE_SELF ? route_block_kernel<Id, ROUTE_SELF>
+                                         : route_block_kernel<Id, ROUTE_HIST>;
+        hipLaunchKernelGGL(kern, dim3(nblk), dim3(1024), mode == ROUTE_SELF ? lds_self : lds_block,
+                           stream, ids, TK, E, rp.nbits, rp.RC, rp.NB, BM, rb.hist, rb.bad,
+                           rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert, rb.status, rb.ctr,
+                           nctr, rb.saved_hdr, rb.problem_hash, rb.epoch, rb.nshared, rb.T, K,
+                           rb.sorted_slot, rb.slot_pos);
         return;
     }
     // many experts (the block table would not fit), or no slots: hist, scan, scatter
@@ -661,8 +738,9 @@ static void launch_route_t(const Id *ids, int64_t TK, int E, int BM, const Route
                            rb.slot_pos);
 }
 
-// One launch when the slots fit 16 chunks, two (hist, block) otherwise, three
-// (hist, scan, scatter) when an expert table of 18 x E words would not fit 64 KB.
+// One launch up to 32768 slots (16 chunks: one block; more: self-counting
+// blocks), two (hist, block) beyond, three (hist, scan, scatter) when an
+// expert table of 18 x E words would not fit 64 KB.
 hipError_t launch_route(const void *ids, bool ids64, int64_t TK, int E, int BM,
                         const RoutePlan &rp, const RouteBufs &rb, hipStream_t stream)
 {
