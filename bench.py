@@ -270,8 +270,10 @@ def measure(workload_name, args, primary):
         k_bytes = g1_bytes
         k_ms = stage_ms["gemm1"]
         mode = "FAST_G1H" if w.backward else "FAST_G1"  # the training forward also saves h
-        kernel = {"tiles": f"moe::fast::moe_fwd_bf16<{tile_rows}, {mode}> "
-                           "(gathered up_proj GEMM + SwiGLU)",
+        g1_tiles = (f"moe::fast::moe_fwd_bf16<{tile_rows}, {mode}> "
+                    "(gathered up_proj GEMM + SwiGLU)")
+        kernel = {"tiles": g1_tiles,
+                  "tiles_big_gemm2": g1_tiles,
                   "big_tiles": f"moe::big::moe_fwd_bf16_big<{mode}> "
                                "(gathered up_proj GEMM + SwiGLU, 256 x 256 tiles)",
                   }.get(kernel_family, f"up_proj GEMM + SwiGLU ({kernel_family} kernel)")

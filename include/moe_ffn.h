@@ -209,7 +209,9 @@ int moe_ffn_fwd(const moe_ffn_problem *p, const void *x, const void *topk_ids,
  * layer. */
 typedef struct {
     size_t counts, offsets, sorted_slot, slot_pos, act, o;
-    int32_t tile_rows; /* rows per M-tile of the grouped GEMMs */
+    int32_t tile_rows; /* rows per M-tile of GEMM1 (and of GEMM2, but for
+                          MOE_FFN_KERNEL_TILES_BIG_GEMM2, whose GEMM2 tiles
+                          have 256 rows) */
     int32_t kernel;    /* their kernel: MOE_FFN_KERNEL_* */
 } moe_ffn_fwd_stage_layout;
 #define MOE_FFN_KERNEL_GENERIC 0   /* fp32 */
@@ -217,6 +219,7 @@ typedef struct {
 #define MOE_FFN_KERNEL_TILES 2     /* bf16 tile kernel: 64 or 128-row tiles */
 #define MOE_FFN_KERNEL_BIG_TILES 3 /* bf16 256 x 256 tile kernel */
 #define MOE_FFN_KERNEL_PIPELINED 4 /* bf16 one-launch forward (MOE_FFN_PIPELINE) */
+#define MOE_FFN_KERNEL_TILES_BIG_GEMM2 5 /* bf16: GEMM1 on 128-row tiles, GEMM2 on 256 x 256 */
 int moe_ffn_fwd_stages(const moe_ffn_problem *p, uint32_t flags, moe_ffn_fwd_stage_layout *layout);
 
 /* moe_ffn_fwd with the per-stage timing hook (ev may be NULL). */

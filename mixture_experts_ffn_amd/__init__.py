@@ -101,7 +101,8 @@ class FwdStageLayout(ctypes.Structure):
                [("tile_rows", ctypes.c_int32), ("kernel", ctypes.c_int32)]
 
 
-KERNELS = {0: "generic", 1: "engine", 2: "tiles", 3: "big_tiles", 4: "pipelined"}
+KERNELS = {0: "generic", 1: "engine", 2: "tiles", 3: "big_tiles", 4: "pipelined",
+           5: "tiles_big_gemm2"}
 
 
 def fwd_plan(problem: Problem, flags: int = 0):

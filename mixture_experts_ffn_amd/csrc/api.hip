@@ -159,6 +159,7 @@ moe::FwdTiles pick_tiles(const moe_ffn_problem &p, uint32_t flags)
     moe::FwdTiles t;
     t.num_cus = 0;
     t.big = false;
+    t.big2 = false;
     if (p.dtype == MOE_FFN_F32) {
         t.BM = 64;
         return t;
@@ -176,6 +177,12 @@ moe::FwdTiles pick_tiles(const moe_ffn_problem &p, uint32_t flags)
         t.big = true;
     } else {
         t.BM = (avg_rows <= 1024.0 || !fast) ? 128 : 256;
+        // from 256 rows per expert on, GEMM2 alone runs on 256 x 256 tiles:
+        // measured on 384 rows per expert (H = 2048, I = 1408, E = 64) it is
+        // 9 % faster there than on 128-row tiles in spite of a third of padded
+        // rows, while GEMM1 is 15 % slower (the 11 N-tiles of I = 1408 leave
+        // the last of six rounds of tiles half empty)
+        t.big2 = fast && !pipe && offsets32 && t.BM == 128 && avg_rows > 256.0;
     }
     return t;
 }
@@ -208,8 +215,10 @@ struct FwdLayout {
     moe::FwdTiles tiles;
     moe::RoutePlan rp;
     int64_t max_mtiles;
+    int64_t max_mtiles2; // M-tiles of 256 rows (GEMM2 on the 256 x 256 kernel), or 0
     // ws
     size_t status, hist, bad, counts, offsets, mtile_off, mtile_expert, sorted_slot, slot_pos;
+    size_t mtile2_off, mtile2_expert;
     size_t ctr, act, o, ws_total;
     // saved
     size_t s_hdr, s_counts, s_offsets, s_sorted, s_slotpos, s_h, saved_total;
@@ -226,6 +235,9 @@ FwdLayout fwd_layout(const moe_ffn_problem &p, uint32_t flags = 0)
     L.tiles = pick_tiles(p, flags);
     L.rp = moe::make_route_plan(TK, E);
     L.max_mtiles = moe::max_mtiles_bound(TKp, Ep, min_tile_rows(p));
+    // the 256-row tables exist whenever the bulk forward of this problem runs
+    // its GEMM2 on 256 x 256 tiles, whatever the flags (one size serves all)
+    L.max_mtiles2 = pick_tiles(p, 0).big2 ? moe::max_mtiles_bound(TKp, Ep, 256) : 0;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -239,6 +251,8 @@ FwdLayout fwd_layout(const moe_ffn_problem &p, uint32_t flags = 0)
     L.offsets = take(sizeof(int32_t) * (size_t)(Ep + 1));
     L.mtile_off = take(sizeof(int32_t) * (size_t)(Ep + 1));
     L.mtile_expert = take(sizeof(int32_t) * (size_t)L.max_mtiles);
+    L.mtile2_off = take(L.max_mtiles2 ? sizeof(int32_t) * (size_t)(Ep + 1) : 0);
+    L.mtile2_expert = take(sizeof(int32_t) * (size_t)L.max_mtiles2);
     // sorted_slot (here and in the saved context) has 256 entries of padding:
     // the GEMMs read their gather indices in whole blocks (up to a tile's rows
     // or a K step's past the end)
@@ -464,6 +478,7 @@ int moe_ffn_fwd_stages(const moe_ffn_problem *p, uint32_t flags, moe_ffn_fwd_sta
                      : !fast                 ? MOE_FFN_KERNEL_ENGINE
                      : use_pipeline(*p, flags) ? MOE_FFN_KERNEL_PIPELINED
                      : L.tiles.big           ? MOE_FFN_KERNEL_BIG_TILES
+                     : L.tiles.big2          ? MOE_FFN_KERNEL_TILES_BIG_GEMM2
                                              : MOE_FFN_KERNEL_TILES;
     return MOE_FFN_OK;
 }
@@ -516,6 +531,14 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
     rb.status = at<int32_t>(ws, L.status);
     rb.ctr = at<int32_t>(ws, L.ctr);
     rb.nctr = (int)(L.max_mtiles + kTickets);
+    // GEMM2 on 256 x 256 tiles (not in the pipelined launch, which runs both
+    // GEMMs on GEMM1's tiles): routing also builds the 256-row M-tile tables
+    const bool big2 = L.tiles.big2 && !use_pipeline(*p, flags);
+    if (big2) {
+        rb.mtile2_off = at<int32_t>(ws, L.mtile2_off);
+        rb.mtile2_expert = at<int32_t>(ws, L.mtile2_expert);
+        rb.BM2 = 256;
+    }
     rb.saved_hdr = saved ? at<moe::SavedHeader>(saved, L.s_hdr) : nullptr;
     rb.problem_hash = problem_hash(*p);
     rb.epoch = saved ? g_epoch.fetch_add(1) : 0;
@@ -657,9 +680,15 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
                                 : moe::launch_fast_fwd(g1mode, BM, a, num_cus, s),
                     "gemm1 launch");
             record(ev, MOE_FFN_STAGE_GEMM1, false, s);
+            moe::FastFwdArgs a2 = a;
+            if (big2) {
+                a2.mtile_off = rb.mtile2_off;
+                a2.mtile_expert = rb.mtile2_expert;
+                a2.max_mtiles = (int)L.max_mtiles2;
+            }
             record(ev, MOE_FFN_STAGE_GEMM2, true, s);
-            HIP_TRY(L.tiles.big ? moe::launch_fast_fwd_big(moe::FAST_G2, a, num_cus, s)
-                                : moe::launch_fast_fwd(moe::FAST_G2, BM, a, num_cus, s),
+            HIP_TRY(L.tiles.big || big2 ? moe::launch_fast_fwd_big(moe::FAST_G2, a2, num_cus, s)
+                                        : moe::launch_fast_fwd(moe::FAST_G2, BM, a, num_cus, s),
                     "gemm2 launch");
             record(ev, MOE_FFN_STAGE_GEMM2, false, s);
         }

@@ -52,6 +52,11 @@ struct RouteBufs {
     int32_t *offsets;     // [E + 1]
     int32_t *mtile_off;   // [E + 1]
     int32_t *mtile_expert; // [max_mtiles]: expert owning each M-tile
+    // optional second pair of M-tile tables for tiles of BM2 rows (a GEMM2 on
+    // another tile height than GEMM1); BM2 = 0: none
+    int32_t *mtile2_off = nullptr;    // [E + 1]
+    int32_t *mtile2_expert = nullptr; // [max M-tiles of BM2 rows]
+    int BM2 = 0;
     int32_t *status;      // [1]
     int32_t *sorted_slot; // [TK]
     int32_t *slot_pos;    // [TK]
@@ -110,6 +115,7 @@ struct GroupedGemmArgs {
 struct FwdTiles {
     int BM;       // 64, 128 or 256
     bool big;     // bf16 fast path: the 256 x 256 tile kernel (BM = 256)
+    bool big2;    // bf16 fast path, BM = 128: GEMM2 alone on the 256 x 256 kernel
     int num_cus;  // compute units of the device (persistent grids)
 };
 

@@ -9,7 +9,9 @@
 // Output: counts[E], offsets[E+1], sorted_slot[p] = s (expert-major, stable in
 // slot index s = t·K + k), slot_pos[s] = p (-1 for an out-of-range id) and
 // mtile_off[E+1], the prefix sum of ceil(counts[e] / BM) M-tiles that the
-// grouped GEMMs walk, with mtile_expert[j], the expert owning M-tile j.
+// grouped GEMMs walk, with mtile_expert[j], the expert owning M-tile j (and,
+// when a GEMM2 runs on taller tiles than GEMM1, the same pair of tables for
+// those tiles).
 //
 // No global atomics and no memset.  The slots are cut into chunks of RC
 // (512) and one wave routes one chunk; the work is
@@ -33,6 +35,13 @@
 #include "kernels.h"
 
 namespace moe {
+
+// the optional second pair of M-tile tables, for tiles of BM rows (BM = 0: none)
+struct MTileTable2 {
+    int32_t *off;    // [E + 1]
+    int32_t *expert; // [sum_e ceil(counts[e] / BM)]
+    int BM;
+};
 
 // Ids of up to 8 rounds of 64 slots from r0 < s1 on (lane's slots
 // r0 + 64 j + lane below s1; -1 past it).  The loads are unconditional (a
@@ -156,46 +165,11 @@ __device__ inline void write_header_and_counters(SavedHeader *hdr, uint64_t prob
         ctr[j] = 0;
 }
 
-// counts, offsets, the M-tile tables and the status word, from expert e's
-// count c and exclusive offset off held by thread e (all 1024 threads of one
-// block call this; E counts the nsh shared-expert chunks, whose counts are T,
-// and total = offsets[E]).  The rows of the shared chunks follow the routed
-// ones: row offsets[E - nsh] + cT + t gets sorted_slot t·K, so the gather of a
-// GEMM (slot / K) reads token t.
-__device__ inline void publish_plan(int32_t c, int32_t off, int32_t total, bool anybad, int E,
-                                    int BM, int32_t *__restrict__ counts,
-                                    int32_t *__restrict__ offsets,
-                                    int32_t *__restrict__ mtile_off,
-                                    int32_t *__restrict__ mtile_expert,
-                                    int32_t *__restrict__ status, int32_t *s_w, int32_t *s_moff,
-                                    int nsh, int64_t T, int K, int32_t *__restrict__ sorted_slot)
+// The owner expert of M-tile j is the last e with s_moff[e] <= j (s_moff holds
+// the exclusive prefix of the experts' M-tiles and the total at [E]).
+__device__ inline void fill_mtile_owners(const int32_t *s_moff, int E, int32_t mtotal,
+                                         int32_t *__restrict__ mtile_expert)
 {
-    // off and total come from expert_excl_scan: with E <= 64 only wave 0
-    // holds them, and wave 0 does all the per-expert work here
-    const int e = threadIdx.x;
-    if (e < E) {
-        counts[e] = c;
-        offsets[e] = off;
-    }
-    const int32_t mt = (c + BM - 1) / BM;
-    int32_t mtotal = 0;
-    const int32_t moff = expert_excl_scan(mt, E, s_w, &mtotal);
-    if (e < E) {
-        mtile_off[e] = moff;
-        s_moff[e] = moff;
-    }
-    if (e == 0) {
-        offsets[E] = total;
-        mtile_off[E] = mtotal;
-        s_moff[E] = mtotal;
-        s_w[36] = total;
-        s_w[37] = mtotal;
-        status[0] = anybad ? MOE_DEV_BAD_ID : 0;
-    }
-    __syncthreads();
-    total = s_w[36];
-    mtotal = s_w[37];
-    // owner expert of every M-tile: the last e with s_moff[e] <= j
     for (int j = threadIdx.x; j < mtotal; j += 1024) {
         int lo = 0, hi = E;
         while (hi - lo > 1) {
@@ -207,6 +181,65 @@ __device__ inline void publish_plan(int32_t c, int32_t off, int32_t total, bool 
         }
         mtile_expert[j] = lo;
     }
+}
+
+// counts, offsets, the M-tile tables and the status word, from expert e's
+// count c and exclusive offset off held by thread e (all 1024 threads of one
+// block call this; E counts the nsh shared-expert chunks, whose counts are T,
+// and total = offsets[E]).  The rows of the shared chunks follow the routed
+// ones: row offsets[E - nsh] + cT + t gets sorted_slot t·K, so the gather of a
+// GEMM (slot / K) reads token t.
+__device__ inline void publish_plan(int32_t c, int32_t off, int32_t total, bool anybad, int E,
+                                    int BM, int32_t *__restrict__ counts,
+                                    int32_t *__restrict__ offsets,
+                                    int32_t *__restrict__ mtile_off,
+                                    int32_t *__restrict__ mtile_expert, MTileTable2 t2,
+                                    int32_t *__restrict__ status, int32_t *s_w, int32_t *s_moff,
+                                    int nsh, int64_t T, int K, int32_t *__restrict__ sorted_slot)
+{
+    // off and total come from expert_excl_scan: with E <= 64 only wave 0
+    // holds them, and wave 0 does all the per-expert work here.  s_moff holds
+    // two prefix arrays of E + 1 entries: the M-tiles of BM rows, then those
+    // of t2.BM rows.
+    const int e = threadIdx.x;
+    if (e < E) {
+        counts[e] = c;
+        offsets[e] = off;
+    }
+    int32_t *s_moff2 = s_moff + 1025;
+    const int32_t mt = (c + BM - 1) / BM;
+    int32_t mtotal = 0, mtotal2 = 0;
+    const int32_t moff = expert_excl_scan(mt, E, s_w, &mtotal);
+    // (t2.BM is uniform: either every thread scans or none)
+    const int32_t moff2 =
+        t2.BM > 0 ? expert_excl_scan((c + t2.BM - 1) / t2.BM, E, s_w, &mtotal2) : 0;
+    if (e < E) {
+        mtile_off[e] = moff;
+        s_moff[e] = moff;
+        if (t2.BM > 0) {
+            t2.off[e] = moff2;
+            s_moff2[e] = moff2;
+        }
+    }
+    if (e == 0) {
+        offsets[E] = total;
+        mtile_off[E] = mtotal;
+        s_moff[E] = mtotal;
+        if (t2.BM > 0) {
+            t2.off[E] = mtotal2;
+            s_moff2[E] = mtotal2;
+        }
+        s_w[36] = total;
+        s_w[37] = mtotal;
+        s_w[38] = mtotal2;
+        status[0] = anybad ? MOE_DEV_BAD_ID : 0;
+    }
+    __syncthreads();
+    total = s_w[36];
+    mtotal = s_w[37];
+    fill_mtile_owners(s_moff, E, mtotal, mtile_expert);
+    if (t2.BM > 0)
+        fill_mtile_owners(s_moff2, E, s_w[38], t2.expert);
     const int64_t routed = total - (int64_t)nsh * T;
     for (int64_t i = threadIdx.x; i < (int64_t)nsh * T; i += 1024)
         sorted_slot[routed + i] = (int32_t)((i % T) * K);
@@ -219,6 +252,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ 
                                                           int32_t *__restrict__ offsets,
                                                           int32_t *__restrict__ mtile_off,
                                                           int32_t *__restrict__ mtile_expert,
+                                                          MTileTable2 t2,
                                                           int32_t *__restrict__ status,
                                                           int32_t *__restrict__ ctr, int nctr,
                                                           SavedHeader *__restrict__ hdr,
@@ -228,7 +262,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ 
 {
     write_header_and_counters(hdr, problem_hash, epoch, ctr, nctr);
     __shared__ int32_t s_cnt[1024];
-    __shared__ int32_t s_moff[1025];
+    __shared__ int32_t s_moff[2 * 1025];
     __shared__ int32_t s_w[40];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int e = wave; e < E; e += 16) {
@@ -255,7 +289,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ 
     int32_t total;
     const int32_t off = block_excl_scan(c, s_w, &total);
     publish_plan(c, off, total, anybad, E + nsh, BM, counts, offsets, mtile_off, mtile_expert,
-                 status, s_w, s_moff, nsh, T, K, sorted_slot);
+                 t2, status, s_w, s_moff, nsh, T, K, sorted_slot);
 }
 
 // One wave routes the slots [s0, s1) in order, 64 at a time: lanes holding
@@ -347,16 +381,17 @@ __global__ __launch_bounds__(1024) void route_block_kernel(
     const Id *__restrict__ ids, int64_t TK, int E, int nbits, int RC, int NB, int BM,
     const int32_t *__restrict__ hist, const int32_t *__restrict__ bad,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ mtile_off,
-    int32_t *__restrict__ mtile_expert, int32_t *__restrict__ status, int32_t *__restrict__ ctr,
-    int nctr, SavedHeader *__restrict__ hdr, uint64_t problem_hash, uint64_t epoch, int nsh,
-    int64_t T, int K, int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_pos)
+    int32_t *__restrict__ mtile_expert, MTileTable2 t2, int32_t *__restrict__ status,
+    int32_t *__restrict__ ctr, int nctr, SavedHeader *__restrict__ hdr, uint64_t problem_hash,
+    uint64_t epoch, int nsh, int64_t T, int K, int32_t *__restrict__ sorted_slot,
+    int32_t *__restrict__ slot_pos)
 {
     extern __shared__ int32_t lds[];
     int32_t *tab = lds;         // [E][16]: chunk counts, then chunk bases
     int32_t *tot = tab + E * 16; // [E]: slots of expert e over all chunks
     int32_t *bef = tot + E;      // [E]: slots of expert e in chunks before this block's
     __shared__ int32_t s_w[40];
-    __shared__ int32_t s_moff[1025];
+    __shared__ int32_t s_moff[2 * 1025];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b0 = blockIdx.x * 16;
     const bool lead = blockIdx.x == 0;
@@ -498,7 +533,7 @@ __global__ __launch_bounds__(1024) void route_block_kernel(
     const int32_t off = expert_excl_scan(c, E + nsh, s_w, &total);
     if (lead)
         publish_plan(c, off, total, anybad, E + nsh, BM, counts, offsets, mtile_off,
-                     mtile_expert, status, s_w, s_moff, nsh, T, K, sorted_slot);
+                     mtile_expert, t2, status, s_w, s_moff, nsh, T, K, sorted_slot);
     if (e < E) {
         int32_t run = off + bef[e];
 #pragma unroll
@@ -705,6 +740,7 @@ static void launch_route_t(const Id *ids, int64_t TK, int E, int BM, const Route
     const size_t lds_self = lds_block + sizeof(int32_t) * (size_t)E; // and aft[E]
     const int K = rb.T > 0 ? (int)(TK / rb.T) : 1;
     const int nctr = rb.ctr ? rb.nctr : 0;
+    MTileTable2 t2{rb.mtile2_off, rb.mtile2_expert, rb.mtile2_off ? rb.BM2 : 0};
     if (TK > 0 && lds_block <= 65536) {
         const int nblk = (rp.NB + 15) / 16;
         const int mode = nblk == 1 ? ROUTE_ONE
@@ -718,7 +754,8 @@ static void launch_route_t(const Id *ids, int64_t TK, int E, int BM, const Route
                                          : route_block_kernel<Id, ROUTE_HIST>;
         hipLaunchKernelGGL(kern, dim3(nblk), dim3(1024), mode == ROUTE_SELF ? lds_self : lds_block,
                            stream, ids, TK, E, rp.nbits, rp.RC, rp.NB, BM, rb.hist, rb.bad,
-                           rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert, rb.status, rb.ctr,
+                           rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert, t2, rb.status,
+                           rb.ctr,
                            nctr, rb.saved_hdr, rb.problem_hash, rb.epoch, rb.nshared, rb.T, K,
                            rb.sorted_slot, rb.slot_pos);
         return;
@@ -729,7 +766,7 @@ static void launch_route_t(const Id *ids, int64_t TK, int E, int BM, const Route
                            rp.RC, rp.NB, rb.hist, rb.bad);
     const int nb_scan = TK > 0 ? rp.NB : 0;
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, rb.hist, rb.bad, E,
-                       nb_scan, BM, rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert,
+                       nb_scan, BM, rb.counts, rb.offsets, rb.mtile_off, rb.mtile_expert, t2,
                        rb.status, rb.ctr, nctr, rb.saved_hdr, rb.problem_hash, rb.epoch,
                        rb.nshared, rb.T, K, rb.sorted_slot);
     if (TK > 0)

@@ -52,8 +52,10 @@ def test_workspace_query_rejects_bad_problems(bad, code):
 @pytest.mark.parametrize("shape,plan", [
     # (T, H, I, E, K): decode, prefill, skewed shapes; rows per expert 32, 384, 2048
     ((128, 7168, 2048, 32, 8), (64, "pipelined")),
-    ((4096, 2048, 1408, 64, 6), (128, "tiles")),
+    ((4096, 2048, 1408, 64, 6), (128, "tiles_big_gemm2")),
     ((8192, 7168, 2048, 32, 8), (256, "big_tiles")),
+    # 225 rows per expert: both GEMMs on 128-row tiles
+    ((600, 512, 384, 8, 3), (128, "tiles")),
     # ragged H: the engine
     ((600, 264, 256, 8, 2), (128, "engine")),
 ])
@@ -66,9 +68,9 @@ def test_forward_plan_picks_the_tile_height_from_rows_per_expert(shape, plan):
     # picks it by default on 64-row tiles only
     rows, fam = m.fwd_plan(p, m.PIPELINE)
     bulk = m.fwd_plan(p, m.BULK)
-    if plan[1] in ("tiles", "pipelined"):
+    if plan[1] in ("tiles", "pipelined", "tiles_big_gemm2"):
         assert (rows, fam) == (plan[0], "pipelined")
-        assert bulk == (plan[0], "tiles")
+        assert bulk == (plan[0], "tiles" if plan[1] == "pipelined" else plan[1])
     elif plan[1] == "big_tiles":
         assert fam == "pipelined" and rows in (128, 256)
         assert bulk == plan

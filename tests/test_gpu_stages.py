@@ -31,7 +31,8 @@ pytestmark = pytest.mark.gpu
 STAGE_CASES = [
     # name, T, H, I, E, K, dtype, routing, flags
     ("bm64", 40, 512, 256, 16, 4, "bf16", "uniform", 0),
-    ("bm128", 700, 512, 384, 8, 3, "bf16", "uniform", 0),
+    ("bm128", 600, 512, 384, 8, 3, "bf16", "uniform", 0),
+    ("bm128_big_gemm2", 1000, 512, 256, 8, 3, "bf16", "uniform", 0),
     ("big_tiles", 1100, 512, 256, 4, 2, "bf16", "uniform", 0),
     ("zipf_empty", 515, 256, 128, 16, 4, "bf16", "zipf", 0),
     ("engine_ragged", 333, 264, 200, 6, 2, "bf16", "uniform", 0),
@@ -65,10 +66,12 @@ def test_stages_match_oracle_intermediates(gpu_lib, case):
 
 
 POISON_CONFIGS = [
-    # name, T, H, I, E, K, flags: 128-row tiles, 64-row tiles, the pipelined launch
+    # name, T, H, I, E, K, flags: 128-row tiles, 64-row tiles, the pipelined
+    # launch, GEMM2 on 256-row tiles
     ("p_bm128", 300, 256, 128, 8, 2, 0),
     ("p_bm64", 64, 256, 128, 16, 2, 0),
     ("p_pipe", 300, 256, 128, 8, 2, 2),
+    ("p_big_gemm2", 1200, 256, 128, 8, 2, 0),
 ]
 
 

@@ -26,6 +26,10 @@ CASES = [
     ("tiles_bm64", 207, 1024, 512, 16, 4, 0, "uniform"),
     ("tiles_bm256", 2051, 512, 512, 2, 2, 0, "uniform"),
     ("tiles_shared", 600, 512, 256, 8, 3, 512, "uniform"),
+    # 257-512 rows per expert: GEMM1 on 128-row tiles, GEMM2 on 256-row tiles
+    ("tiles_big_gemm2", 1000, 512, 256, 8, 3, 0, "uniform"),
+    ("tiles_big_gemm2_zipf_empty", 1400, 512, 256, 8, 2, 0, "zipf"),
+    ("tiles_big_gemm2_shared", 700, 512, 256, 8, 4, 512, "uniform"),
 ]
 
 
@@ -74,7 +78,7 @@ def test_grid_size_does_not_change_the_result(gpu_lib, case):
 
 
 # one case per tile height: the GEMM1 that saves h is its own kernel per height
-SAVED_CASES = [CASES[0], CASES[2], CASES[3]]
+SAVED_CASES = [CASES[0], CASES[2], CASES[3], CASES[5]]
 
 
 @pytest.mark.parametrize("case", SAVED_CASES, ids=[c[0] for c in SAVED_CASES])

@@ -21,11 +21,13 @@ pytestmark = pytest.mark.gpu
 
 # (name, T, H, I, E, K, dtype, routing): a bf16 shape on 64-row tiles, one on
 # the 256 x 256 tile kernel (more than 512 rows per expert), one on 128-row
-# tiles, a ragged bf16 shape (the engine), fp32 (the generic kernels)
+# tiles, one with GEMM2 alone on 256-row tiles (257-512 rows per expert), a
+# ragged bf16 shape (the engine), fp32 (the generic kernels)
 PAIRS = [
     ("bf16_bm64", (200, 1024, 512, 16, 4, "bf16", "uniform"), 37),
     ("bf16_big_tiles", (1024, 512, 256, 4, 4, "bf16", "uniform"), 300),
-    ("bf16_bm128", (700, 512, 384, 8, 3, "bf16", "zipf"), 129),
+    ("bf16_bm128", (600, 512, 384, 8, 3, "bf16", "zipf"), 129),
+    ("bf16_big_gemm2", (1000, 512, 256, 8, 3, "bf16", "uniform"), 700),
     ("bf16_ragged", (333, 264, 200, 6, 2, "bf16", "uniform"), 65),
     ("f32", (256, 256, 512, 8, 2, "f32", "uniform"), 31),
 ]
