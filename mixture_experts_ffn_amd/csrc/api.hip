@@ -634,12 +634,7 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
         a.act = at<void>(ws, L.act);
         a.hsave = saved ? at<void>(saved, L.s_h) : nullptr;
         a.o = at<void>(ws, L.o);
-        a.y = y;
-        a.gates = topk_weights;
-        a.ids = topk_ids;
-        a.ids64 = p->ids_dtype == MOE_FFN_I64;
         a.sorted_slot = rb.sorted_slot;
-        a.slot_pos = rb.slot_pos;
         a.offsets = rb.offsets;
         a.mtile_off = rb.mtile_off;
         a.mtile_expert = rb.mtile_expert;

@@ -133,11 +133,7 @@ struct FastFwdArgs {
     void *act;                   // [TK, I]
     void *hsave;                 // optional [TK, 2I]
     void *o;                     // [TK, H]
-    void *y;                     // [T, H] (pipelined mode)
-    const float *gates;          // [T, K] (pipelined mode)
-    const void *ids;             // [T, K] int32 or int64 (pipelined mode)
     const int32_t *sorted_slot;  // [TK]
-    const int32_t *slot_pos;     // [TK]
     const int32_t *offsets;      // [E + 1]
     const int32_t *mtile_off;    // [E + 1]
     const int32_t *mtile_expert; // [max_mtiles]
@@ -147,7 +143,6 @@ struct FastFwdArgs {
     int32_t *status;             // device status word (MOE_DEV_* bits)
     int64_t timeout_ticks;       // watchdog of every wait, in s_memrealtime ticks
     int T, H, I, E, K;
-    int ids64;
     int max_mtiles;
     int drop_mt;                 // test hook: M-tile whose first GEMM1 release is dropped (-1)
     SharedExperts sh;            // E counts the shared chunks too (sh.Er routed)
