@@ -84,9 +84,19 @@ struct WFrag {
 // Position of a workgroup in its XCD's slice [lo, hi) of the tile order:
 // round j of the walk takes tile lo + j*step + slot, or + (step - 1 - slot) in
 // odd rounds, so that where full and partial M-tiles alternate in the order
-// no workgroup gets only the expensive ones.
+// no workgroup gets only the expensive ones.  With six rounds or more, the
+// last two rounds of every slice (from offset `tail` on) go by tickets
+// instead, to the workgroups that finish first: with the strided walk alone
+// the launch ends with the workgroups that hold one tile more or whose tiles
+// ran slower (weight panels fetched from memory rather than a cache), while
+// the others idle.
 struct Cursor {
     int lo, hi, step, j;
+    int send;  // end of the strided rounds of this slice
+    int tail;  // offset in each slice of the ticketed tiles (-1: none)
+    int L;     // the claimed tile, once the walk takes tickets
+    int tried; // slices found exhausted
+    bool tick; // the walk takes tickets
 };
 
 // Reads an accumulator element (an AGPR) into a VGPR exactly here: volatile
@@ -116,20 +126,69 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
     const int wm = wave >> 1, wn = wave & 1;
 
     // this XCD's eighth of the tile order, walked by its workgroups
+    const int total = mtiles * ntn;
+    const int range = (total + 7) >> 3;
     Cursor cc;
     {
-        const int total = mtiles * ntn;
-        const int range = (total + 7) >> 3;
         cc.step = per_xcd_wg;
         cc.lo = xcd * range;
         cc.hi = min((xcd + 1) * range, total);
         cc.j = 0;
+        const int rounds = (range + cc.step - 1) / cc.step;
+        cc.tail = rounds >= 6 ? (rounds - 2) * cc.step : -1;
+        cc.send = cc.tail >= 0 ? min(cc.hi, cc.lo + cc.tail) : cc.hi;
+        cc.L = 0;
+        cc.tried = 0;
+        cc.tick = false;
     }
     auto pos = [&](const Cursor &c) __attribute__((always_inline)) {
-        return c.lo + c.j * c.step + ((c.j & 1) ? c.step - 1 - slot : slot);
+        return c.tick ? c.L : c.lo + c.j * c.step + ((c.j & 1) ? c.step - 1 - slot : slot);
     };
-    if (pos(cc) >= cc.hi)
-        return;
+    // A ticket of the slices' ticketed tiles, this XCD's slice first: wave 0
+    // draws it from the slice's counter (zeroed by the routing kernel; this
+    // GEMM's eight of them) and passes it to the other waves through LDS.
+    __shared__ int tick_bcast[2];
+    int tick_par = 0;
+    auto claim = [&](Cursor &c) {
+        for (; c.tried < 8; ++c.tried) {
+            const int x = (xcd + c.tried) & 7;
+            const int hi = min((x + 1) * range, total);
+            const int lo = min(x * range + c.tail, hi);
+            if (wave == 0 && lane == 0)
+                tick_bcast[tick_par] =
+                    lo < hi ? __hip_atomic_fetch_add(args.tickets + (G1 ? 0 : 8) + x, 1,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : 0x7fffffff;
+            __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): the ticket is in LDS
+            lds_barrier();
+            const int t = tick_bcast[tick_par];
+            tick_par ^= 1;
+            if (t < hi - lo) {
+                c.L = lo + t;
+                return true;
+            }
+        }
+        return false;
+    };
+    // the walk's next tile; false when none is left
+    auto advance = [&](Cursor &c) {
+        if (!c.tick) {
+            c.j += 1;
+            if (pos(c) < c.send)
+                return true;
+            if (c.tail < 0)
+                return false;
+            c.tick = true;
+        }
+        return claim(c);
+    };
+    if (pos(cc) >= cc.send) {
+        if (cc.tail < 0)
+            return;
+        cc.tick = true;
+        if (!claim(cc))
+            return;
+    }
 
     // Copy sources of one tile: a wave-uniform base per operand and a 32-bit
     // byte offset per lane and copy (the host takes this kernel only when the
@@ -334,8 +393,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
     Src scur, snext;
     make_src(cur, scur);
     Cursor nc = cc;
-    nc.j += 1;
-    bool has_next = pos(nc) < nc.hi;
+    bool has_next = advance(nc);
     if (has_next) {
         nxt = decode_tile(args, KIND, pos(nc), ntn, BM);
         make_src(nxt, snext);
@@ -470,8 +528,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
         for (int q = 0; q < 2 * FN; ++q)
             read_w(W0, sg, 0, q);
         scur = snext;
-        nc.j += 1;
-        has_next = pos(nc) < nc.hi;
+        has_next = advance(nc);
         if (has_next) {
             nxt = decode_tile(args, KIND, pos(nc), ntn, BM);
             make_src(nxt, snext);

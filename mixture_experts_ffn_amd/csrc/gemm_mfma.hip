@@ -163,9 +163,14 @@ __device__ __forceinline__ void wait_counters(const int32_t *p, int need, const 
 // XCD owns a contiguous eighth of the tile order; its workgroups take every
 // (gridDim.x / 8)-th tile of it (separate launches), or claim its tiles from
 // the XCD's ticket counter (the pipelined launch; `tried` counts the XCD
-// slices this workgroup has found exhausted in the current phase).
+// slices this workgroup has found exhausted in the current phase).  In the
+// separate launches the tiles of each slice from `tail` on (its last, partial
+// round) also go by tickets, to the workgroups that finish first.
 struct Cursor {
     int kind, L, hi, step, tried;
+    int tail;   // offset in each slice of the ticketed tiles (-1: none)
+    int send;   // end of the strided part of this workgroup's slice
+    bool tick;  // the walk has reached the ticketed tiles
 };
 
 template <int BM, int MODE, int NWAVES>
@@ -191,31 +196,17 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
     auto kind_of = [&](int k) {
         return G1ONLY ? (int)KIND_G1 : MODE == FAST_G2 ? (int)KIND_G2 : k;
     };
-    auto phase_begin = [&](int kind, Cursor &c) {
-        const int total = mtiles * (kind == KIND_G1 ? ntn1 : ntn2);
-        const int range = (total + 7) >> 3;
-        c.kind = kind;
-        // 64-row tiles stream weights (HBM-bound): as many workgroups as make
-        // every round of the XCD's range full, so no round runs half-empty
-        int wg = per_xcd_wg;
-        if (BM == 64) {
-            const int rounds = (range + per_xcd_wg - 1) / per_xcd_wg;
-            wg = rounds > 0 ? (range + rounds - 1) / rounds : per_xcd_wg;
-        }
-        c.step = wg;
-        c.L = xcd * range + slot;
-        c.hi = min((xcd + 1) * range, total);
-        return slot < wg && c.L < c.hi;
-    };
-    // The pipelined launch hands out its tiles by tickets, so that any tile a
+    // Tickets.  The pipelined launch hands out its tiles by tickets, so that any tile a
     // GEMM2 tile waits for has been claimed by a workgroup that is running:
     // per-XCD counters over the same XCD slices (tiles in flight on one XCD
     // still share panels in its L2); a workgroup whose slice is exhausted
     // claims from the other XCDs' counters in turn, and GEMM2 tickets are only
     // drawn once every GEMM1 slice is exhausted.  GEMM1 tiles wait for
     // nothing, so every claimed tile completes whether or not the other
-    // workgroups of the launch are resident.  Wave 0 draws the ticket and
-    // passes it to the other waves through LDS.
+    // workgroups of the launch are resident.  The separate launches draw the
+    // tickets of their slices' last rounds the same way (one GEMM each, so
+    // they stop after the eighth slice).  Wave 0 draws the ticket and passes
+    // it to the other waves through LDS.
     __shared__ int tick_bcast[2];
     int tick_par = 0;
     auto claim = [&](Cursor &c) {
@@ -223,7 +214,8 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
             const int total = mtiles * (c.kind == KIND_G1 ? ntn1 : ntn2);
             const int range = (total + 7) >> 3;
             const int x = (xcd + c.tried) & 7;
-            const int lo = min(x * range, total), hi = min(lo + range, total);
+            const int hi = min((x + 1) * range, total);
+            const int lo = min(x * range + c.tail, hi);
             if (wave == 0 && lane == 0)
                 tick_bcast[tick_par] =
                     lo < hi ? __hip_atomic_fetch_add(args.tickets + (c.kind == KIND_G1 ? 0 : 8) + x,
@@ -239,19 +231,56 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
             }
             if (++c.tried < 8)
                 continue;
-            if (c.kind == KIND_G2)
+            if (!PIPE || c.kind == KIND_G2)
                 return false;
             c.kind = KIND_G2;
             c.tried = 0;
         }
     };
-    auto advance = [&](Cursor &c) {
-        if (PIPE)
-            return claim(c);
-        c.L += c.step;
-        if (c.L < c.hi)
+    auto phase_begin = [&](int kind, Cursor &c) {
+        const int total = mtiles * (kind == KIND_G1 ? ntn1 : ntn2);
+        const int range = (total + 7) >> 3;
+        c.kind = kind;
+        // 64-row tiles stream weights (HBM-bound): as many workgroups as make
+        // every round of the XCD's range full, so no round runs half-empty
+        int wg = per_xcd_wg;
+        if (BM == 64) {
+            const int rounds = (range + per_xcd_wg - 1) / per_xcd_wg;
+            wg = rounds > 0 ? (range + rounds - 1) / rounds : per_xcd_wg;
+        }
+        c.step = wg;
+        c.L = xcd * range + slot;
+        c.hi = min((xcd + 1) * range, total);
+        c.tried = 0;
+        // A partial last round after two full ones or more goes by tickets:
+        // with the strided walk alone, the workgroups that hold one tile more
+        // than the others (and those on slower compute units) set the end of
+        // the launch while the rest idle.  (64-row tiles make every round
+        // full instead, above.)
+        const int rounds = (range + wg - 1) / wg;
+        const bool ticketed = BM != 64 && rounds >= 3 && range % wg != 0;
+        c.tail = ticketed ? (rounds - 1) * wg : -1;
+        c.send = ticketed ? min(c.hi, xcd * range + c.tail) : c.hi;
+        c.tick = false;
+        if (slot >= wg)
+            return false;
+        if (c.L < c.send)
             return true;
-        return false;
+        if (!ticketed)
+            return false;
+        c.tick = true;
+        return claim(c);
+    };
+    auto advance = [&](Cursor &c) {
+        if (!PIPE && !c.tick) {
+            c.L += c.step;
+            if (c.L < c.send)
+                return true;
+            if (c.tail < 0)
+                return false;
+            c.tick = true;
+        }
+        return claim(c);
     };
     auto decode = [&](const Cursor &c) {
         const int kind = kind_of(c.kind);
@@ -524,6 +553,7 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
     bool have = false;
     if (PIPE) {
         cc.kind = KIND_G1;
+        cc.tail = 0;
         have = claim(cc);
     } else {
         if (MODE != FAST_G2)
