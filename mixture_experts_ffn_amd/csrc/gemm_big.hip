@@ -392,12 +392,6 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
     Tile nxt = cur;
     Src scur, snext;
     make_src(cur, scur);
-    Cursor nc = cc;
-    bool has_next = advance(nc);
-    if (has_next) {
-        nxt = decode_tile(args, KIND, pos(nc), ntn, BM);
-        make_src(nxt, snext);
-    }
     // Ring schedule (stage of a step = its global step index % NSTAGE): a
     // step's copies are issued NSTAGE - 1 steps ahead, during the first half
     // of an earlier step, into the stage whose reads all ended at that step's
@@ -407,10 +401,17 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
     // next tile's first step refills after the epilogue.  Every step issues
     // one copy group: past the last tile it re-copies that tile's last step
     // into a stage nobody reads again, so every wait counts the same.
-    // prologue: steps 0 .. NSTAGE-2 of the first tile
+    // prologue: steps 0 .. NSTAGE-2 of the first tile, in flight while the
+    // next tile is found and decoded
 #pragma unroll
     for (int st = 0; st < NSTAGE - 1; ++st)
         issue(scur, st, st);
+    Cursor nc = cc;
+    bool has_next = advance(nc);
+    if (has_next) {
+        nxt = decode_tile(args, KIND, pos(nc), ntn, BM);
+        make_src(nxt, snext);
+    }
     int sg = 0; // stage of the current step
     XFrag XA;
     WFrag W0, W1;

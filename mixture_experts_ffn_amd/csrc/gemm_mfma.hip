@@ -567,6 +567,12 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
         Tile nxt = cur;
         Src scur, snext;
         make_src(cur, scur);
+        // first NSTAGE-1 steps (every tile has at least that many K steps),
+        // in flight while the next tile is found and decoded
+        wait_ready(cur);
+#pragma unroll
+        for (int st = 0; st < NSTAGE - 1; ++st)
+            issue(scur, st, smem + st * C::STAGE_BYTES);
         Cursor nc = cc;
         bool has_next = advance(nc);
         if (has_next) {
@@ -576,11 +582,6 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
         // copies run ahead into the next tile only within one GEMM: a GEMM2
         // tile may read this very tile's output
         bool chain = has_next && nxt.kind == cur.kind;
-        // first NSTAGE-1 steps (every tile has at least that many K steps)
-        wait_ready(cur);
-#pragma unroll
-        for (int st = 0; st < NSTAGE - 1; ++st)
-            issue(scur, st, smem + st * C::STAGE_BYTES);
         int s_cur = 0; // stage of the current step (global step index % NSTAGE)
         int owed = -1; // release of the previous tile, made once its stores are done
         while (true) {
