@@ -223,13 +223,42 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
                             : 0x7fffffff;
             __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): the ticket is in LDS
             lds_barrier();
-            const int t = tick_bcast[tick_par];
+            const int t = uni(tick_bcast[tick_par]);
             tick_par ^= 1;
             if (t < hi - lo) {
                 c.L = lo + t;
                 return true;
             }
-            if (++c.tried < 8)
+            // The slice is exhausted.  Rather than trying the others one
+            // atomic at a time, wave 0 reads all eight counters at once (a
+            // load per lane; a counter only grows, so a slice seen exhausted
+            // stays so) and picks the next slice in ring order from this XCD
+            // that still has tiles; should its atomic find it exhausted after
+            // all, this repeats.
+            if (wave == 0) {
+                bool left = false;
+                if (lane < 8) {
+                    const int hx = min((lane + 1) * range, total);
+                    const int lx = min(lane * range + c.tail, hx);
+                    left = lx < hx && __hip_atomic_load(args.tickets + (c.kind == KIND_G1 ? 0 : 8) + lane,
+                                                         __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT) < hx - lx;
+                }
+                const uint64_t m = __ballot(left); // bit x: slice x has tiles left
+                int nd = 8;
+                for (int d = c.tried + 1; d < 8; ++d)
+                    if ((m >> ((xcd + d) & 7)) & 1) {
+                        nd = d;
+                        break;
+                    }
+                if (lane == 0)
+                    tick_bcast[tick_par] = nd;
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f); // lgkmcnt(0): the choice is in LDS
+            lds_barrier();
+            c.tried = uni(tick_bcast[tick_par]);
+            tick_par ^= 1;
+            if (c.tried < 8)
                 continue;
             if (!PIPE || c.kind == KIND_G2)
                 return false;
