@@ -196,8 +196,8 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
     auto kind_of = [&](int k) {
         return G1ONLY ? (int)KIND_G1 : MODE == FAST_G2 ? (int)KIND_G2 : k;
     };
-    // Tickets.  The pipelined launch hands out its tiles by tickets, so that any tile a
-    // GEMM2 tile waits for has been claimed by a workgroup that is running:
+    // Tickets.  The pipelined launch hands out its tiles by tickets, so that
+    // any tile a GEMM2 tile waits for has been claimed by a running workgroup:
     // per-XCD counters over the same XCD slices (tiles in flight on one XCD
     // still share panels in its L2); a workgroup whose slice is exhausted
     // claims from the other XCDs' counters in turn, and GEMM2 tickets are only
@@ -240,9 +240,9 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
                 if (lane < 8) {
                     const int hx = min((lane + 1) * range, total);
                     const int lx = min(lane * range + c.tail, hx);
-                    left = lx < hx && __hip_atomic_load(args.tickets + (c.kind == KIND_G1 ? 0 : 8) + lane,
-                                                         __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT) < hx - lx;
+                    const int32_t *ctr = args.tickets + (c.kind == KIND_G1 ? 0 : 8) + lane;
+                    left = lx < hx && __hip_atomic_load(ctr, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT) < hx - lx;
                 }
                 const uint64_t m = __ballot(left); // bit x: slice x has tiles left
                 int nd = 8;
