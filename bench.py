@@ -285,9 +285,12 @@ def measure(workload_name, args, primary):
         roof = {"bound": "mfma", "achieved": k_flops / (k_ms * 1e-3) / 1e12, "peak": peak,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(w.name, "pipeline" if "pipeline" in stage_ms else "gemm1",
-                                       "gemm_big.hip" if kernel_family == "big_tiles"
-                                       else "gemm_mfma.hip")
+    dom_role = "pipeline" if "pipeline" in stage_ms else "gemm1"
+    dom_src = "gemm_big.hip" if kernel_family == "big_tiles" else "gemm_mfma.hip"
+    roof["traffic"] = measured_traffic(w.name, dom_role, dom_src)
+    # the clock the kernel ran at under the power cap, and how busy its matrix
+    # cores were (what separates the clock from the kernel's own efficiency)
+    roof["clock_ghz"], roof["mfma_busy"] = measured_clock(w.name, dom_role, dom_src)
     roof["kernel"] = kernel
     roof["avg_launch_ms"] = k_ms
     # every stage of the bulk forward against its own bound: algorithmic bytes
@@ -412,24 +415,41 @@ def hbm_reference(dev, mib=2048, reps=10):
     return {"bytes_moved": 2 * n * 4, "ms": ms, "gbs": 2 * n * 4 / (ms * 1e-3) / 1e9}
 
 
-def measured_traffic(workload_name, kernel, source="gemm_mfma.hip"):
-    """HBM bytes per launch of the dominant kernel from the committed PMC summary
-    (profiles/traffic.txt), or None when the kernel source has changed since the
-    counters were taken or no summary exists for this workload and kernel."""
+def profile_entry(table_name, workload_name, kernel, source):
+    """The values a committed rocprofv3 summary table (profiles/<table_name>)
+    holds for this workload and kernel role, or None when the kernel source
+    has changed since the counters were taken or the table has no such line.
+    Lines: workload role source:sha1[:12] name=value ..."""
     import hashlib
 
     src = os.path.join(ROOT, "mixture_experts_ffn_amd", "csrc", source)
-    table = os.path.join(ROOT, "profiles", "traffic.txt")
+    table = os.path.join(ROOT, "profiles", table_name)
     if not (os.path.exists(src) and os.path.exists(table)):
         return None
     sha = hashlib.sha1(open(src, "rb").read()).hexdigest()[:12]
     for line in open(table):
         parts = line.split()
-        if (len(parts) == 5 and parts[0] == workload_name and parts[1] == kernel
+        if (len(parts) >= 4 and parts[0] == workload_name and parts[1] == kernel
                 and parts[2] == f"{source}:{sha}"):
-            vals = dict(p.split("=") for p in parts[3:])
-            return float(vals["fetch_bytes"]) + float(vals["write_bytes"])
+            return {k: float(v) for k, v in (p.split("=") for p in parts[3:])}
     return None
+
+
+def measured_traffic(workload_name, kernel, source="gemm_mfma.hip"):
+    """HBM bytes per launch of the dominant kernel from the committed PMC summary
+    (profiles/traffic.txt: FETCH_SIZE and WRITE_SIZE, scaled against a copy of
+    known size), or None when stale or absent."""
+    e = profile_entry("traffic.txt", workload_name, kernel, source)
+    return None if e is None else e["fetch_bytes"] + e["write_bytes"]
+
+
+def measured_clock(workload_name, kernel, source="gemm_mfma.hip"):
+    """Shader clock (GHz) and matrix-core busy fraction of the dominant kernel
+    from the committed PMC summary (profiles/clock.txt: GRBM_GUI_ACTIVE and
+    SQ_VALU_MFMA_BUSY_CYCLES over the dispatch), or (None, None) when stale or
+    absent."""
+    e = profile_entry("clock.txt", workload_name, kernel, source)
+    return (None, None) if e is None else (e["clock_ghz"], e["mfma_busy"])
 
 
 def cpu_baseline(w, inp, y_gpu, target_s):
