@@ -114,3 +114,31 @@ def test_full_size_forward_is_the_same_on_every_call(gpu_lib):
     for i, y in enumerate(ys[1:], 1):
         say(f"[tiles-full] call {i} equal={torch.equal(y, ys[0])}")
         assert torch.equal(y, ys[0])
+
+
+def test_many_experts_three_launch_routing_with_256_row_gemm2(gpu_lib):
+    # More than 910 experts: routing runs as three launches (histogram, scan,
+    # scatter), and its scan also builds the 256-row M-tile tables; about 261
+    # rows per expert put GEMM2 alone on 256 x 256 tiles.  Checked bit for bit
+    # against the pipelined launch (both GEMMs on 128-row tiles, tables of the
+    # one-table routing) and on sampled tokens against the oracle.
+    import numpy as np
+
+    w = Workload("many_experts_big_gemm2", 760, T=30000, H=256, I=128, E=920, K=8)
+    say("[tiles-many] generating T=30000 H=256 I=128 E=920 K=8")
+    inp = make_inputs(w)
+    d = to_device(inp)
+    prob = gpu_lib.make_problem(d["x"], d["topk_ids"], d["up_proj"], d["down_proj"])
+    assert gpu_lib.fwd_plan(prob) == (128, "tiles_big_gemm2")
+    say("[tiles-many] default and pipelined forwards")
+    y = fwd(gpu_lib, d)
+    y_pipe = fwd(gpu_lib, d, pipelined=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_pipe)
+    rng = np.random.default_rng(5)
+    toks = np.array(sorted({0, w.T - 1} | set(rng.choice(w.T, 30, replace=False).tolist())))
+    ref = oracle.forward_tokens(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["up_proj"],
+                                inp["down_proj"], toks)
+    err = max_rel_err(host_f64(y[torch.from_numpy(toks).cuda()]), ref)
+    say(f"[tiles-many] sampled {len(toks)} tokens max_rel_err={err:.3e}")
+    assert err <= TOL["bf16"]
