@@ -35,8 +35,9 @@
 //    the backward; GEMM2: o);
 //  * persistent: each XCD walks a contiguous eighth of the tile order (expert
 //    major, groups of M-tiles with N outer), its workgroups strided through
-//    it, so tiles in flight on one XCD share weight panels and token rows in
-//    its L2; a tile's last steps already copy the next tile's first steps.
+//    it (the last two rounds, from six on, by tickets), so tiles in flight on
+//    one XCD share weight panels and token rows in its L2; a tile's last
+//    steps already copy the next tile's first steps.
 // A tile's rows are split between the two wave rows in 32-row steps (a tile
 // of r rows gives the first ceil(r / 64) * 32 of them to wave row 0 and the
 // rest to wave row 1), and each wave multiplies only the 16-row blocks that

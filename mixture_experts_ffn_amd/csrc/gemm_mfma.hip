@@ -53,9 +53,10 @@
 //    tall tiles waste no more matrix-core time than short ones.
 //  * Persistent: the workgroups resident on the CUs walk XCD-local slices of
 //    the tile order (the hardware hands workgroup b to XCD b % 8), so tiles
-//    in flight on one XCD share weight panels and token rows in its L2; the
-//    next tile's first copies overlap the current tile's last steps and its
-//    epilogue.
+//    in flight on one XCD share weight panels and token rows in its L2; a
+//    slice's partial last round goes by tickets to the workgroups that finish
+//    first; the next tile's first copies overlap the current tile's last
+//    steps and its epilogue.
 #include "common.h"
 #include "kernels.h"
 #include "tile_common.h"
