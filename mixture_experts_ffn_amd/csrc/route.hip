@@ -292,52 +292,62 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t *__restrict__ 
                  t2, status, s_w, s_moff, nsh, T, K, sorted_slot);
 }
 
-// One wave routes the slots [s0, s1) in order, 64 at a time: lanes holding
-// the same expert find each other with ballots over the id bits, so the rank
-// inside the round is a popcount and the order stays stable.  base[e * bs] is
-// expert e's next position for this chunk (LDS, advanced here).
-template <typename Id>
-__device__ inline void scatter_chunk(const Id *__restrict__ ids, int64_t s0, int64_t s1, int E,
+// One wave routes the slots [r0, min(r0 + 512, s1)) in order, 64 at a time,
+// from their ids in idv: lanes holding the same expert find each other with
+// ballots over the id bits, so the rank inside the round is a popcount and the
+// order stays stable.  base[e * bs] is expert e's next position for this chunk
+// (LDS, advanced here).
+__device__ inline void scatter_round(const int64_t (&idv)[8], int64_t r0, int64_t s1, int E,
                                      int nbits, int32_t *base, int bs,
                                      int32_t *__restrict__ sorted_slot,
                                      int32_t *__restrict__ slot_pos)
 {
     const int lane = threadIdx.x & 63;
     const uint64_t lt = lanemask_lt();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int64_t r = r0 + 64 * j;
+        if (r >= s1)
+            break;
+        const int64_t s = r + lane;
+        const bool in = s < s1;
+        const int64_t eid = idv[j];
+        const bool valid = in && eid >= 0 && eid < E;
+        const int e = valid ? (int)eid : 0;
+        uint64_t m = __ballot(valid);
+        for (int bit = 0; bit < nbits; ++bit) {
+            const bool v = (e >> bit) & 1;
+            const uint64_t bb = __ballot(v);
+            m &= v ? bb : ~bb;
+        }
+        const int rank = __popcll(m & lt);
+        int pos = 0;
+        if (valid) {
+            pos = base[e * bs] + rank;
+            sorted_slot[pos] = (int32_t)s;
+            slot_pos[s] = pos;
+        } else if (in) {
+            slot_pos[s] = -1;
+        }
+        // the lowest lane of each expert group advances that expert's base
+        // after every lane of the round has read it (LDS operations of one
+        // wave complete in program order)
+        if (valid && rank == 0)
+            base[e * bs] = pos + __popcll(m);
+    }
+}
+
+// The same for the slots [s0, s1), a round of ids at a time.
+template <typename Id>
+__device__ inline void scatter_chunk(const Id *__restrict__ ids, int64_t s0, int64_t s1, int E,
+                                     int nbits, int32_t *base, int bs,
+                                     int32_t *__restrict__ sorted_slot,
+                                     int32_t *__restrict__ slot_pos)
+{
     for (int64_t r0 = s0; r0 < s1; r0 += 512) {
         int64_t idv[8];
         load_ids8(ids, r0, s1, idv);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t r = r0 + 64 * j;
-            if (r >= s1)
-                break;
-            const int64_t s = r + lane;
-            const bool in = s < s1;
-            const int64_t eid = idv[j];
-            const bool valid = in && eid >= 0 && eid < E;
-            const int e = valid ? (int)eid : 0;
-            uint64_t m = __ballot(valid);
-            for (int bit = 0; bit < nbits; ++bit) {
-                const bool v = (e >> bit) & 1;
-                const uint64_t bb = __ballot(v);
-                m &= v ? bb : ~bb;
-            }
-            const int rank = __popcll(m & lt);
-            int pos = 0;
-            if (valid) {
-                pos = base[e * bs] + rank;
-                sorted_slot[pos] = (int32_t)s;
-                slot_pos[s] = pos;
-            } else if (in) {
-                slot_pos[s] = -1;
-            }
-            // the lowest lane of each expert group advances that expert's base
-            // after every lane of the round has read it (LDS operations of one
-            // wave complete in program order)
-            if (valid && rank == 0)
-                base[e * bs] = pos + __popcll(m);
-        }
+        scatter_round(idv, r0, s1, E, nbits, base, bs, sorted_slot, slot_pos);
     }
 }
 
@@ -395,6 +405,7 @@ __global__ __launch_bounds__(1024) void route_block_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int b0 = blockIdx.x * 16;
     const bool lead = blockIdx.x == 0;
+    int64_t one_ids[8]; // ROUTE_ONE: this wave's ids, from the count to the scatter
     if (lead)
         write_header_and_counters(hdr, problem_hash, epoch, ctr, nctr);
     int anybad = 0;
@@ -443,15 +454,16 @@ __global__ __launch_bounds__(1024) void route_block_kernel(
         for (int i = threadIdx.x; i < E * 16; i += 1024)
             tab[i] = 0;
         __syncthreads();
+        // a chunk is one round of at most 512 slots here: its ids stay in
+        // registers for the scatter
         const int64_t s0 = (int64_t)wave * RC;
         const int64_t s1 = s0 + RC < TK ? s0 + RC : TK;
-        for (int64_t r0 = s0; r0 < s1; r0 += 512) {
-            int64_t v[8];
-            load_ids8(ids, r0, s1, v);
+        if (s0 < s1) {
+            load_ids8(ids, s0, s1, one_ids);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const int64_t e = v[j];
-                if (r0 + 64 * j + lane >= s1)
+                const int64_t e = one_ids[j];
+                if (s0 + 64 * j + lane >= s1)
                     continue;
                 if (e >= 0 && e < E)
                     atomicAdd(&tab[e * 16 + wave], 1);
@@ -548,7 +560,10 @@ __global__ __launch_bounds__(1024) void route_block_kernel(
     if (b < NB) {
         const int64_t s0 = (int64_t)b * RC;
         const int64_t s1 = s0 + RC < TK ? s0 + RC : TK;
-        scatter_chunk(ids, s0, s1, E, nbits, tab + wave, 16, sorted_slot, slot_pos);
+        if constexpr (MODE == ROUTE_ONE)
+            scatter_round(one_ids, s0, s1, E, nbits, tab + wave, 16, sorted_slot, slot_pos);
+        else
+            scatter_chunk(ids, s0, s1, E, nbits, tab + wave, 16, sorted_slot, slot_pos);
     }
 }
 
@@ -743,7 +758,9 @@ static void launch_route_t(const Id *ids, int64_t TK, int E, int BM, const Route
     MTileTable2 t2{rb.mtile2_off, rb.mtile2_expert, rb.mtile2_off ? rb.BM2 : 0};
     if (TK > 0 && lds_block <= 65536) {
         const int nblk = (rp.NB + 15) / 16;
-        const int mode = nblk == 1 ? ROUTE_ONE
+        // (one block means at most 8192 slots, so chunks of at most 512 slots:
+        // one round of ids per wave, which ROUTE_ONE keeps in registers)
+        const int mode = nblk == 1 && rp.RC <= 512 ? ROUTE_ONE
                          : TK <= kSelfCountSlots && lds_self <= 65536 ? ROUTE_SELF
                                                                      : ROUTE_HIST;
         if (mode == ROUTE_HIST)
