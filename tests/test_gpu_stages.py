@@ -67,11 +67,14 @@ def test_stages_match_oracle_intermediates(gpu_lib, case):
 
 POISON_CONFIGS = [
     # name, T, H, I, E, K, flags: 128-row tiles, 64-row tiles, the pipelined
-    # launch, GEMM2 on 256-row tiles
+    # launch, GEMM2 on 256-row tiles, and the last one on 16 workgroups, where
+    # both GEMMs hand out their last rounds by tickets (counters that routing
+    # must reset on every call)
     ("p_bm128", 300, 256, 128, 8, 2, 0),
     ("p_bm64", 64, 256, 128, 16, 2, 0),
     ("p_pipe", 300, 256, 128, 8, 2, 2),
     ("p_big_gemm2", 1200, 256, 128, 8, 2, 0),
+    ("p_ticketed_tails", 1300, 2048, 384, 7, 2, 0x200),
 ]
 
 
