@@ -274,7 +274,7 @@ def measure(workload_name, args, primary):
                     "(gathered up_proj GEMM + SwiGLU)")
         kernel = {"tiles": g1_tiles,
                   "tiles_big_gemm2": g1_tiles,
-                  "big_tiles": f"moe::big::moe_fwd_bf16_big<{mode}> "
+                  "big_tiles": f"moe::big::moe_fwd_bf16_big<{mode}, false> "
                                "(gathered up_proj GEMM + SwiGLU, 256 x 256 tiles)",
                   }.get(kernel_family, f"up_proj GEMM + SwiGLU ({kernel_family} kernel)")
     if w.name.startswith("decode"):

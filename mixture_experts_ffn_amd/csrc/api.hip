@@ -682,7 +682,9 @@ static int fwd_run(const moe_ffn_problem *p, const void *x, const void *topk_ids
                 a2.max_mtiles = (int)L.max_mtiles2;
             }
             record(ev, MOE_FFN_STAGE_GEMM2, true, s);
-            HIP_TRY(L.tiles.big || big2 ? moe::launch_fast_fwd_big(moe::FAST_G2, a2, num_cus, s)
+            // GEMM2 on 256-row tiles over GEMM1's 128: one M-tile in two is
+            // short (prefill: 79-175 of 256 rows), so its padding is not copied
+            HIP_TRY(L.tiles.big || big2 ? moe::launch_fast_fwd_big(moe::FAST_G2, a2, num_cus, s, big2)
                                         : moe::launch_fast_fwd(moe::FAST_G2, BM, a, num_cus, s),
                     "gemm2 launch");
             record(ev, MOE_FFN_STAGE_GEMM2, false, s);

@@ -63,6 +63,7 @@ constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
 constexpr int A_LOADS = A_BYTES / 1024 / NW;  // 1 KB copy chunks per wave per step
 constexpr int B_LOADS = B_BYTES / 1024 / NW;
 constexpr int NL = A_LOADS + B_LOADS;         // copy instructions per wave per step
+constexpr int A_ROWS = A_LOADS * (1024 / (BK * 2)); // token rows one wave copies
 constexpr int PIECES = BK / 8;                // 16-byte pieces per token row
 constexpr int RPC = 1024 / (BK * 2);          // token rows per 1 KB chunk
 constexpr int CPP = BK / 4;                   // 1 KB chunks per weight panel (4 k-rows each)
@@ -72,6 +73,7 @@ constexpr int HALF = FM * FN;                 // MFMAs of one panel per step
 static_assert(NSTAGE * STAGE_BYTES <= 160 * 1024, "LDS");
 static_assert(A_LOADS * NW * 1024 == A_BYTES && B_LOADS * NW * 1024 == B_BYTES, "copy split");
 static_assert(HALF == 4 * NL && HALF == 4 * 2 * FN && FN == 4, "one read and one copy per 4 MFMAs");
+static_assert(NSTAGE == 4 && A_ROWS * NW == BM, "two copy groups stay in flight; waves' rows tile the tile");
 
 // fragments of one step: token rows (MFMA B operand), and one panel's weight
 // columns (MFMA A operand, two transposing reads of 4 k values each)
@@ -110,7 +112,10 @@ __device__ __forceinline__ float acc_rd(float a)
     return v;
 }
 
-template <int MODE>
+// SKIP: waves leave out the copies of token rows that lie past a tile's rows
+// (for launches where many tiles are short: a per-step choice of wait that
+// costs launches of full tiles about 8 %, so it is compiled only where used)
+template <int MODE, bool SKIP>
 __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
 {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NSTAGE * STAGE_BYTES];
@@ -199,6 +204,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
         uint32_t b[B_LOADS];
         const unsigned char *wbase; // weight matrix of the tile's expert
         int ldb;                    // its row stride (elements)
+        bool skip_a;                // this wave's token rows all lie past the tile's
     };
     const unsigned char *abase =
         static_cast<const unsigned char *>(G1 ? args.x : args.act); // token rows
@@ -243,6 +249,11 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
                       : static_cast<const bf16 *>(args.w2) + (int64_t)t.e * I * H);
         sr.wbase = reinterpret_cast<const unsigned char *>(W);
         sr.ldb = G1 ? 2 * (shd ? args.sh.Is : I) : H;
+        // This wave copies token rows A_ROWS * wave .. + A_ROWS - 1.  When they
+        // all lie past the tile's rows no wave reads them (the row split
+        // below never reaches a 32-row step past the last row), so the wave
+        // leaves them out: a third of prefill's GEMM2 rows are such padding.
+        sr.skip_a = SKIP && wave * A_ROWS >= t.rows;
         const int pstride = G1 ? (shd ? args.sh.Is : I) : PW; // column offset of the second panel
 #pragma unroll
         for (int i = 0; i < B_LOADS; ++i) {
@@ -261,10 +272,11 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
     auto copy_one = [&](const Src &sr, int kb, int stage, int i) __attribute__((always_inline)) {
         unsigned char *sbase = smem + stage * STAGE_BYTES;
         const int k0 = kb * BK;
-        if (i < A_LOADS)
-            g2l16s(abase + (size_t)k0 * 2, sr.a[i],
-                   (lds_void *)(sbase + (wave * A_LOADS + i) * 1024));
-        else
+        if (i < A_LOADS) {
+            if (!(SKIP && sr.skip_a))
+                g2l16s(abase + (size_t)k0 * 2, sr.a[i],
+                       (lds_void *)(sbase + (wave * A_LOADS + i) * 1024));
+        } else
             g2l16s(sr.wbase + (size_t)k0 * sr.ldb * 2, sr.b[i - A_LOADS],
                    (lds_void *)(sbase + A_BYTES + (wave * B_LOADS + i - A_LOADS) * 1024));
     };
@@ -272,6 +284,19 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
 #pragma unroll
         for (int i = 0; i < NL; ++i)
             copy_one(sr, kb, stage, i);
+    };
+    // copies in one group (one step) of a tile's sources
+    auto group_size = [&](const Src &sr) { return SKIP && sr.skip_a ? B_LOADS : NL; };
+    // Wait until the oldest of this wave's three copy groups in flight has
+    // landed, the two younger ones (n copies together) may stay in flight.
+    // (Stores issued between them only make the wait stricter.)
+    auto wait_groups = [&](int n) __attribute__((always_inline)) {
+        if (!SKIP || n >= 2 * NL)
+            wait_vm<2 * NL>();
+        else if (n >= NL + B_LOADS)
+            wait_vm<NL + B_LOADS>();
+        else
+            wait_vm<2 * B_LOADS>();
     };
 
     // Fragment reads of one step from a stage.  Token-row block fm: lane l
@@ -417,7 +442,9 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
     XFrag XA;
     WFrag W0, W1;
     split = ((cur.rows + 63) >> 6) << 5;
-    wait_vm<(NSTAGE - 2) * NL>();
+    // size of the copy group issued last (the prologue's, of the first tile)
+    int gprev = group_size(scur);
+    wait_groups(2 * gprev);
     lds_barrier();
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
@@ -463,6 +490,8 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
                 cs.b[i] = use_next ? snext.b[i] : scur.b[i];
             cs.wbase = use_next ? snext.wbase : scur.wbase;
             cs.ldb = use_next ? snext.ldb : scur.ldb;
+            cs.skip_a = use_next ? snext.skip_a : scur.skip_a;
+            const int gsz = group_size(cs);
             const int ckb = own ? ahead : has_next ? ahead - nk : nk - 1;
 #pragma unroll
             for (int j = 0; j < HALF; ++j) {
@@ -477,8 +506,9 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
             }
             // the next step (this tile's kb + 1 or, chained, the next tile's
             // step 0) must have landed; the NSTAGE - 2 copy groups issued
-            // after it may stay in flight
-            wait_vm<(NSTAGE - 2) * NL>();
+            // after it (the previous step's and this one's) may stay in flight
+            wait_groups(gprev + gsz);
+            gprev = gsz;
             __builtin_amdgcn_s_waitcnt(0xc07f); // this wave's reads of the stage are done
             lds_barrier();
             // (after a tile's last step these reads are repeated after the
@@ -538,24 +568,29 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_fwd_bf16_big(FastFwdArgs args)
     }
 }
 
-template <int MODE> static hipError_t launch(const FastFwdArgs &a, int num_cus, hipStream_t stream)
+template <int MODE, bool SKIP>
+static hipError_t launch(const FastFwdArgs &a, int num_cus, hipStream_t stream)
 {
     // one workgroup per CU, whole XCDs
     const int grid = a.grid > 0 ? a.grid : (num_cus + 7) / 8 * 8;
-    hipLaunchKernelGGL((moe_fwd_bf16_big<MODE>), dim3((unsigned)grid), dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((moe_fwd_bf16_big<MODE, SKIP>), dim3((unsigned)grid), dim3(64 * NW), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
 } // namespace big
 
-hipError_t launch_fast_fwd_big(int mode, const FastFwdArgs &a, int num_cus, hipStream_t stream)
+hipError_t launch_fast_fwd_big(int mode, const FastFwdArgs &a, int num_cus, hipStream_t stream,
+                              bool skip_padding)
 {
     if (a.T <= 0)
         return hipSuccess;
     switch (mode) {
-    case FAST_G1: return big::launch<FAST_G1>(a, num_cus, stream);
-    case FAST_G1H: return big::launch<FAST_G1H>(a, num_cus, stream);
-    case FAST_G2: return big::launch<FAST_G2>(a, num_cus, stream);
+    case FAST_G1: return big::launch<FAST_G1, false>(a, num_cus, stream);
+    case FAST_G1H: return big::launch<FAST_G1H, false>(a, num_cus, stream);
+    case FAST_G2:
+        return skip_padding ? big::launch<FAST_G2, true>(a, num_cus, stream)
+                            : big::launch<FAST_G2, false>(a, num_cus, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -153,7 +153,10 @@ hipError_t launch_fast_fwd(int mode, int BM, const FastFwdArgs &a, int num_cus,
 // the same grouped GEMMs (FAST_G1, FAST_G1H, FAST_G2) on 256 x 256 tiles, one
 // 4-wave workgroup per CU (gemm_big.hip); the M-tile tables must be built for
 // 256-row tiles
-hipError_t launch_fast_fwd_big(int mode, const FastFwdArgs &a, int num_cus, hipStream_t stream);
+// skip_padding (GEMM2 only): leave out the copies of token rows past a tile's
+// rows, for launches where many tiles are short
+hipError_t launch_fast_fwd_big(int mode, const FastFwdArgs &a, int num_cus, hipStream_t stream,
+                               bool skip_padding = false);
 
 // bf16 engine (gemm_engine.hip): forward F1/F2 and backward B2/B4/B5/B7
 struct EngineArgs {
