@@ -51,6 +51,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int NSTAGE = 3; // LDS ring depth
 
@@ -464,7 +465,7 @@ __device__ __forceinline__ void make_src(const EngineArgs &a, const TileInfo &t,
 
 template <int KIND, int BM, int WM>
 __device__ __forceinline__ void issue(const EngineArgs &a, const TileInfo &t,
-                                      const Src<KIND, BM, WM> &s, int kb, unsigned char *sbase,
+                                      const Src<KIND, BM, WM> &s, int kb, lds_u8 *sbase,
                                       int wave, int lane, const GatherIdx<KIND, BM, WM> &g)
 {
     using C = Cfg<KIND, BM, WM>;
@@ -845,7 +846,11 @@ __global__ __launch_bounds__(64 * Shape<KIND>::NW, Shape<KIND>::WGPC) void engin
     int gstage_issue = 0; // stage the producer writes next
     int inflight = 0;     // steps copied but not yet consumed
     auto produce = [&]() {
-        issue<KIND, BM, WM>(a, pt, ps, pkb, smem + gstage_issue * C::STAGE_BYTES, wave, lane, pg);
+        // the stage as an LDS pointer formed here, beside the shared array:
+        // each copy's M0 is then one scalar add, not a null-checked
+        // conversion of a generic pointer
+        issue<KIND, BM, WM>(a, pt, ps, pkb, (lds_u8 *)(smem + gstage_issue * C::STAGE_BYTES), wave,
+                            lane, pg);
         gstage_issue = gstage_issue == NSTAGE - 1 ? 0 : gstage_issue + 1;
         ++inflight;
         ++pkb;
