@@ -287,10 +287,10 @@ def measure(workload_name, args, primary):
     roof["frac"] = roof["achieved"] / roof["peak"]
     dom_role = "pipeline" if "pipeline" in stage_ms else "gemm1"
     dom_src = "gemm_big.hip" if kernel_family == "big_tiles" else "gemm_mfma.hip"
-    roof["traffic"] = measured_traffic(w.name, dom_role, dom_src)
+    roof["traffic"] = measured_traffic(w.name, dom_role, dom_src, tile_rows)
     # the clock the kernel ran at under the power cap, and how busy its matrix
     # cores were (what separates the clock from the kernel's own efficiency)
-    roof["clock_ghz"], roof["mfma_busy"] = measured_clock(w.name, dom_role, dom_src)
+    roof["clock_ghz"], roof["mfma_busy"] = measured_clock(w.name, dom_role, dom_src, tile_rows)
     roof["kernel"] = kernel
     roof["avg_launch_ms"] = k_ms
     # every stage of the bulk forward against its own bound: algorithmic bytes
@@ -415,11 +415,13 @@ def hbm_reference(dev, mib=2048, reps=10):
     return {"bytes_moved": 2 * n * 4, "ms": ms, "gbs": 2 * n * 4 / (ms * 1e-3) / 1e9}
 
 
-def profile_entry(table_name, workload_name, kernel, source):
+def profile_entry(table_name, workload_name, kernel, source, tile_rows):
     """The values a committed rocprofv3 summary table (profiles/<table_name>)
     holds for this workload and kernel role, or None when the kernel source
-    has changed since the counters were taken or the table has no such line.
-    Lines: workload role source:sha1[:12] name=value ..."""
+    has changed since the counters were taken, the line was taken with
+    another tile height (one source holds the kernels of several heights) or
+    the table has no such line.
+    Lines: workload role source:sha1[:12] tile_rows=N name=value ..."""
     import hashlib
 
     src = os.path.join(ROOT, "mixture_experts_ffn_amd", "csrc", source)
@@ -431,24 +433,26 @@ def profile_entry(table_name, workload_name, kernel, source):
         parts = line.split()
         if (len(parts) >= 4 and parts[0] == workload_name and parts[1] == kernel
                 and parts[2] == f"{source}:{sha}"):
-            return {k: float(v) for k, v in (p.split("=") for p in parts[3:])}
+            e = {k: float(v) for k, v in (p.split("=") for p in parts[3:])}
+            if e.get("tile_rows") == tile_rows:
+                return e
     return None
 
 
-def measured_traffic(workload_name, kernel, source="gemm_mfma.hip"):
+def measured_traffic(workload_name, kernel, source, tile_rows):
     """HBM bytes per launch of the dominant kernel from the committed PMC summary
     (profiles/traffic.txt: FETCH_SIZE and WRITE_SIZE, scaled against a copy of
     known size), or None when stale or absent."""
-    e = profile_entry("traffic.txt", workload_name, kernel, source)
+    e = profile_entry("traffic.txt", workload_name, kernel, source, tile_rows)
     return None if e is None else e["fetch_bytes"] + e["write_bytes"]
 
 
-def measured_clock(workload_name, kernel, source="gemm_mfma.hip"):
+def measured_clock(workload_name, kernel, source, tile_rows):
     """Shader clock (GHz) and matrix-core busy fraction of the dominant kernel
     from the committed PMC summary (profiles/clock.txt: GRBM_GUI_ACTIVE and
     SQ_VALU_MFMA_BUSY_CYCLES over the dispatch), or (None, None) when stale or
     absent."""
-    e = profile_entry("clock.txt", workload_name, kernel, source)
+    e = profile_entry("clock.txt", workload_name, kernel, source, tile_rows)
     return (None, None) if e is None else (e["clock_ghz"], e["mfma_busy"])
 
 
