@@ -24,7 +24,8 @@
 //  * Global -> LDS copies go straight into LDS (16 bytes per lane, no
 //    register staging), NSTAGE stages deep, NSTAGE - 1 K steps ahead of the
 //    matrix cores; each wave waits only for its own copies of the stage it is
-//    about to use, then one barrier per K step publishes the stage.
+//    about to use, then one barrier per K step publishes the stage, and a
+//    step's copies are issued after its MFMAs.
 //  * A (token rows, K-contiguous) lands as [BM][BK] with the 16-byte piece
 //    index XOR-ed by a function of the row, so the 16 lanes of one 128-bit
 //    LDS read hit 16 different bank groups.  The dispatch gather x[sorted_slot / K] is
@@ -632,9 +633,12 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
             auto kloop = [&](auto fma_c) {
             for (int kb = 0; kb < nk; ++kb) {
                 // wait for this wave's copies of the current step (copy groups
-                // issued after it may stay in flight), publish the stage, then
-                // start the copies of step kb + NSTAGE - 1 into the stage the
-                // previous step used
+                // issued after it may stay in flight), publish the stage, run
+                // the step's MFMAs, then start the copies of step
+                // kb + NSTAGE - 1 into the stage the previous step used (after
+                // the MFMAs are issued, so they start right at the barrier:
+                // prefill GEMM1 on 128-row tiles 335 -> 323 us against issuing
+                // the copies first)
                 const int ahead = min(NSTAGE - 2, nk - 1 - kb + (chain ? NSTAGE - 1 : 0));
                 if (ahead >= 2)
                     wait_vm<2 * C::NL>();
@@ -652,6 +656,8 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
                 lds_barrier();
                 const int s_next = s_cur == 0 ? NSTAGE - 1 : s_cur - 1; // (step + NSTAGE - 1) % NSTAGE
                 const int step = kb + NSTAGE - 1;
+                if (active)
+                    compute(fma_c, smem + s_cur * C::STAGE_BYTES);
                 if (step < nk) {
                     issue(scur, step, smem + s_next * C::STAGE_BYTES);
                 } else if (chain) {
@@ -659,8 +665,6 @@ __global__ __launch_bounds__(64 * NWAVES, 8 / NWAVES) void moe_fwd_bf16(FastFwdA
                         wait_ready(nxt);
                     issue(snext, step - nk, smem + s_next * C::STAGE_BYTES);
                 }
-                if (active)
-                    compute(fma_c, smem + s_cur * C::STAGE_BYTES);
                 s_cur = s_cur == NSTAGE - 1 ? 0 : s_cur + 1;
             }
             };
